@@ -1,0 +1,83 @@
+"""Pins for the oracle's layer product y = x @ (T*alpha)^T (CPU only).
+
+Pins: a pure-Python triple loop on tiny shapes (no BLAS), one-hot inputs that
+read back T[n, k] * alpha exactly, the full pack/unpack path against the
+direct ternary, and the tolerance bound against a bf16-rounded output.
+"""
+
+import numpy as np
+import pytest
+
+import oracle as O
+import workloads as WL
+
+
+def _loop_gemv(x, t, a_w):
+    b_rows, k = x.shape
+    n = t.shape[0]
+    y = [[0.0] * n for _ in range(b_rows)]
+    for b in range(b_rows):
+        for r in range(n):
+            acc = 0.0
+            for kk in range(k):
+                if t[r, kk] != 0:
+                    acc += float(x[b, kk]) * float(t[r, kk]) * float(a_w[r, kk])
+            y[b][r] = acc
+    return np.array(y)
+
+
+@pytest.mark.parametrize("gran", ["per_group", "per_channel", "per_tensor"])
+def test_gemv_against_python_loop(gran):
+    w = WL.latent_weight(6, 256, seed=42)
+    _, x = WL.activations_bf16(2, 256, seed=43)
+    packed, a = O.quantize_pack(w, gran, 128)
+    t = O.decode_codes(O.unpack(packed, 6, 256))
+    wq = O.dequant(t, a, gran, 128)
+    y = O.gemv(x, wq)
+    y_loop = _loop_gemv(x, t, O.alpha_per_weight(a, 6, 256, gran, 128))
+    assert np.allclose(y, y_loop, rtol=1e-12, atol=1e-12)
+
+
+def test_pack_path_matches_direct_ternary():
+    w = WL.latent_weight(256, 512, seed=0)
+    packed, _ = O.quantize_pack(w)
+    assert packed.size == 256 * 512 * 5 // 32
+    t = O.decode_codes(O.unpack(packed, 256, 512))
+    assert np.array_equal(t, O.ternary(w))
+
+
+def test_one_hot_reads_back_weight():
+    w = WL.latent_weight(8, 256, seed=3)
+    packed, a = O.quantize_pack(w, "per_group", 128)
+    t = O.ternary(w)
+    wq = O.dequant(t, a, "per_group", 128)
+    for k in (0, 5, 127, 128, 255):
+        x = np.zeros((1, 256), dtype=np.float32)
+        x[0, k] = 1.0
+        y = O.gemv(x, wq)[0]
+        expect = t[:, k].astype(np.float64) * a[k // 128].astype(np.float64)
+        assert np.array_equal(y, expect)
+
+
+def test_rows_subset():
+    w = WL.latent_weight(16, 128, seed=8)
+    _, x = WL.activations_bf16(1, 128, seed=9)
+    _, a = O.quantize_pack(w)
+    wq = O.dequant(O.ternary(w), a, "per_group", 128)
+    rows = [0, 7, 15]
+    assert np.array_equal(O.gemv(x, wq, rows=rows), O.gemv(x, wq)[:, rows])
+
+
+def test_bf16_output_within_tolerance():
+    """Rounding the fp64 result to bf16 stays inside 1e-3 * sum|x*alpha| at
+    the small workload, so a bf16 output can pass the bound."""
+    w = WL.latent_weight(256, 512, seed=0)
+    _, x = WL.activations_bf16(1, 512, seed=1)
+    _, a = O.quantize_pack(w)
+    t = O.ternary(w)
+    wq = O.dequant(t, a, "per_group", 128)
+    y = O.gemv(x, wq)
+    yb = O.bf16_bits_to_f32(O.round_to_bf16_bits(y.astype(np.float32)))
+    bound = O.tolerance_bound(x, O.alpha_per_weight(a, 256, 512, "per_group"))
+    assert np.all(np.abs(yb - y) <= bound)
+    assert np.max(np.abs(yb - y) / bound) < 0.5

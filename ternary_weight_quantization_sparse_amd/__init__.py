@@ -1,0 +1,183 @@
+"""Sherry 1.25-bit ternary linear layer for MI355X (gfx950).
+
+Thin Python binding over libsherry (include/sherry.h).  Functions take torch
+CUDA (HIP) tensors, allocate outputs and workspaces with torch, and pass raw
+device pointers plus the current stream to the C ABI.  Every step of the
+computation runs in the library's HIP kernels.
+
+The method: "Sherry: Hardware-Efficient 1.25-Bit Ternary Quantization via
+Fine-grained Sparsification" (3:4 ternary blocks, 5-bit codes, Sparse-AbsMean
+scales) and the SherryNMQuant / SherryLinear listings of "Sherry, Tequila and
+Fairies in Python", section 1.1.
+"""
+
+from __future__ import annotations
+
+from dataclasses import dataclass
+
+from . import _lib
+from ._lib import SherryError, check, load  # noqa: F401
+
+__all__ = [
+    "PackedWeight", "quantize_pack", "unpack", "gemv", "gemm", "packed_bytes", "num_scales",
+    "workspace_bytes", "SherryError", "load",
+]
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _stream(stream):
+    torch = _torch()
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return s.cuda_stream
+
+
+def _ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+def _gran(granularity) -> int:
+    if isinstance(granularity, int):
+        return granularity
+    try:
+        return _lib.GRANULARITY[granularity]
+    except KeyError:
+        raise ValueError(f"unsupported granularity: {granularity!r}") from None
+
+
+def packed_bytes(n: int, k: int) -> int:
+    return int(load().sherry_packed_bytes(n, k))
+
+
+def num_scales(n: int, k: int, granularity="per_group", group_size: int = 128) -> int:
+    return int(load().sherry_num_scales(n, k, _gran(granularity), group_size))
+
+
+def workspace_bytes(op: int, n: int, k: int, granularity="per_group", group_size: int = 128,
+                    batch_or_m: int = 1, count: int = 1) -> int:
+    v = int(load().sherry_workspace_bytes(op, n, k, _gran(granularity), group_size, batch_or_m, count))
+    if v == (1 << 64) - 1:
+        raise ValueError("invalid arguments for sherry_workspace_bytes")
+    return v
+
+
+def _workspace(nbytes: int, device):
+    if nbytes == 0:
+        return None
+    torch = _torch()
+    return torch.empty(nbytes, dtype=torch.uint8, device=device)
+
+
+@dataclass
+class PackedWeight:
+    """Packed planes + scales of one [N, K] weight (the offline artifact)."""
+    packed: object          # torch.uint8 [N*K*5/32]
+    alpha: object           # torch.float32 [num_scales]
+    n: int
+    k: int
+    granularity: str = "per_group"
+    group_size: int = 128
+
+
+def quantize_pack(w, granularity: str = "per_group", group_size: int = 128, stream=None) -> PackedWeight:
+    """Sparse-AbsMean quantize + pack of a latent weight ``w`` [N, K] (fp32 or
+    bf16, CUDA)."""
+    torch = _torch()
+    if w.dim() != 2:
+        raise ValueError("Sherry quantization expects a 2-D weight")
+    n, k = w.shape
+    gran = _gran(granularity)
+    dtype = {torch.float32: _lib.F32, torch.bfloat16: _lib.BF16}.get(w.dtype)
+    if dtype is None:
+        raise ValueError("w must be float32 or bfloat16")
+    w = w.contiguous()
+    lib = load()
+    nbytes = int(lib.sherry_packed_bytes(n, k))
+    nsc = int(lib.sherry_num_scales(n, k, gran, group_size))
+    packed = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=w.device)
+    alpha = torch.empty(max(nsc, 1), dtype=torch.float32, device=w.device)
+    ws_bytes = int(lib.sherry_workspace_bytes(_lib.OP_QUANTIZE_PACK, n, k, gran, group_size, 1, 1))
+    ws = _workspace(ws_bytes if ws_bytes != (1 << 64) - 1 else 0, w.device)
+    check(lib.sherry_quantize_pack(n, k, gran, group_size, _ptr(w), dtype, _ptr(packed), _ptr(alpha),
+                                   _ptr(ws), 0 if ws is None else ws.numel(), _stream(stream)))
+    return PackedWeight(packed[:nbytes], alpha[:nsc], n, k, granularity, group_size)
+
+
+def unpack(pw: PackedWeight, out_dtype="int8", stream=None):
+    """Decode to int8 T, fp32 T*alpha or bf16 RNE(T*alpha), [N, K]."""
+    torch = _torch()
+    tdt, code = {"int8": (torch.int8, _lib.I8), "float32": (torch.float32, _lib.F32),
+                 "bfloat16": (torch.bfloat16, _lib.BF16)}[str(out_dtype).replace("torch.", "")]
+    out = torch.empty((pw.n, pw.k), dtype=tdt, device=pw.packed.device)
+    check(load().sherry_unpack(pw.n, pw.k, _gran(pw.granularity), pw.group_size, _ptr(pw.packed),
+                               _ptr(pw.alpha), _ptr(out), code, _stream(stream)))
+    return out
+
+
+def gemv(pw: PackedWeight, x, y_dtype="bfloat16", stream=None, out=None):
+    """y = x @ (T*alpha)^T for a decode batch ``x`` [B, K] bf16 (B = 1..16)."""
+    torch = _torch()
+    if x.dim() == 1:
+        x = x.unsqueeze(0)
+    if x.dtype != torch.bfloat16:
+        raise ValueError("x must be bfloat16")
+    x = x.contiguous()
+    b = x.shape[0]
+    ydt, code = {"bfloat16": (torch.bfloat16, _lib.BF16), "float32": (torch.float32, _lib.F32)}[
+        str(y_dtype).replace("torch.", "")]
+    y = out if out is not None else torch.empty((b, pw.n), dtype=ydt, device=x.device)
+    gran = _gran(pw.granularity)
+    lib = load()
+    ws_bytes = int(lib.sherry_workspace_bytes(_lib.OP_GEMV, pw.n, pw.k, gran, pw.group_size, b, 1))
+    ws = _workspace(ws_bytes if ws_bytes != (1 << 64) - 1 else 0, x.device)
+    check(lib.sherry_gemv(pw.n, pw.k, gran, pw.group_size, _ptr(pw.packed), _ptr(pw.alpha), _ptr(x), b,
+                          _ptr(y), code, 1, 0, 0, 0, _ptr(ws), 0 if ws is None else ws.numel(),
+                          _stream(stream)))
+    return y
+
+
+def gemv_batched(packed_all, alpha_all, n: int, k: int, x, count: int, packed_stride: int,
+                 alpha_stride: int, granularity="per_group", group_size: int = 128,
+                 y_dtype="bfloat16", y=None, y_stride=None, ws=None, stream=None):
+    """One launch over ``count`` same-shape packed matrices that share ``x``:
+    matrix c reads ``packed_all`` at byte c*packed_stride and ``alpha_all`` at
+    element c*alpha_stride, and writes y[c]."""
+    torch = _torch()
+    if x.dim() == 1:
+        x = x.unsqueeze(0)
+    b = x.shape[0]
+    ydt, code = {"bfloat16": (torch.bfloat16, _lib.BF16), "float32": (torch.float32, _lib.F32)}[
+        str(y_dtype).replace("torch.", "")]
+    if y_stride is None:
+        y_stride = b * n
+    if y is None:
+        y = torch.empty((count, y_stride), dtype=ydt, device=x.device)
+    gran = _gran(granularity)
+    lib = load()
+    if ws is None:
+        ws_bytes = int(lib.sherry_workspace_bytes(_lib.OP_GEMV, n, k, gran, group_size, b, count))
+        ws = _workspace(ws_bytes, x.device)
+    check(lib.sherry_gemv(n, k, gran, group_size, _ptr(packed_all), _ptr(alpha_all), _ptr(x), b, _ptr(y),
+                          code, count, packed_stride, alpha_stride, y_stride, _ptr(ws),
+                          0 if ws is None else ws.numel(), _stream(stream)))
+    return y
+
+
+def gemm(pw: PackedWeight, x, stream=None, out=None):
+    """Y = X @ (T*alpha)^T for prefill activations ``x`` [M, K] bf16 -> [M, N] bf16."""
+    torch = _torch()
+    if x.dtype != torch.bfloat16 or x.dim() != 2:
+        raise ValueError("x must be a 2-D bfloat16 tensor")
+    x = x.contiguous()
+    m = x.shape[0]
+    y = out if out is not None else torch.empty((m, pw.n), dtype=torch.bfloat16, device=x.device)
+    gran = _gran(pw.granularity)
+    lib = load()
+    ws_bytes = int(lib.sherry_workspace_bytes(_lib.OP_GEMM, pw.n, pw.k, gran, pw.group_size, m, 1))
+    ws = _workspace(ws_bytes if ws_bytes != (1 << 64) - 1 else 0, x.device)
+    check(lib.sherry_gemm(pw.n, pw.k, gran, pw.group_size, _ptr(pw.packed), _ptr(pw.alpha), _ptr(x), m,
+                          _ptr(y), _ptr(ws), 0 if ws is None else ws.numel(), _stream(stream)))
+    return y

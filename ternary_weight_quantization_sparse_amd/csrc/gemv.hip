@@ -1,0 +1,389 @@
+// Decode-time product y[b, n] = sum_k x[b, k] * T[n, k] * alpha(n, k).
+//
+// Method: "Sherry, Tequila and Fairies in Python", section 1.1 (SherryLinear
+// runs F.linear with the quantized weight) and the agihunt digest, inference
+// paragraph (weights packed offline as index + sign; tables built from the
+// activations online; accumulate; apply the scale).  The pages' kernel is an
+// x86 AVX2 byte-shuffle table; here the same idea is mapped to a CDNA4
+// workgroup.
+//
+// Batch 1 (gemv_b1_lut_kernel): HBM-bound streaming.  Each workgroup builds,
+// in LDS, a 32-entry fp32 table per block of 4 activations: the signed sum of
+// the three kept activations for every code (sign bit folded in).  Each lane
+// owns one weight row; per superblock it reads 16 bytes of nibbles (dwordx4)
+// and one sign dword, turns 4 blocks at a time into 4 byte offsets with 4
+// VALU ops (a nibble shift, a sign shift, a mask and an and-or), and then per
+// block does one byte extract, one ds_read_b32 and one fp32 add.  All 64 lanes
+// of a wave read the same block's 128-byte table, which spans the 32 LDS
+// banks once, so the lookups are conflict-free (equal entries broadcast).
+// The scale is applied once per group in fp32.
+//
+// Batch 2..16 (gemv_mfma_kernel): the contraction is no longer HBM-bound on
+// VALU (batch x 3 adds per block), so blocks are decoded to bf16 and fed to
+// v_mfma_f32_16x16x32_bf16 with the batch as the M dimension.  Decode: the
+// same 4-block byte offsets index a 128-byte LDS table whose 32 dword entries
+// hold the high bytes of the four bf16 weights (+-0.5 or 0, so the low bytes
+// are 0 and the result is rescaled by 2, exactly); two v_perm_b32 spread a
+// dword into the two bf16x2 operand registers.
+#include "sherry_internal.h"
+
+namespace sherry {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kLutThreads = 256;
+constexpr int kTableFloatsPerSb = kBlocksPerSb * 32;  // 32 entries per block
+
+// The 4 byte offsets (entry*4 into a block's 32-entry fp32 table, or into the
+// 128-byte decode table) of the blocks in quad q of a superblock record.
+// Quad q = 2d + h holds blocks q + 8b (b = 0..3): nibble dword d, nibble half
+// h, and sign bits q + 8b, which a shift moves to bit 6 of byte b.
+__device__ inline uint32_t quad_offsets(uint32_t nib_dword, uint32_t sign_word, int q) {
+  const uint32_t nq = (q & 1) ? (nib_dword >> 2) : (nib_dword << 2);
+  const uint32_t sq = (q <= 6) ? (sign_word << (6 - q)) : (sign_word >> 1);
+  return (nq & 0x3C3C3C3Cu) | (sq & 0x40404040u);
+}
+
+// Table entries part*8 .. part*8+7 of one block of 4 activations.  Entry
+// index = s<<4 | z<<2 | p1<<1 | p0; value = +-(x_k0 +- x_k1 +- x_k2) over the
+// kept positions k0 < k1 < k2 (all but z).
+__device__ inline void build_entries(const float xs[4], int part, float out[8]) {
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const int idx = part * 8 + e;
+    const int s = idx >> 4, z = (idx >> 2) & 3, p1 = (idx >> 1) & 1, p0 = idx & 1;
+    const int k0 = (z == 0) ? 1 : 0;
+    const int k1 = (z <= 1) ? 2 : 1;
+    const int k2 = (z <= 2) ? 3 : 2;
+    float v = xs[k0] + (p0 ? -xs[k1] : xs[k1]);
+    v = v + (p1 ? -xs[k2] : xs[k2]);
+    out[e] = s ? -v : v;
+  }
+}
+
+template <bool BF16>
+__device__ inline void store_y(void* y, int64_t idx, float v) {
+  if constexpr (BF16) {
+    reinterpret_cast<uint16_t*>(y)[idx] = f32_to_bf16_rne(v);
+  } else {
+    reinterpret_cast<float*>(y)[idx] = v;
+  }
+}
+
+template <int GRAN, int M, bool YBF16>
+__global__ __launch_bounds__(kLutThreads) void gemv_b1_lut_kernel(
+    const uint8_t* __restrict__ packed, const float* __restrict__ alpha,
+    const uint16_t* __restrict__ x, void* __restrict__ y, float* __restrict__ partial, int64_t n,
+    int64_t k, int group_sbs, int window_sbs, int ksplit, int64_t packed_stride,
+    int64_t alpha_stride, int64_t y_stride) {
+  extern __shared__ float tbl[];
+  const int tid = threadIdx.x;
+  const int64_t c = blockIdx.y;
+  const int kz = blockIdx.z;
+  const int64_t nsb = k / kSuperblock;
+  const int64_t sb_per_split = nsb / ksplit;
+  const int64_t sb_begin = kz * sb_per_split;
+  const int64_t sb_end = sb_begin + sb_per_split;
+
+  const uint8_t* pk = packed + c * packed_stride;
+  const uint4* __restrict__ nib = reinterpret_cast<const uint4*>(pk);
+  const uint32_t* __restrict__ sgn = reinterpret_cast<const uint32_t*>(pk + nibble_plane_bytes(n, k));
+  const float* __restrict__ al = alpha + c * alpha_stride;
+  const int64_t row_base = (int64_t)blockIdx.x * (kLutThreads * M) + tid;
+
+  float acc[M], accg[M];
+#pragma unroll
+  for (int i = 0; i < M; ++i) acc[i] = accg[i] = 0.f;
+
+  for (int64_t w0 = sb_begin; w0 < sb_end; w0 += window_sbs) {
+    const int wn = (int)((sb_end - w0) < window_sbs ? (sb_end - w0) : window_sbs);
+    __syncthreads();
+    // Build the window's tables: 4 tasks of 8 entries per block.
+    const int tasks = wn * kBlocksPerSb * 4;
+    for (int task = tid; task < tasks; task += kLutThreads) {
+      const int blk = task >> 2, part = task & 3;
+      const uint2 xv = *reinterpret_cast<const uint2*>(x + w0 * kSuperblock + blk * 4);
+      float xs[4] = {__uint_as_float(xv.x << 16), __uint_as_float(xv.x & 0xFFFF0000u),
+                     __uint_as_float(xv.y << 16), __uint_as_float(xv.y & 0xFFFF0000u)};
+      float e[8];
+      build_entries(xs, part, e);
+      float4* dst = reinterpret_cast<float4*>(tbl + blk * 32 + part * 8);
+      dst[0] = make_float4(e[0], e[1], e[2], e[3]);
+      dst[1] = make_float4(e[4], e[5], e[6], e[7]);
+    }
+    __syncthreads();
+
+    const int gpos0 = (int)((w0 - sb_begin) % group_sbs);
+#pragma unroll
+    for (int i = 0; i < M; ++i) {
+      const int64_t row = row_base + (int64_t)i * kLutThreads;
+      if (row >= n) continue;
+      int gpos = gpos0;
+#pragma unroll 2
+      for (int gi = 0; gi < wn; ++gi) {
+        const int64_t g = w0 + gi;
+        const uint4 nb = nib[g * n + row];
+        const uint32_t sg = sgn[g * n + row];
+        const char* t = reinterpret_cast<const char*>(tbl + gi * kTableFloatsPerSb);
+        float s[4] = {0.f, 0.f, 0.f, 0.f};
+        const uint32_t nd[4] = {nb.x, nb.y, nb.z, nb.w};
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+          const uint32_t off = quad_offsets(nd[q >> 1], sg, q);
+#pragma unroll
+          for (int b = 0; b < 4; ++b) {
+            const uint32_t o = (off >> (8 * b)) & 0xFFu;
+            s[b] += *reinterpret_cast<const float*>(t + (q + 8 * b) * 128 + o);
+          }
+        }
+        const float sb = (s[0] + s[1]) + (s[2] + s[3]);
+        if constexpr (GRAN == SHERRY_PER_GROUP) {
+          accg[i] += sb;
+          if (++gpos == group_sbs) {
+            acc[i] += al[(g / group_sbs) * n + row] * accg[i];
+            accg[i] = 0.f;
+            gpos = 0;
+          }
+        } else {
+          acc[i] += sb;
+        }
+      }
+    }
+  }
+
+#pragma unroll
+  for (int i = 0; i < M; ++i) {
+    const int64_t row = row_base + (int64_t)i * kLutThreads;
+    if (row >= n) continue;
+    float v = acc[i];
+    if (ksplit == 1) {
+      if constexpr (GRAN == SHERRY_PER_CHANNEL) v *= al[row];
+      if constexpr (GRAN == SHERRY_PER_TENSOR) v *= al[0];
+      store_y<YBF16>(y, c * y_stride + row, v);
+    } else {
+      partial[(c * ksplit + kz) * n + row] = v;
+    }
+  }
+}
+
+// Decode table entry for a code: the high bytes of the 4 bf16 weights, with
+// +-0.5 (0x3F / 0xBF) for kept weights and 0 for the pruned one.
+__device__ inline uint32_t decode_table_entry(uint32_t code) {
+  const uint32_t z = (code >> 2) & 3;
+  const uint32_t neg0 = (code >> 4) & 1;
+  const uint32_t neg1 = neg0 ^ (code & 1);
+  const uint32_t neg2 = neg0 ^ ((code >> 1) & 1);
+  uint32_t e = 0;
+  uint32_t rank = 0;
+  for (uint32_t pos = 0; pos < 4; ++pos) {
+    if (pos == z) continue;
+    const uint32_t neg = rank == 0 ? neg0 : (rank == 1 ? neg1 : neg2);
+    e |= (neg ? 0xBFu : 0x3Fu) << (8 * pos);
+    ++rank;
+  }
+  return e;
+}
+
+template <int GRAN, bool YBF16>
+__global__ __launch_bounds__(256) void gemv_mfma_kernel(
+    const uint8_t* __restrict__ packed, const float* __restrict__ alpha,
+    const uint16_t* __restrict__ x, void* __restrict__ y, float* __restrict__ partial, int64_t n,
+    int64_t k, int group_sbs, int batch, int ksplit, int64_t packed_stride, int64_t alpha_stride,
+    int64_t y_stride) {
+  __shared__ uint32_t dtbl[32];
+  if (threadIdx.x < 32) dtbl[threadIdx.x] = decode_table_entry(threadIdx.x);
+  __syncthreads();
+
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int r = lane & 15;  // weight row inside the 16-row tile / batch row of x
+  const int q = lane >> 4;  // k-quarter: nibble dword q of each superblock record
+  const int64_t row = (int64_t)blockIdx.x * 64 + wave * 16 + r;
+  const bool valid = row < n;
+  const int64_t c = blockIdx.y;
+  const int kz = blockIdx.z;
+  const int64_t nsb = k / kSuperblock;
+  const int64_t sb_per_split = nsb / ksplit;
+  const int64_t sb_begin = kz * sb_per_split;
+  const int64_t sb_end = sb_begin + sb_per_split;
+
+  const uint8_t* pk = packed + c * packed_stride;
+  const uint32_t* __restrict__ nibw = reinterpret_cast<const uint32_t*>(pk);
+  const uint32_t* __restrict__ sgn = reinterpret_cast<const uint32_t*>(pk + nibble_plane_bytes(n, k));
+  const float* __restrict__ al = alpha + c * alpha_stride;
+  const bool has_x = r < batch;
+  const uint16_t* xrow = x + (int64_t)(has_x ? r : 0) * k;
+  const char* dt = reinterpret_cast<const char*>(dtbl);
+
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  f32x4 accg = {0.f, 0.f, 0.f, 0.f};
+  int gpos = 0;
+  for (int64_t g = sb_begin; g < sb_end; ++g) {
+    uint32_t nd = 0, sg = 0;
+    if (valid) {
+      nd = nibw[(g * n + row) * 4 + q];
+      sg = sgn[g * n + row];
+    }
+    // blocks 2q + 8t (low nibbles) and 2q + 1 + 8t (high nibbles), t = 0..3
+    const uint32_t off_lo = quad_offsets(nd, sg, 2 * q);
+    const uint32_t off_hi = quad_offsets(nd, sg, 2 * q + 1);
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const uint32_t e0 = *reinterpret_cast<const uint32_t*>(dt + ((off_lo >> (8 * t)) & 0xFFu));
+      const uint32_t e1 = *reinterpret_cast<const uint32_t*>(dt + ((off_hi >> (8 * t)) & 0xFFu));
+      u32x4 wv;
+      wv[0] = __builtin_amdgcn_perm(0u, e0, 0x010C000Cu);
+      wv[1] = __builtin_amdgcn_perm(0u, e0, 0x030C020Cu);
+      wv[2] = __builtin_amdgcn_perm(0u, e1, 0x010C000Cu);
+      wv[3] = __builtin_amdgcn_perm(0u, e1, 0x030C020Cu);
+      u32x4 xv = {0u, 0u, 0u, 0u};
+      if (has_x) xv = *reinterpret_cast<const u32x4*>(xrow + g * kSuperblock + 32 * t + 8 * q);
+      if constexpr (GRAN == SHERRY_PER_GROUP) {
+        accg = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, xv),
+                                                       __builtin_bit_cast(bf16x8, wv), accg, 0, 0, 0);
+      } else {
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, xv),
+                                                      __builtin_bit_cast(bf16x8, wv), acc, 0, 0, 0);
+      }
+    }
+    if constexpr (GRAN == SHERRY_PER_GROUP) {
+      if (++gpos == group_sbs) {
+        const float a2 = valid ? 2.f * al[(g / group_sbs) * n + row] : 0.f;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc[e] += a2 * accg[e];
+        accg = f32x4{0.f, 0.f, 0.f, 0.f};
+        gpos = 0;
+      }
+    }
+  }
+
+  if (!valid) return;
+  float scale = 1.f;
+  if constexpr (GRAN != SHERRY_PER_GROUP) scale = 2.f;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const int b = 4 * q + e;  // output row of the MFMA = batch index
+    if (b >= batch) continue;
+    float v = acc[e] * scale;
+    if (ksplit == 1) {
+      if constexpr (GRAN == SHERRY_PER_CHANNEL) v *= al[row];
+      if constexpr (GRAN == SHERRY_PER_TENSOR) v *= al[0];
+      store_y<YBF16>(y, c * y_stride + (int64_t)b * n + row, v);
+    } else {
+      partial[((c * ksplit + kz) * batch + b) * n + row] = v;
+    }
+  }
+}
+
+// Split-K second stage: fixed-order sum of the partials, then the per-channel
+// or per-tensor scale and the output conversion.
+template <int GRAN, bool YBF16>
+__global__ void gemv_split_reduce(const float* __restrict__ partial, const float* __restrict__ alpha,
+                                  void* __restrict__ y, int64_t n, int batch, int ksplit, int count,
+                                  int64_t alpha_stride, int64_t y_stride) {
+  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t per = (int64_t)batch * n;
+  if (idx >= per * count) return;
+  const int64_t c = idx / per;
+  const int64_t bn = idx % per;
+  const int64_t row = bn % n;
+  float v = 0.f;
+  for (int s = 0; s < ksplit; ++s) v += partial[(c * ksplit + s) * per + bn];
+  const float* al = alpha + c * alpha_stride;
+  if constexpr (GRAN == SHERRY_PER_CHANNEL) v *= al[row];
+  if constexpr (GRAN == SHERRY_PER_TENSOR) v *= al[0];
+  store_y<YBF16>(y, c * y_stride + bn, v);
+}
+
+template <int GRAN, bool YBF16>
+hipError_t launch_gemv_t(const GemvPlan& p, int64_t n, int64_t k, int group_size,
+                         const uint8_t* packed, const float* alpha, const uint16_t* x, int batch,
+                         void* y, int count, int64_t packed_stride, int64_t alpha_stride,
+                         int64_t y_stride, float* ws, hipStream_t s) {
+  const int group_sbs = GRAN == SHERRY_PER_GROUP ? group_size / kSuperblock : 1;
+  const dim3 grid((unsigned)p.panels, (unsigned)count, (unsigned)p.ksplit);
+  if (p.kind == 0) {
+    const size_t lds = (size_t)p.window_sbs * kTableFloatsPerSb * sizeof(float);
+    switch (p.rows_per_thread) {
+      case 1:
+        hipLaunchKernelGGL((gemv_b1_lut_kernel<GRAN, 1, YBF16>), grid, dim3(kLutThreads), lds, s, packed,
+                           alpha, x, y, ws, n, k, group_sbs, p.window_sbs, p.ksplit, packed_stride,
+                           alpha_stride, y_stride);
+        break;
+      case 2:
+        hipLaunchKernelGGL((gemv_b1_lut_kernel<GRAN, 2, YBF16>), grid, dim3(kLutThreads), lds, s, packed,
+                           alpha, x, y, ws, n, k, group_sbs, p.window_sbs, p.ksplit, packed_stride,
+                           alpha_stride, y_stride);
+        break;
+      default:
+        hipLaunchKernelGGL((gemv_b1_lut_kernel<GRAN, 4, YBF16>), grid, dim3(kLutThreads), lds, s, packed,
+                           alpha, x, y, ws, n, k, group_sbs, p.window_sbs, p.ksplit, packed_stride,
+                           alpha_stride, y_stride);
+        break;
+    }
+  } else {
+    hipLaunchKernelGGL((gemv_mfma_kernel<GRAN, YBF16>), grid, dim3(256), 0, s, packed, alpha, x, y, ws, n,
+                       k, group_sbs, batch, p.ksplit, packed_stride, alpha_stride, y_stride);
+  }
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || p.ksplit == 1) return e;
+  const int64_t items = (int64_t)count * batch * n;
+  hipLaunchKernelGGL((gemv_split_reduce<GRAN, YBF16>), dim3((unsigned)((items + 255) / 256)), dim3(256), 0,
+                     s, ws, alpha, y, n, batch, p.ksplit, count, alpha_stride, y_stride);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+GemvPlan plan_gemv(int64_t n, int64_t k, int gran, int group_size, int batch, int count) {
+  GemvPlan p{};
+  const int64_t nsb = k / kSuperblock;
+  const int64_t group_sbs = gran == SHERRY_PER_GROUP ? group_size / kSuperblock : 1;
+  p.kind = batch == 1 ? 0 : 1;
+  int64_t rows_per_wg;
+  if (p.kind == 0) {
+    // more rows per thread amortize the table build once the grid is large
+    const int64_t wg1 = ((n + kLutThreads - 1) / kLutThreads) * count;
+    p.rows_per_thread = wg1 >= 8192 ? 4 : (wg1 >= 4096 ? 2 : 1);
+    rows_per_wg = (int64_t)kLutThreads * p.rows_per_thread;
+  } else {
+    p.rows_per_thread = 1;
+    rows_per_wg = 64;
+  }
+  p.panels = (n + rows_per_wg - 1) / rows_per_wg;
+  // Split K (in whole groups) until the launch has ~1024 workgroups.
+  const int64_t wgs = p.panels * count;
+  const int64_t groups = nsb / group_sbs;
+  int64_t split = 1;
+  while (wgs * split * 2 <= 1024 && groups % (split * 2) == 0) split *= 2;
+  p.ksplit = (int)split;
+  const int64_t sb_per_split = nsb / split;
+  p.window_sbs = (int)(sb_per_split < 16 ? sb_per_split : 16);
+  p.workspace_bytes = split > 1 ? (size_t)count * split * batch * n * sizeof(float) : 0;
+  return p;
+}
+
+hipError_t launch_gemv(const GemvPlan& p, int64_t n, int64_t k, int gran, int group_size,
+                       const uint8_t* packed, const float* alpha, const uint16_t* x, int batch,
+                       void* y, bool y_bf16, int count, int64_t packed_stride,
+                       int64_t alpha_stride, int64_t y_stride, float* ws, hipStream_t s) {
+#define SHERRY_GEMV_CASE(G, B)                                                                        \
+  return launch_gemv_t<G, B>(p, n, k, group_size, packed, alpha, x, batch, y, count, packed_stride, \
+                             alpha_stride, y_stride, ws, s)
+  if (gran == SHERRY_PER_GROUP) {
+    if (y_bf16) SHERRY_GEMV_CASE(SHERRY_PER_GROUP, true);
+    SHERRY_GEMV_CASE(SHERRY_PER_GROUP, false);
+  } else if (gran == SHERRY_PER_CHANNEL) {
+    if (y_bf16) SHERRY_GEMV_CASE(SHERRY_PER_CHANNEL, true);
+    SHERRY_GEMV_CASE(SHERRY_PER_CHANNEL, false);
+  } else {
+    if (y_bf16) SHERRY_GEMV_CASE(SHERRY_PER_TENSOR, true);
+    SHERRY_GEMV_CASE(SHERRY_PER_TENSOR, false);
+  }
+#undef SHERRY_GEMV_CASE
+}
+
+}  // namespace sherry

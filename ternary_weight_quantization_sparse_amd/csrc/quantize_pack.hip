@@ -1,0 +1,258 @@
+// Sparse-AbsMean quantize + 5-bit pack, and the scale reduction.
+//
+// Method: "Sherry: Hardware-Efficient 1.25-Bit Ternary Quantization via
+// Fine-grained Sparsification" (agihunt digest, format paragraph): in every
+// block of 4 weights along K the smallest |w| becomes 0, the other three keep
+// their sign, and the scale is the mean |w| of the kept weights.  Granules and
+// the nominal kept count L/4*3: "Sherry, Tequila and Fairies in Python",
+// section 1.1 (_reshape_by_granularity, SherryNMQuant.forward).
+//
+// Mapping: one workgroup (4 waves) per tile of 64 rows x one superblock of
+// 128 weights.  Each half-wave owns one (row, superblock) pair and each of its
+// 32 lanes one block of 4 weights, so a wave's loads are two contiguous row
+// segments (coalesced dwordx4 for fp32, dwordx2 for bf16).  The sign plane is
+// a ballot, the nibble dwords an OR-reduction over lanes 1/8/16 apart, and the
+// kept-|w| sum of the superblock a butterfly over XOR offsets 1..16 -- which
+// is exactly the index-order pairwise tree (each level adds lanes 2i and
+// 2i+1, and fp32 addition is commutative).
+#include "sherry_internal.h"
+
+namespace sherry {
+namespace {
+
+constexpr int kRowsPerTile = 64;
+constexpr int kIters = kRowsPerTile / 8;  // 4 waves x 2 halves = 8 rows per iteration
+
+template <bool BF16>
+struct Block4 { float v[4]; };
+
+template <bool BF16>
+__device__ inline Block4<BF16> load_block(const void* w, int64_t row, int64_t k, int64_t col) {
+  Block4<BF16> b;
+  if constexpr (BF16) {
+    const uint2 u = *reinterpret_cast<const uint2*>(
+        reinterpret_cast<const uint16_t*>(w) + row * k + col);
+    b.v[0] = __uint_as_float(u.x << 16);
+    b.v[1] = __uint_as_float(u.x & 0xFFFF0000u);
+    b.v[2] = __uint_as_float(u.y << 16);
+    b.v[3] = __uint_as_float(u.y & 0xFFFF0000u);
+  } else {
+    const float4 f = *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(w) + row * k + col);
+    b.v[0] = f.x; b.v[1] = f.y; b.v[2] = f.z; b.v[3] = f.w;
+  }
+  return b;
+}
+
+// Quantize one block: returns the 5-bit code, and the kept-|w| sum of the
+// block as a two-level pairwise tree ((a0 + a1) + (a2 + a3)) with the zeroed
+// weight contributing +0.
+__device__ inline uint32_t quantize_block(const float v[4], float& kept_sum) {
+  const float a0 = fabsf(v[0]), a1 = fabsf(v[1]), a2 = fabsf(v[2]), a3 = fabsf(v[3]);
+  // zero position: first index of the minimum magnitude (strict compares)
+  uint32_t z = 0;
+  float m = a0;
+  if (a1 < m) { z = 1; m = a1; }
+  if (a2 < m) { z = 2; m = a2; }
+  if (a3 < m) { z = 3; }
+  // positive-sign mask, bit i = (v[i] > 0)
+  const uint32_t pos = (v[0] > 0.f ? 1u : 0u) | (v[1] > 0.f ? 2u : 0u) |
+                       (v[2] > 0.f ? 4u : 0u) | (v[3] > 0.f ? 8u : 0u);
+  // kept positions k0 < k1 < k2
+  const uint32_t k0 = (z == 0) ? 1u : 0u;
+  const uint32_t k1 = (z <= 1) ? 2u : 1u;
+  const uint32_t k2 = (z <= 2) ? 3u : 2u;
+  const uint32_t g0 = (pos >> k0) & 1u, g1 = (pos >> k1) & 1u, g2 = (pos >> k2) & 1u;
+  const uint32_t s = g0 ^ 1u;        // 1 when the first kept weight is negative
+  const uint32_t p0 = g1 ^ g0;       // second kept sign differs from the first
+  const uint32_t p1 = g2 ^ g0;       // third kept sign differs from the first
+  kept_sum = ((z == 0 ? 0.f : a0) + (z == 1 ? 0.f : a1)) +
+             ((z == 2 ? 0.f : a2) + (z == 3 ? 0.f : a3));
+  return (s << 4) | (z << 2) | (p1 << 1) | p0;
+}
+
+template <bool BF16>
+__global__ __launch_bounds__(256) void quantize_pack_kernel(
+    const void* __restrict__ w, int64_t n, int64_t k, uint8_t* __restrict__ packed,
+    float* __restrict__ alpha_direct, float* __restrict__ sb_sums) {
+  const int64_t nsb = k / kSuperblock;
+  const int64_t g = blockIdx.y;
+  const int64_t row0 = (int64_t)blockIdx.x * kRowsPerTile;
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int half = lane >> 5;
+  const int j = lane & 31;  // block index inside the superblock
+  const int64_t col = g * kSuperblock + 4 * j;
+
+  // Issue every load of this thread first (8 rows), then compute.
+  Block4<BF16> blk[kIters];
+#pragma unroll
+  for (int it = 0; it < kIters; ++it) {
+    const int64_t row = row0 + wave * (2 * kIters) + 2 * it + half;
+    if (row < n) {
+      blk[it] = load_block<BF16>(w, row, k, col);
+    } else {
+      blk[it].v[0] = blk[it].v[1] = blk[it].v[2] = blk[it].v[3] = 0.f;
+    }
+  }
+
+  uint32_t* nib_plane = reinterpret_cast<uint32_t*>(packed);
+  uint32_t* sign_plane = reinterpret_cast<uint32_t*>(packed + nibble_plane_bytes(n, k));
+
+#pragma unroll
+  for (int it = 0; it < kIters; ++it) {
+    const int64_t row = row0 + wave * (2 * kIters) + 2 * it + half;
+    float sum;
+    const uint32_t code = quantize_block(blk[it].v, sum);
+
+    // sign plane: bit j of the dword = sign bit of block j
+    const unsigned long long ballot = __ballot((code >> 4) & 1u);
+    const uint32_t sign_word = (uint32_t)(ballot >> (32 * half));
+
+    // nibble dword (j & 7) >> 1: block 2d + h + 8b sits at bit 4h + 8b
+    uint32_t nib = (code & 15u) << (4 * (j & 1) + 8 * (j >> 3));
+    nib |= __shfl_xor(nib, 1);
+    nib |= __shfl_xor(nib, 8);
+    nib |= __shfl_xor(nib, 16);
+
+    // pairwise tree over the 32 blocks of the superblock
+    sum += __shfl_xor(sum, 1);
+    sum += __shfl_xor(sum, 2);
+    sum += __shfl_xor(sum, 4);
+    sum += __shfl_xor(sum, 8);
+    sum += __shfl_xor(sum, 16);
+
+    if (row < n) {
+      const int64_t rec = g * n + row;  // (superblock, row) record index
+      if (j < 8 && (j & 1) == 0) nib_plane[rec * 4 + (j >> 1)] = nib;
+      if (j == 1) sign_plane[rec] = sign_word;
+      if (j == 3) {
+        if (alpha_direct) {
+          alpha_direct[g * n + row] = (float)((double)sum / 96.0);
+        } else {
+          sb_sums[row * nsb + g] = sum;
+        }
+      }
+    }
+  }
+}
+
+// Pairwise tree over `width` (a power of two) consecutive values starting at
+// x, of which only the first `real` are read; the rest count as +0.  The
+// sequential form keeps one partial per tree level: after element i, the
+// partials of completed subtrees are merged (left + right), so the adds are
+// exactly those of the level-by-level tree.
+__device__ inline float tree_sum(const float* __restrict__ x, int64_t real, int64_t width) {
+  float stack[40];
+  int top_level = 0;
+  for (int64_t i = 0; i < width; ++i) {
+    float v = (i < real) ? x[i] : 0.f;
+    int lvl = 0;
+    int64_t t = i;
+    while (t & 1) {
+      v = stack[lvl] + v;
+      t >>= 1;
+      ++lvl;
+    }
+    stack[lvl] = v;
+    top_level = lvl;
+  }
+  return stack[top_level];
+}
+
+__host__ __device__ inline int64_t next_pow2(int64_t v) {
+  int64_t p = 1;
+  while (p < v) p <<= 1;
+  return p;
+}
+
+// per_group with G = 128*r (r > 1): tree over r superblock sums per group.
+__global__ void alpha_group_kernel(const float* __restrict__ sb, int64_t n, int64_t nsb, int r,
+                                   float* __restrict__ alpha) {
+  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t groups = nsb / r;
+  if (idx >= n * groups) return;
+  const int64_t gg = idx / n, row = idx % n;
+  const float s = tree_sum(sb + row * nsb + gg * r, r, next_pow2(r));
+  const double d = (double)r * kSuperblock / 4.0 * 3.0;
+  alpha[gg * n + row] = (float)((double)s / d);
+}
+
+// per_channel: tree over the nsb superblock sums of a row (K flat order).
+__global__ void alpha_channel_kernel(const float* __restrict__ sb, int64_t n, int64_t nsb, int64_t k,
+                                     float* __restrict__ alpha) {
+  const int64_t row = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (row >= n) return;
+  const float s = tree_sum(sb + row * nsb, nsb, next_pow2(nsb));
+  alpha[row] = (float)((double)s / ((double)k / 4.0 * 3.0));
+}
+
+// per_tensor, stage 1: aligned chunks of the row-major sequence of all
+// superblock sums (which is the flat weight order cut at 128).
+__global__ void alpha_tensor_stage1(const float* __restrict__ sb, int64_t total, int64_t chunk,
+                                    int64_t chunks, float* __restrict__ part) {
+  const int64_t c = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (c >= chunks) return;
+  const int64_t begin = c * chunk;
+  const int64_t real = (total - begin < chunk) ? total - begin : chunk;
+  part[c] = tree_sum(sb + begin, real, chunk);
+}
+
+// per_tensor, stage 2: tree over the chunk partials (padded with +0).
+__global__ void alpha_tensor_stage2(const float* __restrict__ part, int64_t chunks, int64_t width,
+                                    double denom, float* __restrict__ alpha) {
+  if (blockIdx.x != 0 || threadIdx.x != 0) return;
+  const float s = tree_sum(part, chunks, width);
+  alpha[0] = (float)((double)s / denom);
+}
+
+}  // namespace
+
+QuantizePlan plan_quantize(int64_t n, int64_t k, int gran, int group_size) {
+  QuantizePlan p{};
+  const int64_t nsb = k / kSuperblock;
+  p.direct_alpha = (gran == SHERRY_PER_GROUP && group_size == kSuperblock);
+  if (p.direct_alpha) return p;
+  p.sb_sums = n * nsb;
+  if (gran == SHERRY_PER_TENSOR) {
+    const int64_t width = next_pow2(p.sb_sums);
+    p.chunk = width < 256 ? width : 256;
+    p.chunks = (p.sb_sums + p.chunk - 1) / p.chunk;
+  }
+  p.workspace_bytes = (size_t)(p.sb_sums + p.chunks) * sizeof(float);
+  return p;
+}
+
+hipError_t launch_quantize_pack(const QuantizePlan& p, int64_t n, int64_t k, int gran,
+                                int group_size, const void* w, bool w_bf16, uint8_t* packed,
+                                float* alpha, float* ws, hipStream_t s) {
+  const int64_t nsb = k / kSuperblock;
+  dim3 grid((unsigned)((n + kRowsPerTile - 1) / kRowsPerTile), (unsigned)nsb);
+  float* direct = p.direct_alpha ? alpha : nullptr;
+  if (w_bf16) {
+    hipLaunchKernelGGL(quantize_pack_kernel<true>, grid, dim3(256), 0, s, w, n, k, packed, direct, ws);
+  } else {
+    hipLaunchKernelGGL(quantize_pack_kernel<false>, grid, dim3(256), 0, s, w, n, k, packed, direct, ws);
+  }
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || p.direct_alpha) return e;
+
+  if (gran == SHERRY_PER_GROUP) {
+    const int r = group_size / kSuperblock;
+    const int64_t items = n * (nsb / r);
+    hipLaunchKernelGGL(alpha_group_kernel, dim3((unsigned)((items + 255) / 256)), dim3(256), 0, s,
+                       ws, n, nsb, r, alpha);
+  } else if (gran == SHERRY_PER_CHANNEL) {
+    hipLaunchKernelGGL(alpha_channel_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s,
+                       ws, n, nsb, k, alpha);
+  } else {
+    float* part = ws + p.sb_sums;
+    hipLaunchKernelGGL(alpha_tensor_stage1, dim3((unsigned)((p.chunks + 255) / 256)), dim3(256), 0, s,
+                       ws, p.sb_sums, p.chunk, p.chunks, part);
+    const int64_t width = next_pow2(p.sb_sums) / p.chunk;
+    const double denom = (double)n * (double)k / 4.0 * 3.0;
+    hipLaunchKernelGGL(alpha_tensor_stage2, dim3(1), dim3(64), 0, s, part, p.chunks, width, denom, alpha);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace sherry

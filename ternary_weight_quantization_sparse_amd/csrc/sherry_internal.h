@@ -1,0 +1,71 @@
+// Internal declarations shared by the libsherry translation units (HIP kernels
+// and the C-ABI host code).  Not part of the public ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/sherry.h"
+
+namespace sherry {
+
+constexpr int kBlock = 4;            // weights per block
+constexpr int kSuperblock = 128;     // weights per superblock (32 blocks)
+constexpr int kBlocksPerSb = 32;
+
+// Offsets into the packed buffer.
+inline __host__ __device__ int64_t nibble_plane_bytes(int64_t n, int64_t k) { return n * k / 8; }
+
+// ---------------------------------------------------------------- quantize
+struct QuantizePlan {
+  bool direct_alpha;       // per_group with G == 128: alpha written by the pack kernel
+  int64_t sb_sums;         // number of fp32 superblock sums in the workspace
+  int64_t chunk;           // per_tensor first-stage chunk (power of two)
+  int64_t chunks;          // per_tensor first-stage partials
+  size_t workspace_bytes;
+};
+QuantizePlan plan_quantize(int64_t n, int64_t k, int gran, int group_size);
+hipError_t launch_quantize_pack(const QuantizePlan& p, int64_t n, int64_t k, int gran,
+                                int group_size, const void* w, bool w_bf16, uint8_t* packed,
+                                float* alpha, float* ws, hipStream_t s);
+
+// ---------------------------------------------------------------- unpack
+hipError_t launch_unpack(int64_t n, int64_t k, int gran, int group_size, const uint8_t* packed,
+                         const float* alpha, void* out, int out_dtype, hipStream_t s);
+
+// ---------------------------------------------------------------- gemv
+struct GemvPlan {
+  int kind;               // 0 = table-lookup kernel (batch 1), 1 = MFMA kernel (batch 2..16)
+  int rows_per_thread;    // kind 0
+  int window_sbs;         // kind 0: superblocks per LDS table window
+  int ksplit;             // split of K across workgroups (1 = none)
+  int64_t panels;         // workgroups along N
+  size_t workspace_bytes; // ksplit > 1: fp32 partials [count][ksplit][batch][N]
+};
+GemvPlan plan_gemv(int64_t n, int64_t k, int gran, int group_size, int batch, int count);
+hipError_t launch_gemv(const GemvPlan& p, int64_t n, int64_t k, int gran, int group_size,
+                       const uint8_t* packed, const float* alpha, const uint16_t* x, int batch,
+                       void* y, bool y_bf16, int count, int64_t packed_stride,
+                       int64_t alpha_stride, int64_t y_stride, float* ws, hipStream_t s);
+
+// ---------------------------------------------------------------- gemm
+struct GemmPlan {
+  int tile_n, tile_m;
+  size_t workspace_bytes;
+};
+GemmPlan plan_gemm(int64_t n, int64_t k, int gran, int group_size, int64_t m);
+hipError_t launch_gemm(const GemmPlan& p, int64_t n, int64_t k, int gran, int group_size,
+                       const uint8_t* packed, const float* alpha, const uint16_t* x, int64_t m,
+                       uint16_t* y, hipStream_t s);
+
+// ---------------------------------------------------------------- device helpers
+// Round an fp32 value to bf16, nearest-even (inputs are finite).
+__device__ inline uint16_t f32_to_bf16_rne(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+__device__ inline float bf16_to_f32(uint16_t h) { return __uint_as_float((uint32_t)h << 16); }
+
+}  // namespace sherry

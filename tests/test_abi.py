@@ -1,0 +1,151 @@
+"""C-ABI checks that need no GPU: the library loads, exports every symbol
+include/sherry.h declares, answers the size queries, and rejects every bad
+argument before any launch.
+
+Every rejected call here has exactly one invalid argument, and each check
+returns before anything is enqueued, so no kernel ever sees the fake (but
+aligned) device addresses used below.
+"""
+
+import os
+import re
+
+import pytest
+
+from conftest import ROOT
+
+S = pytest.importorskip("ternary_weight_quantization_sparse_amd")
+L = S._lib
+
+FAKE = 0x10000          # aligned, never dereferenced (the call fails validation first)
+FAKE2 = 0x20000
+MIS = 0x10008           # 8-byte aligned only
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return L.load()
+
+
+def _declared_symbols():
+    src = open(os.path.join(ROOT, "include", "sherry.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(sherry_[a-z_]+)\s*\(", src)))
+
+
+def test_exports_every_declared_symbol(lib):
+    declared = _declared_symbols()
+    assert len(declared) == 9
+    assert set(declared) == set(L.SYMBOLS)
+    for name in declared:
+        assert hasattr(lib, name), name
+
+
+def test_version_and_status_strings(lib):
+    assert lib.sherry_abi_version() == 1
+    for code in range(11):
+        assert lib.sherry_status_string(code).decode().startswith("SHERRY_")
+    assert b"unknown" in lib.sherry_status_string(99)
+
+
+def test_size_queries(lib):
+    assert lib.sherry_packed_bytes(256, 512) == 256 * 512 * 5 // 32
+    assert lib.sherry_packed_bytes(8192, 8192) == 10485760
+    assert lib.sherry_packed_bytes(2048, 100) == 0
+    assert lib.sherry_num_scales(8192, 8192, L.PER_GROUP, 128) == 524288
+    assert lib.sherry_num_scales(8192, 8192, L.PER_CHANNEL, 128) == 8192
+    assert lib.sherry_num_scales(8192, 8192, L.PER_TENSOR, 128) == 1
+    assert lib.sherry_num_scales(8, 130, L.PER_GROUP, 128) == -1
+    # quantize workspace: none for G=128, N*K/128 sums otherwise (+ chunk partials per tensor)
+    assert lib.sherry_workspace_bytes(L.OP_QUANTIZE_PACK, 64, 512, L.PER_GROUP, 128, 1, 1) == 0
+    assert lib.sherry_workspace_bytes(L.OP_QUANTIZE_PACK, 64, 512, L.PER_CHANNEL, 128, 1, 1) == 64 * 4 * 4
+    assert lib.sherry_workspace_bytes(L.OP_QUANTIZE_PACK, 64, 512, L.PER_TENSOR, 128, 1, 1) == (256 + 1) * 4
+    assert lib.sherry_workspace_bytes(L.OP_UNPACK, 64, 512, L.PER_TENSOR, 128, 1, 1) == 0
+    assert lib.sherry_workspace_bytes(L.OP_GEMV, 64, 512, L.PER_GROUP, 128, 17, 1) == (1 << 64) - 1
+    assert lib.sherry_workspace_bytes(9, 64, 512, L.PER_GROUP, 128, 1, 1) == (1 << 64) - 1
+
+
+def qp(lib, n=64, k=512, gran=L.PER_GROUP, g=128, w=FAKE, wd=L.F32, packed=FAKE, alpha=FAKE2,
+       ws=None, wsb=0):
+    return lib.sherry_quantize_pack(n, k, gran, g, w, wd, packed, alpha, ws, wsb, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(n=0), L.ERR_SHAPE), (dict(k=0), L.ERR_SHAPE), (dict(k=514), L.ERR_SHAPE),
+    (dict(n=-3), L.ERR_SHAPE), (dict(gran=3), L.ERR_GRANULARITY), (dict(gran=-1), L.ERR_GRANULARITY),
+    (dict(g=0), L.ERR_GROUP), (dict(g=-128), L.ERR_GROUP), (dict(g=96), L.ERR_GROUP),
+    (dict(k=520, g=130), L.ERR_GROUP),
+    (dict(k=520, gran=L.PER_TENSOR), L.ERR_UNSUPPORTED), (dict(g=64), L.ERR_UNSUPPORTED),
+    (dict(wd=L.I8), L.ERR_DTYPE), (dict(wd=7), L.ERR_DTYPE),
+    (dict(w=None), L.ERR_NULL), (dict(packed=None), L.ERR_NULL), (dict(alpha=None), L.ERR_NULL),
+    (dict(w=MIS), L.ERR_ALIGN), (dict(packed=MIS), L.ERR_ALIGN), (dict(alpha=MIS), L.ERR_ALIGN),
+    (dict(gran=L.PER_TENSOR), L.ERR_WORKSPACE), (dict(gran=L.PER_CHANNEL, ws=FAKE, wsb=4), L.ERR_WORKSPACE),
+    (dict(g=256), L.ERR_WORKSPACE),
+])
+def test_quantize_pack_rejects(lib, kw, code):
+    assert qp(lib, **kw) == code
+
+
+def up(lib, n=64, k=512, gran=L.PER_GROUP, g=128, packed=FAKE, alpha=FAKE2, out=FAKE, od=L.F32):
+    return lib.sherry_unpack(n, k, gran, g, packed, alpha, out, od, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(k=6), L.ERR_SHAPE), (dict(gran=5), L.ERR_GRANULARITY), (dict(g=100), L.ERR_GROUP),
+    (dict(od=9), L.ERR_DTYPE), (dict(packed=None), L.ERR_NULL), (dict(out=None), L.ERR_NULL),
+    (dict(alpha=None), L.ERR_NULL), (dict(out=MIS), L.ERR_ALIGN), (dict(k=132, gran=L.PER_TENSOR), L.ERR_UNSUPPORTED),
+])
+def test_unpack_rejects(lib, kw, code):
+    assert up(lib, **kw) == code
+
+
+def gv(lib, n=64, k=512, gran=L.PER_GROUP, g=128, packed=FAKE, alpha=FAKE2, x=FAKE, b=1, y=FAKE2,
+       yd=L.BF16, count=1, ps=0, as_=0, ys=0, ws=None, wsb=0):
+    return lib.sherry_gemv(n, k, gran, g, packed, alpha, x, b, y, yd, count, ps, as_, ys, ws, wsb, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(n=0), L.ERR_SHAPE), (dict(gran=7), L.ERR_GRANULARITY), (dict(g=0), L.ERR_GROUP),
+    (dict(yd=L.I8), L.ERR_DTYPE), (dict(x=None), L.ERR_NULL), (dict(alpha=None), L.ERR_NULL),
+    (dict(y=None), L.ERR_NULL), (dict(packed=None), L.ERR_NULL), (dict(x=MIS), L.ERR_ALIGN),
+    (dict(b=0), L.ERR_BATCH), (dict(b=17), L.ERR_BATCH), (dict(count=0), L.ERR_BATCH),
+    (dict(count=2, ps=100, as_=256, ys=64), L.ERR_BATCH),
+    (dict(count=2, ps=64 * 512 * 5 // 32, as_=255, ys=64), L.ERR_BATCH),
+    (dict(count=2, ps=64 * 512 * 5 // 32, as_=256, ys=63), L.ERR_BATCH),
+    (dict(count=2, ps=64 * 512 * 5 // 32 + 8, as_=256, ys=64), L.ERR_ALIGN),
+    (dict(count=2, ps=64 * 512 * 5 // 32, as_=258, ys=64), L.ERR_ALIGN),
+    (dict(k=520, gran=L.PER_TENSOR), L.ERR_UNSUPPORTED),
+])
+def test_gemv_rejects(lib, kw, code):
+    assert gv(lib, **kw) == code
+
+
+def test_gemv_workspace_rejected_when_needed(lib):
+    # a 64x512 single call is split along K, which needs a workspace
+    need = lib.sherry_workspace_bytes(L.OP_GEMV, 64, 512, L.PER_GROUP, 128, 1, 1)
+    assert need > 0
+    assert gv(lib) == L.ERR_WORKSPACE
+    assert gv(lib, ws=FAKE, wsb=need - 4) == L.ERR_WORKSPACE
+
+
+def gm(lib, n=64, k=512, gran=L.PER_GROUP, g=128, packed=FAKE, alpha=FAKE2, x=FAKE, m=32, y=FAKE2):
+    return lib.sherry_gemm(n, k, gran, g, packed, alpha, x, m, y, None, 0, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(k=2), L.ERR_SHAPE), (dict(gran=9), L.ERR_GRANULARITY), (dict(g=1000), L.ERR_GROUP),
+    (dict(x=None), L.ERR_NULL), (dict(y=None), L.ERR_NULL), (dict(y=MIS), L.ERR_ALIGN),
+    (dict(m=0), L.ERR_BATCH), (dict(m=-5), L.ERR_BATCH), (dict(k=516, gran=L.PER_TENSOR), L.ERR_UNSUPPORTED),
+])
+def test_gemm_rejects(lib, kw, code):
+    assert gm(lib, **kw) == code
+
+
+def test_binding_raises_value_error():
+    with pytest.raises(ValueError):
+        L.check(L.ERR_SHAPE)
+    with pytest.raises(NotImplementedError):
+        L.check(L.ERR_UNSUPPORTED)
+    with pytest.raises(S.SherryError):
+        L.check(L.ERR_HIP)
+    L.check(L.OK)

@@ -85,3 +85,13 @@ def layer_1b_weight_seed(i: int) -> int:
 
 def layer_3b_weight_seed(layer: int, i: int) -> int:
     return 1000 + 7 * layer + i
+
+
+def latent_weight_device(n: int, k: int, seed: int, device, std: float = 0.02):
+    """fp32 latent weight ~ N(0, std^2) drawn on the GPU with torch's seeded
+    Philox generator (for the 28-layer 3B stack, where host generation would
+    dominate the run).  Checks copy the same bytes back to the host."""
+    import torch
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+    return torch.randn((n, k), generator=g, device=device, dtype=torch.float32) * std

@@ -188,14 +188,15 @@ def bench_gemv_1b(args, dev):
         pw = S.quantize_pack(dev_f32(w, dev), "per_group", 128)
         ref_p, ref_a = O.quantize_pack(w, "per_group", 128)
         ok_q = bool(np.array_equal(to_np(pw.packed), ref_p) and
-                    np.array_equal(to_np(pw.alpha).view(np.uint32), ref_a.view(np.uint32)))
+                    np.array_equal(to_np(pw.alpha).view(np.uint32), ref_a.reshape(-1).view(np.uint32)))
         rep = Replicated(pw, copies_for(n, k))
         xb, xv = WL.activations_bf16(1, k, 200)
         x = dev_bf16(xb, dev)
         y = to_np(rep.gemv(x))
         wq = O.dequant(O.ternary(w), ref_a, "per_group", 128)
-        ok_y, ratio = within_tol(O.bf16_bits_to_f32(y[0, :n]).reshape(1, n), O.gemv(xv, wq),
-                                 O.tolerance_bound(xv, O.alpha_per_weight(ref_a, n, k, "per_group", 128)))
+        y_ref = O.gemv(xv, wq)
+        ok_y, ratio = within_tol(O.bf16_bits_to_f32(y[0, :n]).reshape(1, n), y_ref,
+                                 O.tolerance_bound(xv, O.alpha_per_weight(ref_a, n, k, "per_group", 128), y_ref))
         same = bool(np.all(y[:, :n] == y[0:1, :n]))
         checks.append({"shape": name, "pack_bit_exact": ok_q, "gemv_within_tol": ok_y,
                        "max_err_over_bound": ratio, "copies_identical": same})
@@ -263,8 +264,9 @@ def bench_gemm(pws, dev, ms, reps=10):
             yv = O.bf16_bits_to_f32(to_np(y))[rows]
             a = to_np(pw.alpha)
             wq = O.dequant(O.ternary(w), a, "per_group", 128)
-            ok, ratio = within_tol(yv, O.gemm(xvs[k][rows], wq),
-                                   O.tolerance_bound(xvs[k][rows], O.alpha_per_weight(a, n, k, "per_group", 128)))
+            y_ref = O.gemm(xvs[k][rows], wq)
+            ok, ratio = within_tol(yv, y_ref,
+                                   O.tolerance_bound(xvs[k][rows], O.alpha_per_weight(a, n, k, "per_group", 128), y_ref))
             checks.append({"shape": name, "within_tol_sampled_rows": ok, "max_err_over_bound": ratio})
         launches = [(lambda pw=pw, x=xs[k], y=ys[name]: S.gemm(pw, x, out=y)) for (name, n, k, pw, _) in pws]
         total, per, _ = timed_launches(launches, reps, 3)
@@ -298,7 +300,7 @@ def bench_quantize(dev, reps=10):
         pw = S.quantize_pack(w0, gran, 128)
         ref_p, ref_a = O.quantize_pack(vals, gran, 128)
         ok = bool(np.array_equal(to_np(pw.packed), ref_p) and
-                  np.array_equal(to_np(pw.alpha).view(np.uint32), ref_a.view(np.uint32)))
+                  np.array_equal(to_np(pw.alpha).view(np.uint32), ref_a.reshape(-1).view(np.uint32)))
         ws_b = S.workspace_bytes(0, n, k, gran, 128)
         ws = torch.empty(max(ws_b, 16), dtype=torch.uint8, device=dev)
         packed = torch.empty(S.packed_bytes(n, k), dtype=torch.uint8, device=dev)
@@ -349,7 +351,7 @@ def bench_gemv_3b(dev, batches, steps=10):
     name, n, k, rep, (pw, wv) = shapes[0]
     ref_p, ref_a = O.quantize_pack(wv, "per_group", 128)
     res["layer0_q_pack_bit_exact"] = bool(np.array_equal(to_np(pw.packed), ref_p) and
-                                          np.array_equal(to_np(pw.alpha), ref_a))
+                                          np.array_equal(to_np(pw.alpha), ref_a.reshape(-1)))
     for b in batches:
         launches, reps_b = [], []
         for (name, n, k, rep, (pw, wv)) in shapes:
@@ -370,8 +372,9 @@ def bench_gemv_3b(dev, batches, steps=10):
             y = to_np(rb.gemv(x))
             a = to_np(pw.alpha)
             wq = O.dequant(O.ternary(wv), a, "per_group", 128)
-            ok, ratio = within_tol(O.bf16_bits_to_f32(y[0, :b * n]).reshape(b, n), O.gemv(xv, wq),
-                                   O.tolerance_bound(xv, O.alpha_per_weight(a, n, k, "per_group", 128)))
+            y_ref = O.gemv(xv, wq)
+            ok, ratio = within_tol(O.bf16_bits_to_f32(y[0, :b * n]).reshape(b, n), y_ref,
+                                   O.tolerance_bound(xv, O.alpha_per_weight(a, n, k, "per_group", 128), y_ref))
             ok_all &= ok
             worst = max(worst, ratio)
         total, per, _ = timed_launches(launches, steps, 2)

@@ -65,7 +65,7 @@ __all__ = [
     "encode_block", "decode_code", "encode", "decode_codes",
     "pack", "unpack", "packed_bytes",
     "pairwise_sum_f32", "alpha", "alpha_per_weight", "dequant",
-    "quantize_pack", "gemv", "gemm", "tolerance_bound", "round_to_bf16_bits",
+    "quantize_pack", "gemv", "gemm", "tolerance_bound", "bf16_half_ulp", "round_to_bf16_bits",
     "bf16_bits_to_f32",
 ]
 
@@ -360,13 +360,34 @@ def gemv(x: np.ndarray, wq: np.ndarray, rows=None) -> np.ndarray:
 gemm = gemv  # the prefill product is the same definition with M rows of x
 
 
-def tolerance_bound(x: np.ndarray, alpha_w: np.ndarray) -> np.ndarray:
+def tolerance_bound(x: np.ndarray, alpha_w: np.ndarray, y_ref=None) -> np.ndarray:
     """Per-element bound ``1e-3 * sum_k |x_k * alpha(n, k)|`` over all k,
     pruned positions included.  ``x`` [B, K], ``alpha_w`` [N, K]; returns
-    [B, N]."""
+    [B, N].
+
+    The 1e-3 term bounds the accumulation against the fp64 product.  When the
+    output is stored in bf16, pass the fp64 result as ``y_ref``: rounding to
+    bf16 adds at most half a bf16 ulp of the result, which is added to the
+    bound (reading: the bf16 output format is part of the workload, and its
+    final rounding can exceed 1e-3 * sum|x*alpha| whenever |y| is a large
+    fraction of sum|x*alpha|, e.g. short K or x correlated with the weights).
+    """
     x64 = np.abs(np.asarray(x, dtype=np.float64))
     a64 = np.abs(np.asarray(alpha_w, dtype=np.float64))
-    return 1e-3 * (x64 @ a64.T)
+    bound = 1e-3 * (x64 @ a64.T)
+    if y_ref is not None:
+        bound = bound + bf16_half_ulp(y_ref)
+    return bound
+
+
+def bf16_half_ulp(y: np.ndarray) -> np.ndarray:
+    """Half the bf16 spacing at |y| (8 significant bits): 2^(floor(log2|y|) - 8);
+    0 where y == 0."""
+    a = np.abs(np.asarray(y, dtype=np.float64))
+    out = np.zeros_like(a)
+    nz = a > 0
+    out[nz] = np.exp2(np.floor(np.log2(a[nz])) - 8.0)
+    return out
 
 
 # --------------------------------------------------------------------------

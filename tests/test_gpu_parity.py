@@ -51,7 +51,8 @@ def check_quantize(w_dev, w_vals, gran, g=128):
     pw = S.quantize_pack(w_dev, gran, g)
     ref_p, ref_a = O.quantize_pack(w_vals, gran, g)
     got_p, got_a = to_np(pw.packed), to_np(pw.alpha)
-    assert got_p.size == ref_p.size
+    ref_a = np.ascontiguousarray(ref_a).reshape(-1)
+    assert got_p.size == ref_p.size and got_a.size == ref_a.size
     bad = np.flatnonzero(got_p != ref_p)
     assert bad.size == 0, f"{bad.size} packed bytes differ, first at {bad[:5]}"
     bad_a = np.flatnonzero(got_a.view(np.uint32) != ref_a.view(np.uint32))
@@ -150,7 +151,8 @@ def gemv_case(n, k, wseed, xbits, xvals, gran="per_group", g=128, y_dtype="float
     if y_dtype == "bfloat16":
         yv = O.bf16_bits_to_f32(yv)
     y_ref = O.gemv(xvals, wq)
-    bound = O.tolerance_bound(xvals, O.alpha_per_weight(a, n, k, gran, g))
+    bound = O.tolerance_bound(xvals, O.alpha_per_weight(a, n, k, gran, g),
+                              y_ref if y_dtype == "bfloat16" else None)
     return check_close(yv, y_ref, bound, f"gemv {n}x{k} {gran} B={xbits.shape[0]}")
 
 
@@ -198,7 +200,7 @@ def test_gemv_one_hot_exact(batch):
     n, k = 192, 384
     w = WL.latent_weight(n, k, 99)
     pw = S.quantize_pack(dev_f32(w), "per_group", 128)
-    a = to_np(pw.alpha)
+    a = to_np(pw.alpha).reshape(k // 128, n)
     t = O.ternary(w)
     cols = [0, 131, 383, 200][:batch] if batch > 1 else [131]
     xv = np.zeros((batch, k), dtype=np.float32)
@@ -262,8 +264,9 @@ def test_gemv_bench_launch_configuration():
     yv = to_np(y)
     a = to_np(pw.alpha)
     wq = O.dequant(O.ternary(w), a, "per_group", 128)
-    bound = O.tolerance_bound(xv, O.alpha_per_weight(a, n, k, "per_group", 128))
-    check_close(O.bf16_bits_to_f32(yv[0, :n]).reshape(1, n), O.gemv(xv, wq), bound, "copy 0")
+    y_ref = O.gemv(xv, wq)
+    bound = O.tolerance_bound(xv, O.alpha_per_weight(a, n, k, "per_group", 128), y_ref)
+    check_close(O.bf16_bits_to_f32(yv[0, :n]).reshape(1, n), y_ref, bound, "copy 0")
     assert np.all(yv[:, :n] == yv[0:1, :n])
 
 
@@ -278,7 +281,7 @@ def gemm_case(n, k, m, wseed, xseed, gran="per_group", g=128, rows=None):
     if rows is not None:
         xv, y = xv[rows], y[rows]
     y_ref = O.gemm(xv, wq)
-    bound = O.tolerance_bound(xv, O.alpha_per_weight(a, n, k, gran, g))
+    bound = O.tolerance_bound(xv, O.alpha_per_weight(a, n, k, gran, g), y_ref)
     return check_close(y, y_ref, bound, f"gemm {n}x{k} M={m} {gran}")
 
 
@@ -300,7 +303,15 @@ def test_gemm_llama1b_m2048_sampled(i):
 @pytest.mark.parametrize("n,k,m", [(100, 256, 77), (1, 128, 1), (130, 384, 129), (64, 128, 300)])
 @pytest.mark.parametrize("gran,g", [("per_group", 128), ("per_channel", 128), ("per_tensor", 128)])
 def test_gemm_ragged(n, k, m, gran, g):
-    gemm_case(n, k, m, 900 + n, 901 + m, gran, g)
+    gemm_case(n, k, m, 900 + n, 5000 + m, gran, g)
+
+
+@pytest.mark.parametrize("gran", ["per_group", "per_channel", "per_tensor"])
+def test_gemm_correlated_inputs(gran):
+    """Activation rows drawn from the weight's own stream (x = w / 0.02 for
+    the first rows), so |y| approaches sum|x*alpha| on the diagonal: the
+    case where the bf16 output rounding dominates the bound."""
+    gemm_case(130, 384, 129, 1030, 1030, gran, 128)
 
 
 def test_gemm_group_256():
@@ -311,7 +322,7 @@ def test_gemm_one_hot_exact():
     n, k = 160, 256
     w = WL.latent_weight(n, k, 17)
     pw = S.quantize_pack(dev_f32(w))
-    a = to_np(pw.alpha)
+    a = to_np(pw.alpha).reshape(k // 128, n)
     t = O.ternary(w)
     xv = np.zeros((3, k), dtype=np.float32)
     cols = [0, 129, 255]

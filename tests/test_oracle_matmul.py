@@ -81,3 +81,21 @@ def test_bf16_output_within_tolerance():
     bound = O.tolerance_bound(x, O.alpha_per_weight(a, 256, 512, "per_group"))
     assert np.all(np.abs(yb - y) <= bound)
     assert np.max(np.abs(yb - y) / bound) < 0.5
+
+
+def test_bf16_half_ulp_bounds_rounding():
+    """Half-ulp values at powers of two, and the bound holds (and is reached
+    at ties) for torch's bf16 rounding."""
+    torch = pytest.importorskip("torch")
+    assert O.bf16_half_ulp(np.array([1.0]))[0] == 2.0**-8
+    assert O.bf16_half_ulp(np.array([1.99]))[0] == 2.0**-8
+    assert O.bf16_half_ulp(np.array([-4.0]))[0] == 2.0**-6
+    assert O.bf16_half_ulp(np.array([0.0]))[0] == 0.0
+    g = np.random.default_rng(3)
+    y = np.concatenate([g.standard_normal(20000) * 10.0 ** g.integers(-3, 4, 20000),
+                        [1.0 + 2.0**-8, 3.0 * (1.0 + 2.0**-8)]])
+    yb = torch.from_numpy(y.astype(np.float32)).to(torch.bfloat16).double().numpy()
+    err = np.abs(yb - y.astype(np.float32).astype(np.float64))
+    hu = O.bf16_half_ulp(y)
+    assert np.all(err <= hu * (1 + 1e-12))
+    assert err[-2] == hu[-2]

@@ -387,38 +387,34 @@ def bench_gemv_3b(dev, batches, steps=10):
     return res
 
 
-def cpu_baseline(pws):
-    """The oracle on one 1B layer (7 linears, batch 1) from packed bytes to
-    fp64 outputs, with NumPy/BLAS held to one thread."""
+def cpu_baseline(pws, min_seconds=10.0):
+    """The oracle on a bounded sample of the headline workload: whole passes
+    over one 1B layer (7 linears, batch 1) from packed bytes to fp64 outputs,
+    repeated until ``min_seconds`` have elapsed, NumPy/BLAS held to one
+    thread."""
     import numpy as np
     import oracle as O
     import workloads as WL
-    try:
-        from threadpoolctl import threadpool_limits
-    except ImportError:  # pragma: no cover
-        threadpool_limits = None
-    ctx = threadpool_limits(limits=1) if threadpool_limits else None
-    total_bytes, t0 = 0, time.perf_counter()
-    try:
-        for (name, n, k, pw, _) in pws:
-            packed, alpha = to_np(pw.packed), to_np(pw.alpha)
-            xb, xv = WL.activations_bf16(1, k, 200)
-            t_start = time.perf_counter()
-            t = O.decode_codes(O.unpack(packed, n, k))
-            wq = O.dequant(t, alpha, "per_group", 128)
-            O.gemv(xv, wq)
-            total_bytes += packed.size + alpha.size * 4 + 2 * k + 2 * n
-            del t, wq
-            _ = t_start
-    finally:
-        if ctx is not None:
-            ctx.__exit__(None, None, None)
-    secs = time.perf_counter() - t0
+    from threadpoolctl import threadpool_limits
+    host = [(n, k, to_np(pw.packed), to_np(pw.alpha), WL.activations_bf16(1, k, 200)[1])
+            for (name, n, k, pw, _) in pws]
+    total_bytes, passes = 0, 0
+    with threadpool_limits(limits=1):
+        t0 = time.perf_counter()
+        while True:
+            for (n, k, packed, alpha, xv) in host:
+                t = O.decode_codes(O.unpack(packed, n, k))
+                O.gemv(xv, O.dequant(t, alpha, "per_group", 128))
+                total_bytes += packed.size + alpha.size * 4 + 2 * k + 2 * n
+            passes += 1
+            if time.perf_counter() - t0 >= min_seconds:
+                break
+        secs = time.perf_counter() - t0
     return {"value": total_bytes / secs / 1e9, "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "seconds": secs,
-            "sample": "one LLaMA-3.2-1B layer (7 linears, batch 1, group 128): packed bytes -> "
-                      "unpack -> fp64 dequant -> fp64 product, NumPy with BLAS held to 1 thread; "
-                      "same algorithmic-bytes definition as the headline"}
+            "seconds": secs, "passes": passes,
+            "sample": f"{passes} passes over one LLaMA-3.2-1B layer (7 linears, batch 1, group 128): "
+                      "packed bytes -> unpack -> fp64 dequant -> fp64 product, NumPy with BLAS held to "
+                      "1 thread; same algorithmic-bytes definition as the headline"}
 
 
 # ----------------------------------------------------------------------------
@@ -428,7 +424,8 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--sections", default="gemv,single,gemm,quantize,gemv3b,cpu",
-                    help="comma list of: gemv (always), single, gemm, quantize, gemv3b, cpu")
+                    help="comma list of: gemv (always), single, gemm, quantize, gemv3b, cpu, "
+                         "copycal (a 1 GiB device copy for scaling HBM counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU: this build has no multi-GPU path (asked for {args.gpus}). "
@@ -452,6 +449,14 @@ def main():
         extra["quantize"] = bench_quantize(dev)
     if "gemv3b" in sections:
         extra["gemv_3b"] = bench_gemv_3b(dev, (1, 4, 16))
+    if "copycal" in sections:
+        # a plain copy of known size, for scaling HBM counters (FETCH_SIZE / WRITE_SIZE)
+        src = torch.empty(GIB, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     cpu = cpu_baseline(pws) if "cpu" in sections else None
     if cpu:
         log(f"[cpu] oracle {cpu['value']:.3f} GB/s in {cpu['seconds']:.1f} s (1 thread)")

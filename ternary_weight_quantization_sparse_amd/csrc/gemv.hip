@@ -35,6 +35,15 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kLutThreads = 256;
+#ifndef SHERRY_LUT_WIN_MAX
+#define SHERRY_LUT_WIN_MAX 4  // superblocks per LDS table window (4 -> 16 KB)
+#endif
+#ifndef SHERRY_LUT_NT
+#define SHERRY_LUT_NT 1       // non-temporal loads for the packed stream
+#endif
+#ifndef SHERRY_LUT_ROWS
+#define SHERRY_LUT_ROWS 1     // row slots per thread on large launches
+#endif
 constexpr int kTableFloatsPerSb = kBlocksPerSb * 32;  // 32 entries per block
 
 // The 4 byte offsets (entry*4 into a block's 32-entry fp32 table, or into the
@@ -43,25 +52,38 @@ constexpr int kTableFloatsPerSb = kBlocksPerSb * 32;  // 32 entries per block
 // h, and sign bits q + 8b, which a shift moves to bit 6 of byte b.
 __device__ inline uint32_t quad_offsets(uint32_t nib_dword, uint32_t sign_word, int q) {
   const uint32_t nq = (q & 1) ? (nib_dword >> 2) : (nib_dword << 2);
-  const uint32_t sq = (q <= 6) ? (sign_word << (6 - q)) : (sign_word >> 1);
-  return (nq & 0x3C3C3C3Cu) | (sq & 0x40404040u);
+  const uint32_t sq = ((q <= 6) ? (sign_word << (6 - q)) : (sign_word >> 1)) & 0x40404040u;
+  // (nq & 0x3C3C3C3C) | sq as one 3-input bit operation
+  return __builtin_amdgcn_bitop3_b32(nq, sq, 0x3C3C3C3Cu, 0xEC);
 }
 
-// Table entries part*8 .. part*8+7 of one block of 4 activations.  Entry
-// index = s<<4 | z<<2 | p1<<1 | p0; value = +-(x_k0 +- x_k1 +- x_k2) over the
-// kept positions k0 < k1 < k2 (all but z).
-__device__ inline void build_entries(const float xs[4], int part, float out[8]) {
+// Table of one block of 4 activations, half h: entries for zero positions
+// z = 2h, 2h+1 with both sign bits.  Entry index = s<<4 | z<<2 | p1<<1 | p0;
+// value = (x_k0 +- x_k1) +- x_k2 over the kept positions k0 < k1 < k2 (all
+// but z), negated when s = 1.  Writes entries [8h, 8h+8) and [16+8h, 24+8h).
+__device__ inline void build_block_half(float* blk_tbl, const uint16_t* __restrict__ xblk, int h) {
+  const uint2 xv = *reinterpret_cast<const uint2*>(xblk);
+  const float xs[4] = {__uint_as_float(xv.x << 16), __uint_as_float(xv.x & 0xFFFF0000u),
+                       __uint_as_float(xv.y << 16), __uint_as_float(xv.y & 0xFFFF0000u)};
+  float e[8];
 #pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    const int idx = part * 8 + e;
-    const int s = idx >> 4, z = (idx >> 2) & 3, p1 = (idx >> 1) & 1, p0 = idx & 1;
-    const int k0 = (z == 0) ? 1 : 0;
-    const int k1 = (z <= 1) ? 2 : 1;
-    const int k2 = (z <= 2) ? 3 : 2;
-    float v = xs[k0] + (p0 ? -xs[k1] : xs[k1]);
-    v = v + (p1 ? -xs[k2] : xs[k2]);
-    out[e] = s ? -v : v;
+  for (int zz = 0; zz < 2; ++zz) {
+    const int z = 2 * h + zz;
+    const float a = xs[z == 0 ? 1 : 0];
+    const float b = xs[z <= 1 ? 2 : 1];
+    const float c = xs[z <= 2 ? 3 : 2];
+    const float apb = a + b, amb = a - b;
+    e[4 * zz + 0] = apb + c;
+    e[4 * zz + 1] = amb + c;
+    e[4 * zz + 2] = apb - c;
+    e[4 * zz + 3] = amb - c;
   }
+  float4* pos = reinterpret_cast<float4*>(blk_tbl + 8 * h);
+  float4* neg = reinterpret_cast<float4*>(blk_tbl + 16 + 8 * h);
+  pos[0] = make_float4(e[0], e[1], e[2], e[3]);
+  pos[1] = make_float4(e[4], e[5], e[6], e[7]);
+  neg[0] = make_float4(-e[0], -e[1], -e[2], -e[3]);
+  neg[1] = make_float4(-e[4], -e[5], -e[6], -e[7]);
 }
 
 template <bool BF16>
@@ -73,84 +95,143 @@ __device__ inline void store_y(void* y, int64_t idx, float v) {
   }
 }
 
-template <int GRAN, int M, bool YBF16>
+// Scale handling of the batch-1 kernel.
+enum LutMode { kGroup1 = 0, kGroupN = 1, kChannel = 2, kTensor = 3 };
+
+// The packed data of one row over one window of WIN superblocks.
+template <int MODE, int WIN>
+struct RowWindow {
+  uint4 nb[WIN];
+  uint32_t sg[WIN];
+  float al[(MODE == kGroup1 || MODE == kGroupN) ? WIN : 1];
+};
+
+// Packed weights and scales are read once per launch: streaming loads.
+template <typename T>
+__device__ inline T stream_load(const T* p) {
+#if SHERRY_LUT_NT
+  return __builtin_nontemporal_load(p);
+#else
+  return *p;
+#endif
+}
+
+// Loads of one row-window.  The per-superblock bases are wave-uniform (SGPR)
+// and the per-lane part is a 32-bit byte offset, so every load is a
+// saddr + voffset global load.
+template <int MODE, int WIN>
+__device__ inline void load_row_window(RowWindow<MODE, WIN>& r, const uint8_t* __restrict__ nib_base,
+                                       const uint8_t* __restrict__ sgn_base, const float* __restrict__ al,
+                                       int64_t n, uint32_t row, int64_t g0, int group_sbs) {
+#pragma unroll
+  for (int gi = 0; gi < WIN; ++gi) {
+    const int64_t g = g0 + gi;
+    const u32x4 v = stream_load(reinterpret_cast<const u32x4*>(nib_base + g * n * 16 + row * 16u));
+    r.nb[gi] = make_uint4(v[0], v[1], v[2], v[3]);
+    r.sg[gi] = stream_load(reinterpret_cast<const uint32_t*>(sgn_base + g * n * 4 + row * 4u));
+    if constexpr (MODE == kGroup1) r.al[gi] = stream_load(al + g * n + row);
+    if constexpr (MODE == kGroupN) r.al[gi] = stream_load(al + (g / group_sbs) * n + row);
+  }
+}
+
+// Sum of the 32 table lookups of superblock slot GI (4 partial sums for ILP).
+// Every LDS offset is a compile-time immediate, GI*4096 + (q + 8b)*128, added
+// to the byte taken from the quad's offsets.
+template <int GI>
+__device__ inline float superblock_sum(const float* tbl, const uint4 nb, const uint32_t sg) {
+  const uint32_t nd[4] = {nb.x, nb.y, nb.z, nb.w};
+  const char* t = reinterpret_cast<const char*>(tbl) + GI * kTableFloatsPerSb * 4;
+  float s[4];
+#pragma unroll
+  for (int q = 0; q < 8; ++q) {
+    const uint32_t off = quad_offsets(nd[q >> 1], sg, q);
+    const uint32_t o[4] = {off & 0xFFu, __builtin_amdgcn_ubfe(off, 8, 8), __builtin_amdgcn_ubfe(off, 16, 8),
+                           off >> 24};
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      const float v = *reinterpret_cast<const float*>(t + (q + 8 * b) * 128 + o[b]);
+      s[b] = q == 0 ? v : s[b] + v;
+    }
+  }
+  return (s[0] + s[1]) + (s[2] + s[3]);
+}
+
+template <int MODE, int WIN, int GI = 0>
+__device__ inline void window_accumulate(const float* tbl, const RowWindow<MODE, WIN>& r, float& acc,
+                                         float& accg, int& gpos, int group_sbs) {
+  if constexpr (GI < WIN) {
+    const float sb = superblock_sum<GI>(tbl, r.nb[GI], r.sg[GI]);
+    if constexpr (MODE == kGroup1) {
+      acc += r.al[GI] * sb;
+    } else if constexpr (MODE == kGroupN) {
+      accg += sb;
+      if (++gpos == group_sbs) {
+        acc += r.al[GI] * accg;
+        accg = 0.f;
+        gpos = 0;
+      }
+    } else {
+      acc += sb;
+    }
+    window_accumulate<MODE, WIN, GI + 1>(tbl, r, acc, accg, gpos, group_sbs);
+  }
+}
+
+// Batch-1 GEMV.  Workgroup = 256 threads = 256 rows x M row slots; K range =
+// one split; LDS holds the tables of WIN superblocks at a time (WIN*4 KB).
+// For each window: build the tables, then per row slot issue the whole
+// row-window of loads (WIN x 24 bytes per lane, non-temporal: read once) and
+// consume it.  Latency is hidden by occupancy: at ~55 VGPRs and 16 KB of LDS
+// per workgroup, 8 waves share each SIMD.
+template <int MODE, int WIN, int M, bool YBF16>
 __global__ __launch_bounds__(kLutThreads) void gemv_b1_lut_kernel(
     const uint8_t* __restrict__ packed, const float* __restrict__ alpha,
     const uint16_t* __restrict__ x, void* __restrict__ y, float* __restrict__ partial, int64_t n,
-    int64_t k, int group_sbs, int window_sbs, int ksplit, int64_t packed_stride,
-    int64_t alpha_stride, int64_t y_stride) {
-  extern __shared__ float tbl[];
+    int64_t k, int group_sbs, int ksplit, int64_t packed_stride, int64_t alpha_stride,
+    int64_t y_stride) {
+  __shared__ __attribute__((aligned(16))) float tbl[WIN * kTableFloatsPerSb];
   const int tid = threadIdx.x;
   const int64_t c = blockIdx.y;
   const int kz = blockIdx.z;
   const int64_t nsb = k / kSuperblock;
   const int64_t sb_per_split = nsb / ksplit;
   const int64_t sb_begin = kz * sb_per_split;
-  const int64_t sb_end = sb_begin + sb_per_split;
+  const int nwin = (int)(sb_per_split / WIN);
 
   const uint8_t* pk = packed + c * packed_stride;
-  const uint4* __restrict__ nib = reinterpret_cast<const uint4*>(pk);
-  const uint32_t* __restrict__ sgn = reinterpret_cast<const uint32_t*>(pk + nibble_plane_bytes(n, k));
+  const uint8_t* __restrict__ sgn_base = pk + nibble_plane_bytes(n, k);
   const float* __restrict__ al = alpha + c * alpha_stride;
   const int64_t row_base = (int64_t)blockIdx.x * (kLutThreads * M) + tid;
 
-  float acc[M], accg[M];
+  // rows past the end are clamped for loads (their results are not stored)
+  uint32_t rows[M];
 #pragma unroll
-  for (int i = 0; i < M; ++i) acc[i] = accg[i] = 0.f;
+  for (int i = 0; i < M; ++i) {
+    const int64_t r = row_base + (int64_t)i * kLutThreads;
+    rows[i] = (uint32_t)(r < n ? r : n - 1);
+  }
 
-  for (int64_t w0 = sb_begin; w0 < sb_end; w0 += window_sbs) {
-    const int wn = (int)((sb_end - w0) < window_sbs ? (sb_end - w0) : window_sbs);
-    __syncthreads();
-    // Build the window's tables: 4 tasks of 8 entries per block.
-    const int tasks = wn * kBlocksPerSb * 4;
-    for (int task = tid; task < tasks; task += kLutThreads) {
-      const int blk = task >> 2, part = task & 3;
-      const uint2 xv = *reinterpret_cast<const uint2*>(x + w0 * kSuperblock + blk * 4);
-      float xs[4] = {__uint_as_float(xv.x << 16), __uint_as_float(xv.x & 0xFFFF0000u),
-                     __uint_as_float(xv.y << 16), __uint_as_float(xv.y & 0xFFFF0000u)};
-      float e[8];
-      build_entries(xs, part, e);
-      float4* dst = reinterpret_cast<float4*>(tbl + blk * 32 + part * 8);
-      dst[0] = make_float4(e[0], e[1], e[2], e[3]);
-      dst[1] = make_float4(e[4], e[5], e[6], e[7]);
+  float acc[M], accg[M];
+  int gpos[M];
+#pragma unroll
+  for (int i = 0; i < M; ++i) {
+    acc[i] = accg[i] = 0.f;
+    gpos[i] = 0;
+  }
+
+  for (int w = 0; w < nwin; ++w) {
+    const int64_t g0 = sb_begin + (int64_t)w * WIN;
+    __syncthreads();  // previous window's lookups are done
+    for (int task = tid; task < WIN * kBlocksPerSb * 2; task += kLutThreads) {
+      const int blk = task >> 1;
+      build_block_half(tbl + blk * 32, x + g0 * kSuperblock + blk * 4, task & 1);
     }
     __syncthreads();
-
-    const int gpos0 = (int)((w0 - sb_begin) % group_sbs);
 #pragma unroll
     for (int i = 0; i < M; ++i) {
-      const int64_t row = row_base + (int64_t)i * kLutThreads;
-      if (row >= n) continue;
-      int gpos = gpos0;
-#pragma unroll 2
-      for (int gi = 0; gi < wn; ++gi) {
-        const int64_t g = w0 + gi;
-        const uint4 nb = nib[g * n + row];
-        const uint32_t sg = sgn[g * n + row];
-        const char* t = reinterpret_cast<const char*>(tbl + gi * kTableFloatsPerSb);
-        float s[4] = {0.f, 0.f, 0.f, 0.f};
-        const uint32_t nd[4] = {nb.x, nb.y, nb.z, nb.w};
-#pragma unroll
-        for (int q = 0; q < 8; ++q) {
-          const uint32_t off = quad_offsets(nd[q >> 1], sg, q);
-#pragma unroll
-          for (int b = 0; b < 4; ++b) {
-            const uint32_t o = (off >> (8 * b)) & 0xFFu;
-            s[b] += *reinterpret_cast<const float*>(t + (q + 8 * b) * 128 + o);
-          }
-        }
-        const float sb = (s[0] + s[1]) + (s[2] + s[3]);
-        if constexpr (GRAN == SHERRY_PER_GROUP) {
-          accg[i] += sb;
-          if (++gpos == group_sbs) {
-            acc[i] += al[(g / group_sbs) * n + row] * accg[i];
-            accg[i] = 0.f;
-            gpos = 0;
-          }
-        } else {
-          acc[i] += sb;
-        }
-      }
+      RowWindow<MODE, WIN> rw;
+      load_row_window<MODE, WIN>(rw, pk, sgn_base, al, n, rows[i], g0, group_sbs);
+      window_accumulate<MODE, WIN>(tbl, rw, acc[i], accg[i], gpos[i], group_sbs);
     }
   }
 
@@ -160,8 +241,8 @@ __global__ __launch_bounds__(kLutThreads) void gemv_b1_lut_kernel(
     if (row >= n) continue;
     float v = acc[i];
     if (ksplit == 1) {
-      if constexpr (GRAN == SHERRY_PER_CHANNEL) v *= al[row];
-      if constexpr (GRAN == SHERRY_PER_TENSOR) v *= al[0];
+      if constexpr (MODE == kChannel) v *= al[row];
+      if constexpr (MODE == kTensor) v *= al[0];
       store_y<YBF16>(y, c * y_stride + row, v);
     } else {
       partial[(c * ksplit + kz) * n + row] = v;
@@ -298,6 +379,48 @@ __global__ void gemv_split_reduce(const float* __restrict__ partial, const float
   store_y<YBF16>(y, c * y_stride + bn, v);
 }
 
+template <int MODE, int WIN, int M, bool YBF16>
+void launch_lut_one(dim3 grid, size_t lds, hipStream_t s, const uint8_t* packed, const float* alpha,
+                    const uint16_t* x, void* y, float* ws, int64_t n, int64_t k, int group_sbs, int ksplit,
+                    int64_t ps, int64_t as, int64_t ys) {
+  hipLaunchKernelGGL((gemv_b1_lut_kernel<MODE, WIN, M, YBF16>), grid, dim3(kLutThreads), lds, s, packed,
+                     alpha, x, y, ws, n, k, group_sbs, ksplit, ps, as, ys);
+}
+
+template <int MODE, int WIN, bool YBF16>
+void launch_lut_m(int m, dim3 grid, size_t lds, hipStream_t s, const uint8_t* packed, const float* alpha,
+                  const uint16_t* x, void* y, float* ws, int64_t n, int64_t k, int group_sbs, int ksplit,
+                  int64_t ps, int64_t as, int64_t ys) {
+  if (m >= 4) launch_lut_one<MODE, WIN, 4, YBF16>(grid, lds, s, packed, alpha, x, y, ws, n, k, group_sbs, ksplit, ps, as, ys);
+  else if (m == 2) launch_lut_one<MODE, WIN, 2, YBF16>(grid, lds, s, packed, alpha, x, y, ws, n, k, group_sbs, ksplit, ps, as, ys);
+  else launch_lut_one<MODE, WIN, 1, YBF16>(grid, lds, s, packed, alpha, x, y, ws, n, k, group_sbs, ksplit, ps, as, ys);
+}
+
+template <int MODE, bool YBF16>
+void launch_lut_w(int win, int m, dim3 grid, size_t lds, hipStream_t s, const uint8_t* packed,
+                  const float* alpha, const uint16_t* x, void* y, float* ws, int64_t n, int64_t k,
+                  int group_sbs, int ksplit, int64_t ps, int64_t as, int64_t ys) {
+  switch (win) {
+    case 16: launch_lut_m<MODE, 16, YBF16>(m, grid, lds, s, packed, alpha, x, y, ws, n, k, group_sbs, ksplit, ps, as, ys); break;
+    case 8: launch_lut_m<MODE, 8, YBF16>(m, grid, lds, s, packed, alpha, x, y, ws, n, k, group_sbs, ksplit, ps, as, ys); break;
+    case 4: launch_lut_m<MODE, 4, YBF16>(m, grid, lds, s, packed, alpha, x, y, ws, n, k, group_sbs, ksplit, ps, as, ys); break;
+    case 2: launch_lut_m<MODE, 2, YBF16>(m, grid, lds, s, packed, alpha, x, y, ws, n, k, group_sbs, ksplit, ps, as, ys); break;
+    default: launch_lut_m<MODE, 1, YBF16>(m, grid, lds, s, packed, alpha, x, y, ws, n, k, group_sbs, ksplit, ps, as, ys); break;
+  }
+}
+
+template <bool YBF16>
+void launch_lut(int mode, int win, int m, dim3 grid, size_t lds, hipStream_t s, const uint8_t* packed,
+                const float* alpha, const uint16_t* x, void* y, float* ws, int64_t n, int64_t k, int group_sbs,
+                int ksplit, int64_t ps, int64_t as, int64_t ys) {
+  switch (mode) {
+    case kGroup1: launch_lut_w<kGroup1, YBF16>(win, m, grid, lds, s, packed, alpha, x, y, ws, n, k, group_sbs, ksplit, ps, as, ys); break;
+    case kGroupN: launch_lut_w<kGroupN, YBF16>(win, m, grid, lds, s, packed, alpha, x, y, ws, n, k, group_sbs, ksplit, ps, as, ys); break;
+    case kChannel: launch_lut_w<kChannel, YBF16>(win, m, grid, lds, s, packed, alpha, x, y, ws, n, k, group_sbs, ksplit, ps, as, ys); break;
+    default: launch_lut_w<kTensor, YBF16>(win, m, grid, lds, s, packed, alpha, x, y, ws, n, k, group_sbs, ksplit, ps, as, ys); break;
+  }
+}
+
 template <int GRAN, bool YBF16>
 hipError_t launch_gemv_t(const GemvPlan& p, int64_t n, int64_t k, int group_size,
                          const uint8_t* packed, const float* alpha, const uint16_t* x, int batch,
@@ -306,24 +429,12 @@ hipError_t launch_gemv_t(const GemvPlan& p, int64_t n, int64_t k, int group_size
   const int group_sbs = GRAN == SHERRY_PER_GROUP ? group_size / kSuperblock : 1;
   const dim3 grid((unsigned)p.panels, (unsigned)count, (unsigned)p.ksplit);
   if (p.kind == 0) {
-    const size_t lds = (size_t)p.window_sbs * kTableFloatsPerSb * sizeof(float);
-    switch (p.rows_per_thread) {
-      case 1:
-        hipLaunchKernelGGL((gemv_b1_lut_kernel<GRAN, 1, YBF16>), grid, dim3(kLutThreads), lds, s, packed,
-                           alpha, x, y, ws, n, k, group_sbs, p.window_sbs, p.ksplit, packed_stride,
-                           alpha_stride, y_stride);
-        break;
-      case 2:
-        hipLaunchKernelGGL((gemv_b1_lut_kernel<GRAN, 2, YBF16>), grid, dim3(kLutThreads), lds, s, packed,
-                           alpha, x, y, ws, n, k, group_sbs, p.window_sbs, p.ksplit, packed_stride,
-                           alpha_stride, y_stride);
-        break;
-      default:
-        hipLaunchKernelGGL((gemv_b1_lut_kernel<GRAN, 4, YBF16>), grid, dim3(kLutThreads), lds, s, packed,
-                           alpha, x, y, ws, n, k, group_sbs, p.window_sbs, p.ksplit, packed_stride,
-                           alpha_stride, y_stride);
-        break;
-    }
+    const size_t lds = 0;  // the table is static LDS sized by the window
+    const int mode = GRAN == SHERRY_PER_CHANNEL ? kChannel
+                   : GRAN == SHERRY_PER_TENSOR  ? kTensor
+                   : (group_sbs == 1 ? kGroup1 : kGroupN);
+    launch_lut<YBF16>(mode, p.window_sbs, p.rows_per_thread, grid, lds, s, packed, alpha, x, y, ws, n, k,
+                      group_sbs, p.ksplit, packed_stride, alpha_stride, y_stride);
   } else {
     hipLaunchKernelGGL((gemv_mfma_kernel<GRAN, YBF16>), grid, dim3(256), 0, s, packed, alpha, x, y, ws, n,
                        k, group_sbs, batch, p.ksplit, packed_stride, alpha_stride, y_stride);
@@ -345,9 +456,9 @@ GemvPlan plan_gemv(int64_t n, int64_t k, int gran, int group_size, int batch, in
   p.kind = batch == 1 ? 0 : 1;
   int64_t rows_per_wg;
   if (p.kind == 0) {
-    // more rows per thread amortize the table build once the grid is large
+    // four row slots per thread amortize the table build once the grid is large
     const int64_t wg1 = ((n + kLutThreads - 1) / kLutThreads) * count;
-    p.rows_per_thread = wg1 >= 8192 ? 4 : (wg1 >= 4096 ? 2 : 1);
+    p.rows_per_thread = wg1 >= 4096 ? SHERRY_LUT_ROWS : 1;
     rows_per_wg = (int64_t)kLutThreads * p.rows_per_thread;
   } else {
     p.rows_per_thread = 1;
@@ -361,7 +472,9 @@ GemvPlan plan_gemv(int64_t n, int64_t k, int gran, int group_size, int batch, in
   while (wgs * split * 2 <= 1024 && groups % (split * 2) == 0) split *= 2;
   p.ksplit = (int)split;
   const int64_t sb_per_split = nsb / split;
-  p.window_sbs = (int)(sb_per_split < 16 ? sb_per_split : 16);
+  int win = SHERRY_LUT_WIN_MAX;
+  while (sb_per_split % win != 0) win >>= 1;
+  p.window_sbs = win;
   p.workspace_bytes = split > 1 ? (size_t)count * split * batch * n * sizeof(float) : 0;
   return p;
 }

@@ -1,24 +1,32 @@
 // Prefill product Y[m, n] = sum_k X[m, k] * T[n, k] * alpha(n, k) on bf16 MFMA.
 //
 // Method: "Sherry, Tequila and Fairies in Python", section 1.1 (SherryLinear:
-// F.linear with the dequantized ternary weight; activations stay bf16 per the
-// same section and the agihunt digest's limits paragraph).
+// F.linear with the dequantized ternary weight); activations stay bf16 (same
+// section, and the agihunt digest's limits paragraph).
 //
-// Tiling: one workgroup (4 waves, 2 x 2) per 128 (n) x 128 (m) output tile;
-// each wave owns 64 x 64 = 4 x 4 tiles of v_mfma_f32_16x16x32_bf16.  The K
-// loop steps one superblock (128 = one scale group at G = 128) at a time:
-//   1. X[m0:m0+128, k0:k0+128] (bf16) is copied to LDS with dwordx4 loads;
-//   2. the packed weights of rows n0:n0+128 are decoded to bf16 {-1, 0, +1}
-//      and written to LDS;
-//   3. 4 k-steps of 32 run 16 MFMAs each per wave into a per-group fp32
-//      accumulator, which is then scaled by alpha(n, group) and added to the
-//      output accumulator in fp32 (per_group); per_channel / per_tensor
-//      accumulate directly and scale once at the end.
-// LDS rows are 256 bytes (128 bf16); 16-byte chunks are XOR-swizzled by the
-// row index so the 16 rows read by one MFMA operand load hit distinct banks.
-// The MFMA A operand is the weight tile (M index = n) and B the activations
-// (N index = m), so each lane's four accumulators are four consecutive n of
-// one output row m: one 8-byte bf16 store per tile.
+// Tiling: one workgroup of 4 waves (2 x 2) per BM (m) x BN (n) output tile;
+// a wave owns (BM/2) x (BN/2) as 16 x 16 tiles of v_mfma_f32_16x16x32_bf16
+// with the weight tile as the A operand (MFMA row = n) and the activations as
+// B (MFMA column = m), so each lane's four accumulators are four consecutive n
+// of one output row: one 8-byte bf16 store per tile.
+//
+// K loop: stages of 64 (half a 128-weight superblock), double-buffered in
+// LDS.  While the MFMAs of stage s run, the threads fetch stage s+1 into
+// registers: X with dwordx4 loads, and the packed weight record of their row.
+// After the MFMAs they store X to LDS and decode the weights: a byte of a
+// nibble dword holds two consecutive blocks (8 consecutive k), and with their
+// two adjacent sign bits it forms a 10-bit index into a 16 KB LDS table of
+// ready-made 16-byte bf16 chunks {-1, 0, +1}; one ds_read_b128 + one
+// ds_write_b128 decode 8 weights.  LDS rows are 128 bytes (64 bf16); 16-byte
+// chunks are XOR-swizzled by (row & 7) so MFMA operand loads are
+// conflict-free.
+//
+// Scales: per_group keeps an fp32 accumulator per group (over its 2 or more
+// stages) and adds alpha(n, group) * acc_g to the output accumulator in fp32
+// when the group ends; per_channel / per_tensor accumulate directly and scale
+// once in the epilogue.
+#include <type_traits>
+
 #include "sherry_internal.h"
 
 namespace sherry {
@@ -28,13 +36,17 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int kTile = 128;
-constexpr int kRowBytes = kTile * 2;  // one LDS row: 128 bf16
+constexpr int kStageK = 64;                 // k per LDS stage
+constexpr int kRowBytes = kStageK * 2;      // one LDS row: 64 bf16
+constexpr int kChunks = kRowBytes / 16;     // 8 chunks of 8 k per row
 
-// Byte offset of 16-byte chunk `ch` (0..15) of LDS row `row`.
-__device__ inline int swz(int row, int ch) { return row * kRowBytes + ((ch ^ (row & 15)) << 4); }
+#ifndef SHERRY_GEMM_SWZ
+#define SHERRY_GEMM_SWZ 1  // 0: chunk ^ (row & 7); 1: chunk ^ ((row >> 1) & 7)
+#endif
+__device__ inline int swz_key(int row) { return SHERRY_GEMM_SWZ ? ((row >> 1) & 7) : (row & 7); }
+__device__ inline int swz(int row, int ch) { return row * kRowBytes + ((ch ^ swz_key(row)) << 4); }
 
-// bf16 patterns of one block (4 weights) from its 5-bit code: two dwords.
+// bf16 patterns of one block (4 weights) from its 5-bit code.
 __device__ inline uint2 decode_bf16(uint32_t code) {
   const uint32_t z = (code >> 2) & 3;
   const uint32_t neg0 = (code >> 4) & 1;
@@ -51,127 +63,251 @@ __device__ inline uint2 decode_bf16(uint32_t code) {
   return make_uint2(h[0] | (h[1] << 16), h[2] | (h[3] << 16));
 }
 
-template <int GRAN>
-__global__ __launch_bounds__(256) void gemm_kernel(const uint8_t* __restrict__ packed,
-                                                   const float* __restrict__ alpha,
-                                                   const uint16_t* __restrict__ x,
-                                                   uint16_t* __restrict__ y, int64_t n, int64_t k,
-                                                   int64_t m, int group_sbs) {
-  __shared__ __attribute__((aligned(16))) char xs[kTile * kRowBytes];
-  __shared__ __attribute__((aligned(16))) char ws[kTile * kRowBytes];
+template <int GRAN, int BM, int BN>
+struct GemmCfg {
+  static constexpr int WM = BM / 2, WN = BN / 2;   // wave tile (m, n)
+  static constexpr int TM = WM / 16, TN = WN / 16; // MFMA tiles per wave
+  static constexpr int XLOADS = BM / 32;           // 1 KB X copies per wave per stage (8 rows each)
+  static constexpr int VM_PER_STAGE = XLOADS + 2;  // + nibble and sign record copies
+  static constexpr bool kGroup = GRAN == SHERRY_PER_GROUP;
+};
+
+// s_waitcnt with only a vmcnt limit (expcnt / lgkmcnt left at their maxima).
+template <int VM>
+__device__ inline void wait_vmcnt() {
+  static_assert(VM >= 0 && VM < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((VM & 15) | (7 << 4) | (15 << 8) | ((VM >> 4) << 14));
+}
+
+// Direct global -> LDS copy: lane l of the wave writes lds_wave_base + size*l
+// (the LDS base is wave-uniform; inactive lanes write nothing).
+typedef __attribute__((address_space(3))) void lds_void;
+__device__ inline void g2l_16(const void* g, void* lds_wave_base) {
+  __builtin_amdgcn_global_load_lds(const_cast<void*>(g), (lds_void*)lds_wave_base, 16, 0, 0);
+}
+__device__ inline void g2l_4(const void* g, void* lds_wave_base) {
+  __builtin_amdgcn_global_load_lds(const_cast<void*>(g), (lds_void*)lds_wave_base, 4, 0, 0);
+}
+
+// Workgroup barrier that orders LDS only: this wave's LDS reads and writes
+// are complete (lgkmcnt 0) before it arrives.  Unlike __syncthreads it does
+// not wait for vector-memory operations, so direct copies for later stages
+// stay in flight; their completion is waited for explicitly (vmcnt) before
+// the barrier that publishes them.  The memory clobber keeps the compiler
+// from moving LDS accesses across it.
+__device__ inline void lds_barrier() {
+  __builtin_amdgcn_s_waitcnt(15 | (7 << 4) | (0 << 8) | (3 << 14));
+  asm volatile("s_barrier" ::: "memory");
+}
+
+template <int J>
+using Slot = std::integral_constant<int, J>;
+
+template <int GRAN, int BM, int BN>
+__global__ __launch_bounds__(256, 1) void gemm_kernel(const uint8_t* __restrict__ packed,
+                                                      const float* __restrict__ alpha,
+                                                      const uint16_t* __restrict__ x,
+                                                      uint16_t* __restrict__ y, int64_t n, int64_t k,
+                                                      int64_t m, int group_sbs, int tiles_m, int tiles_n) {
+  using C = GemmCfg<GRAN, BM, BN>;
+  static_assert(BN == 128, "the record copies and the decode assume 128 weight rows");
+  constexpr int kRecBytes = BN * 16 + BN * 4;  // nibble records + sign dwords of one superblock
+  // Three-deep rings, one __shared__ object per slot: the compiler's wait
+  // insertion then knows an LDS read of one slot never aliases the direct
+  // copies in flight into another.
+  __shared__ __attribute__((aligned(16))) char xs0[BM * kRowBytes], xs1[BM * kRowBytes], xs2[BM * kRowBytes];
+  __shared__ __attribute__((aligned(16))) char ws0[BN * kRowBytes], ws1[BN * kRowBytes], ws2[BN * kRowBytes];
+  __shared__ __attribute__((aligned(16))) char rc0[kRecBytes], rc1[kRecBytes], rc2[kRecBytes];
+  __shared__ __attribute__((aligned(16))) uint2 dtab[32];
+
+  auto XS = [&](auto J) -> char* {
+    if constexpr (decltype(J)::value == 0) return xs0; else if constexpr (decltype(J)::value == 1) return xs1; else return xs2;
+  };
+  auto WS = [&](auto J) -> char* {
+    if constexpr (decltype(J)::value == 0) return ws0; else if constexpr (decltype(J)::value == 1) return ws1; else return ws2;
+  };
+  auto RC = [&](auto J) -> char* {
+    if constexpr (decltype(J)::value == 0) return rc0; else if constexpr (decltype(J)::value == 1) return rc1; else return rc2;
+  };
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  const int wn = wave >> 1, wm = wave & 1;  // wave position in the 2 x 2 grid
+  const int wm = wave & 1, wn = wave >> 1;
   const int r = lane & 15, q = lane >> 4;
-  const int64_t n0 = (int64_t)blockIdx.x * kTile;
-  const int64_t m0 = (int64_t)blockIdx.y * kTile;
+
+  // XCD-aware tile order: consecutive workgroup ids land on different XCDs;
+  // give each XCD a contiguous range of tiles (m-major) so its L2 shares X.
+  const int tiles = tiles_m * tiles_n;
+  int bid = blockIdx.x;
+  if ((tiles & 7) == 0) bid = (bid & 7) * (tiles >> 3) + (bid >> 3);
+  const int tm = bid / tiles_n, tn = bid % tiles_n;
+  const int64_t m0 = (int64_t)tm * BM;
+  const int64_t n0 = (int64_t)tn * BN;
+
+  if (tid < 32) dtab[tid] = decode_bf16(tid);
+
   const int64_t nsb = k / kSuperblock;
-  const uint32_t* __restrict__ nibw = reinterpret_cast<const uint32_t*>(packed);
-  const uint32_t* __restrict__ sgn = reinterpret_cast<const uint32_t*>(packed + nibble_plane_bytes(n, k));
+  const int stages = (int)(nsb * 2);
+  const uint8_t* __restrict__ nib_plane = packed;
+  const uint8_t* __restrict__ sgn_plane = packed + nibble_plane_bytes(n, k);
 
-  f32x4 acc[4][4], accg[4][4];
+  // this thread decodes weight row tid/2 (wave w owns rows 32w .. 32w+31)
+  const int wrow = tid >> 1;
+
+  // Direct copies of stage st into ring slot J.  X: wave w copies rows
+  // [w*BM/4, (w+1)*BM/4) in pieces of 8 rows; lane l -> physical chunk l%8 of
+  // row l/8, which holds logical chunk (l%8) ^ swz_key(row).  Records: each
+  // wave copies the 32 rows it decodes (lanes 32..63 idle).
+  auto issue = [&](auto J, int st) {
+    const int64_t kbase = (int64_t)st * kStageK;
+    char* xb = XS(J);
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-      accg[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int i = 0; i < C::XLOADS; ++i) {
+      const int row = (wave * C::XLOADS + i) * 8 + (lane >> 3);
+      const int ch = (lane & 7) ^ swz_key(row);
+      int64_t gm = m0 + row;
+      gm = gm < m ? gm : m - 1;  // clamped rows feed only outputs that are not stored
+      g2l_16(x + gm * k + kbase + ch * 8, xb + (wave * C::XLOADS + i) * 1024);
     }
+    char* rb = RC(J);
+    const int64_t g = st >> 1;
+    int64_t gn = n0 + wave * 32 + (lane & 31);
+    gn = gn < n ? gn : n - 1;
+    if (lane < 32) {
+      g2l_16(nib_plane + (g * n + gn) * 16, rb + wave * 512);
+      g2l_4(sgn_plane + (g * n + gn) * 4, rb + BN * 16 + wave * 128);
+    }
+  };
+  // Decode stage st from record slot J into the bf16 tile slot J: byte
+  // cb = 2*(st&1) + (tid&1) of nibble dword d holds blocks 8cb + 2d and
+  // 8cb + 2d + 1 = the 8 weights of chunk d + 4cb.
+  auto decode = [&](auto J, int st) {
+    const char* rb = RC(J);
+    char* wb = WS(J);
+    const int cb = 2 * (st & 1) + (tid & 1);
+    const uint4 nr = *reinterpret_cast<const uint4*>(rb + wrow * 16);
+    const uint32_t sg = *reinterpret_cast<const uint32_t*>(rb + BN * 16 + wrow * 4);
+    const uint32_t nd[4] = {nr.x, nr.y, nr.z, nr.w};
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+      const uint32_t byte = __builtin_amdgcn_ubfe(nd[d], 8 * cb, 8);
+      const uint32_t s2 = __builtin_amdgcn_ubfe(sg, 2 * d + 8 * cb, 2);
+      const uint2 lo = dtab[(byte & 15u) | ((s2 & 1u) << 4)];
+      const uint2 hi = dtab[(byte >> 4) | ((s2 >> 1) << 4)];
+      const int ch = d + 4 * (cb & 1);  // chunk inside this stage's 8
+      *reinterpret_cast<u32x4*>(wb + swz(wrow, ch)) = u32x4{lo.x, lo.y, hi.x, hi.y};
+    }
+  };
 
+  f32x4 acc[C::TN][C::TM];
+  f32x4 accg[C::kGroup ? C::TN : 1][C::kGroup ? C::TM : 1];
+#pragma unroll
+  for (int i = 0; i < C::TN; ++i)
+#pragma unroll
+    for (int j = 0; j < C::TM; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  if constexpr (C::kGroup) {
+#pragma unroll
+    for (int i = 0; i < C::TN; ++i)
+#pragma unroll
+      for (int j = 0; j < C::TM; ++j) accg[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
   int gpos = 0;
-  for (int64_t g = 0; g < nsb; ++g) {
-    __syncthreads();
-    // 1. activations: 128 rows x 16 chunks of 16 B; thread -> 8 chunks
-#pragma unroll
-    for (int it = 0; it < 8; ++it) {
-      const int idx = it * 256 + tid;
-      const int row = idx >> 4, ch = idx & 15;
-      const int64_t gm = m0 + row;
-      u32x4 v = {0u, 0u, 0u, 0u};
-      if (gm < m) v = *reinterpret_cast<const u32x4*>(x + gm * k + g * kSuperblock + ch * 8);
-      *reinterpret_cast<u32x4*>(xs + swz(row, ch)) = v;
-    }
-    // 2. weights: thread -> (row tid/2, 16 blocks = 8 chunks)
-    {
-      const int row = tid >> 1, hb = tid & 1;
-      const int64_t gn = n0 + row;
-      uint32_t nd[4] = {0u, 0u, 0u, 0u};
-      uint32_t sg = 0;
-      if (gn < n) {
-        const uint4 v = reinterpret_cast<const uint4*>(nibw)[g * n + gn];
-        nd[0] = v.x; nd[1] = v.y; nd[2] = v.z; nd[3] = v.w;
-        sg = sgn[g * n + gn];
-      }
-#pragma unroll
-      for (int c2 = 0; c2 < 8; ++c2) {
-        const int j0 = hb * 16 + 2 * c2;  // blocks j0, j0+1 -> chunk j0/2
-        uint2 a = make_uint2(0u, 0u), b = make_uint2(0u, 0u);
-        if (gn < n) {
-          const uint32_t ja = j0, jb = j0 + 1;
-          const uint32_t ca = (((nd[(ja & 7) >> 1] >> (4 * (ja & 1) + 8 * (ja >> 3))) & 15u)) | (((sg >> ja) & 1u) << 4);
-          const uint32_t cb = (((nd[(jb & 7) >> 1] >> (4 * (jb & 1) + 8 * (jb >> 3))) & 15u)) | (((sg >> jb) & 1u) << 4);
-          a = decode_bf16(ca);
-          b = decode_bf16(cb);
-        }
-        const u32x4 v = {a.x, a.y, b.x, b.y};
-        *reinterpret_cast<u32x4*>(ws + swz(row, j0 >> 1)) = v;
-      }
-    }
-    __syncthreads();
 
-    // 3. MFMA: 4 k-steps of 32
+  // One stage: stage st sits in slot J = st % 3.
+  auto stage = [&](auto J, int st) {
+    constexpr int j = decltype(J)::value;
+    constexpr int j1 = (j + 1) % 3, j2 = (j + 2) % 3;
+    // per_group: this stage ends a group -> load the group's scales first, so
+    // the wait for them does not include the copies issued below
+    const bool group_end = C::kGroup && (st & 1) == 1 && gpos + 1 == group_sbs;
+    float av[C::kGroup ? C::TN : 1][4];
+    if constexpr (C::kGroup) {
+      if (group_end) {
+        const int64_t gg = (st >> 1) / group_sbs;
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
-      const int ch = kk * 4 + q;  // this lane's 8 k values
-      bf16x8 a[4], b[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        a[i] = *reinterpret_cast<const bf16x8*>(ws + swz(wn * 64 + i * 16 + r, ch));
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-        b[j] = *reinterpret_cast<const bf16x8*>(xs + swz(wm * 64 + j * 16 + r, ch));
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          if constexpr (GRAN == SHERRY_PER_GROUP) {
-            accg[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i], b[j], accg[i][j], 0, 0, 0);
-          } else {
-            acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
-          }
-        }
-    }
-
-    if constexpr (GRAN == SHERRY_PER_GROUP) {
-      if (++gpos == group_sbs) {
-        const int64_t gg = g / group_sbs;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          // accumulator element e of tile i is weight row n0 + wn*64 + 16i + 4q + e
-          float av[4];
+        for (int i = 0; i < C::TN; ++i)
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
-            const int64_t gn = n0 + wn * 64 + i * 16 + 4 * q + e;
-            av[e] = gn < n ? alpha[gg * n + gn] : 0.f;
+            int64_t gn = n0 + wn * C::WN + i * 16 + 4 * q + e;
+            gn = gn < n ? gn : n - 1;  // clamped rows are not stored
+            av[i][e] = alpha[gg * n + gn];
           }
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-#pragma unroll
-            for (int e = 0; e < 4; ++e) acc[i][j][e] += av[e] * accg[i][j][e];
-            accg[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-          }
-        }
-        gpos = 0;
       }
     }
+    // copies two stages ahead (slot j2 was consumed in the previous stage)
+    const bool ahead = st + 2 < stages;
+    if (ahead) issue(Slot<j2>{}, st + 2);
+
+    const char* xb = XS(J);
+    const char* wb = WS(J);
+#pragma unroll
+    for (int kk = 0; kk < kStageK / 32; ++kk) {
+      const int ch = kk * 4 + q;
+      bf16x8 a[C::TN], b[C::TM];
+#pragma unroll
+      for (int i = 0; i < C::TN; ++i)
+        a[i] = *reinterpret_cast<const bf16x8*>(wb + swz(wn * C::WN + i * 16 + r, ch));
+#pragma unroll
+      for (int jj = 0; jj < C::TM; ++jj)
+        b[jj] = *reinterpret_cast<const bf16x8*>(xb + swz(wm * C::WM + jj * 16 + r, ch));
+#pragma unroll
+      for (int i = 0; i < C::TN; ++i)
+#pragma unroll
+        for (int jj = 0; jj < C::TM; ++jj) {
+          if constexpr (C::kGroup) {
+            accg[i][jj] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i], b[jj], accg[i][jj], 0, 0, 0);
+          } else {
+            acc[i][jj] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i], b[jj], acc[i][jj], 0, 0, 0);
+          }
+        }
+    }
+
+    if constexpr (C::kGroup) {
+      if ((st & 1) == 1) {
+        if (group_end) {
+#pragma unroll
+          for (int i = 0; i < C::TN; ++i)
+#pragma unroll
+            for (int jj = 0; jj < C::TM; ++jj) {
+#pragma unroll
+              for (int e = 0; e < 4; ++e) acc[i][jj][e] += av[i][e] * accg[i][jj][e];
+              accg[i][jj] = f32x4{0.f, 0.f, 0.f, 0.f};
+            }
+          gpos = 0;
+        } else {
+          ++gpos;
+        }
+      }
+    }
+
+    if (st + 1 < stages) {
+      // this wave's copies of stage st+1 (issued one stage ago) have landed;
+      // only this stage's copies may still be in flight
+      if (ahead) wait_vmcnt<C::VM_PER_STAGE>(); else wait_vmcnt<0>();
+      decode(Slot<j1>{}, st + 1);
+    }
+    lds_barrier();
+  };
+
+  // prologue: stages 0 and 1 copied, stage 0 decoded
+  issue(Slot<0>{}, 0);
+  if (stages > 1) issue(Slot<1>{}, 1);
+  if (stages > 1) wait_vmcnt<C::VM_PER_STAGE>(); else wait_vmcnt<0>();
+  lds_barrier();  // decode table written
+  decode(Slot<0>{}, 0);
+  lds_barrier();
+
+  for (int st = 0; st < stages; st += 3) {
+    stage(Slot<0>{}, st);
+    if (st + 1 < stages) stage(Slot<1>{}, st + 1);
+    if (st + 2 < stages) stage(Slot<2>{}, st + 2);
   }
 
-  // epilogue: lane holds Y[m0 + wm*64 + 16j + r][n0 + wn*64 + 16i + 4q + e]
+  // epilogue: lane holds Y[m0 + wm*WM + 16j + r][n0 + wn*WN + 16i + 4q + e]
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int64_t gn0 = n0 + wn * 64 + i * 16 + 4 * q;
+  for (int i = 0; i < C::TN; ++i) {
+    const int64_t gn0 = n0 + wn * C::WN + i * 16 + 4 * q;
     float sc[4] = {1.f, 1.f, 1.f, 1.f};
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
@@ -179,12 +315,12 @@ __global__ __launch_bounds__(256) void gemm_kernel(const uint8_t* __restrict__ p
       if constexpr (GRAN == SHERRY_PER_TENSOR) sc[e] = alpha[0];
     }
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int64_t gm = m0 + wm * 64 + j * 16 + r;
+    for (int jj = 0; jj < C::TM; ++jj) {
+      const int64_t gm = m0 + wm * C::WM + jj * 16 + r;
       if (gm >= m) continue;
       uint16_t h[4];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) h[e] = f32_to_bf16_rne(acc[i][j][e] * sc[e]);
+      for (int e = 0; e < 4; ++e) h[e] = f32_to_bf16_rne(acc[i][jj][e] * sc[e]);
       uint16_t* dst = y + gm * n + gn0;
       if (gn0 + 3 < n && (n & 3) == 0) {
         *reinterpret_cast<uint2*>(dst) = make_uint2(h[0] | ((uint32_t)h[1] << 16), h[2] | ((uint32_t)h[3] << 16));
@@ -196,13 +332,35 @@ __global__ __launch_bounds__(256) void gemm_kernel(const uint8_t* __restrict__ p
   }
 }
 
+template <int GRAN, int BM>
+hipError_t launch_t(int64_t n, int64_t k, int group_sbs, const uint8_t* packed, const float* alpha,
+                    const uint16_t* x, int64_t m, uint16_t* y, hipStream_t s) {
+  constexpr int BN = 128;
+  const int tiles_m = (int)((m + BM - 1) / BM), tiles_n = (int)((n + BN - 1) / BN);
+  hipLaunchKernelGGL((gemm_kernel<GRAN, BM, BN>), dim3((unsigned)(tiles_m * tiles_n)), dim3(256), 0, s, packed,
+                     alpha, x, y, n, k, m, group_sbs, tiles_m, tiles_n);
+  return hipGetLastError();
+}
+
+template <int GRAN>
+hipError_t launch_g(int tile_m, int64_t n, int64_t k, int group_sbs, const uint8_t* packed, const float* alpha,
+                    const uint16_t* x, int64_t m, uint16_t* y, hipStream_t s) {
+  if constexpr (GRAN != SHERRY_PER_GROUP) {
+    if (tile_m == 256) return launch_t<GRAN, 256>(n, k, group_sbs, packed, alpha, x, m, y, s);
+  }
+  return launch_t<GRAN, 128>(n, k, group_sbs, packed, alpha, x, m, y, s);
+}
+
 }  // namespace
 
 GemmPlan plan_gemm(int64_t n, int64_t k, int gran, int group_size, int64_t m) {
-  (void)n; (void)k; (void)gran; (void)group_size; (void)m;
+  (void)k; (void)group_size;
   GemmPlan p{};
-  p.tile_n = kTile;
-  p.tile_m = kTile;
+  p.tile_n = 128;
+  // 256-row tiles once they still give >= 2 tiles per CU; per_group keeps a
+  // second accumulator set per wave, which only fits at 128 rows
+  const int64_t big = ((m + 255) / 256) * ((n + 127) / 128);
+  p.tile_m = (big >= 512 && gran != SHERRY_PER_GROUP) ? 256 : 128;
   p.workspace_bytes = 0;
   return p;
 }
@@ -210,16 +368,10 @@ GemmPlan plan_gemm(int64_t n, int64_t k, int gran, int group_size, int64_t m) {
 hipError_t launch_gemm(const GemmPlan& p, int64_t n, int64_t k, int gran, int group_size,
                        const uint8_t* packed, const float* alpha, const uint16_t* x, int64_t m,
                        uint16_t* y, hipStream_t s) {
-  const dim3 grid((unsigned)((n + p.tile_n - 1) / p.tile_n), (unsigned)((m + p.tile_m - 1) / p.tile_m));
   const int group_sbs = gran == SHERRY_PER_GROUP ? group_size / kSuperblock : 1;
-  if (gran == SHERRY_PER_GROUP) {
-    hipLaunchKernelGGL(gemm_kernel<SHERRY_PER_GROUP>, grid, dim3(256), 0, s, packed, alpha, x, y, n, k, m, group_sbs);
-  } else if (gran == SHERRY_PER_CHANNEL) {
-    hipLaunchKernelGGL(gemm_kernel<SHERRY_PER_CHANNEL>, grid, dim3(256), 0, s, packed, alpha, x, y, n, k, m, group_sbs);
-  } else {
-    hipLaunchKernelGGL(gemm_kernel<SHERRY_PER_TENSOR>, grid, dim3(256), 0, s, packed, alpha, x, y, n, k, m, group_sbs);
-  }
-  return hipGetLastError();
+  if (gran == SHERRY_PER_GROUP) return launch_g<SHERRY_PER_GROUP>(p.tile_m, n, k, group_sbs, packed, alpha, x, m, y, s);
+  if (gran == SHERRY_PER_CHANNEL) return launch_g<SHERRY_PER_CHANNEL>(p.tile_m, n, k, group_sbs, packed, alpha, x, m, y, s);
+  return launch_g<SHERRY_PER_TENSOR>(p.tile_m, n, k, group_sbs, packed, alpha, x, m, y, s);
 }
 
 }  // namespace sherry

@@ -268,7 +268,17 @@ __device__ inline uint32_t decode_table_entry(uint32_t code) {
   return e;
 }
 
-template <int GRAN, bool YBF16>
+// Batch 2..16.  Workgroup = 4 waves; a wave owns 4 tiles of 16 rows (64
+// rows) so every activation fragment feeds 4 MFMAs.  Per window of MWIN
+// superblocks, a lane first loads, for each of its 4 rows, nibble dword q and
+// the sign dword of every superblock (and the group scales), then runs the
+// MFMAs: lane (r, q) supplies blocks 2q+8t and 2q+1+8t (t = 0..3) of row r,
+// i.e. k = 32t + 8q .. +7 of the superblock, and the activations of batch row
+// r at the same k.
+constexpr int kMfmaTiles = 4;
+constexpr int kMfmaWin = 4;
+
+template <int MODE, bool YBF16>
 __global__ __launch_bounds__(256) void gemv_mfma_kernel(
     const uint8_t* __restrict__ packed, const float* __restrict__ alpha,
     const uint16_t* __restrict__ x, void* __restrict__ y, float* __restrict__ partial, int64_t n,
@@ -280,10 +290,9 @@ __global__ __launch_bounds__(256) void gemv_mfma_kernel(
 
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
-  const int r = lane & 15;  // weight row inside the 16-row tile / batch row of x
-  const int q = lane >> 4;  // k-quarter: nibble dword q of each superblock record
-  const int64_t row = (int64_t)blockIdx.x * 64 + wave * 16 + r;
-  const bool valid = row < n;
+  const int r = lane & 15;  // weight row inside a 16-row tile / batch row of x
+  const int q = lane >> 4;  // nibble dword q of each superblock record
+  const int64_t row0 = (int64_t)blockIdx.x * 256 + wave * 64 + r;
   const int64_t c = blockIdx.y;
   const int kz = blockIdx.z;
   const int64_t nsb = k / kSuperblock;
@@ -292,69 +301,108 @@ __global__ __launch_bounds__(256) void gemv_mfma_kernel(
   const int64_t sb_end = sb_begin + sb_per_split;
 
   const uint8_t* pk = packed + c * packed_stride;
-  const uint32_t* __restrict__ nibw = reinterpret_cast<const uint32_t*>(pk);
-  const uint32_t* __restrict__ sgn = reinterpret_cast<const uint32_t*>(pk + nibble_plane_bytes(n, k));
+  const uint8_t* __restrict__ sgn_base = pk + nibble_plane_bytes(n, k);
   const float* __restrict__ al = alpha + c * alpha_stride;
   const bool has_x = r < batch;
   const uint16_t* xrow = x + (int64_t)(has_x ? r : 0) * k;
   const char* dt = reinterpret_cast<const char*>(dtbl);
+  constexpr bool kGroup = MODE == kGroup1 || MODE == kGroupN;
 
-  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-  f32x4 accg = {0.f, 0.f, 0.f, 0.f};
-  int gpos = 0;
-  for (int64_t g = sb_begin; g < sb_end; ++g) {
-    uint32_t nd = 0, sg = 0;
-    if (valid) {
-      nd = nibw[(g * n + row) * 4 + q];
-      sg = sgn[g * n + row];
-    }
-    // blocks 2q + 8t (low nibbles) and 2q + 1 + 8t (high nibbles), t = 0..3
-    const uint32_t off_lo = quad_offsets(nd, sg, 2 * q);
-    const uint32_t off_hi = quad_offsets(nd, sg, 2 * q + 1);
+  uint32_t rows[kMfmaTiles];
 #pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      const uint32_t e0 = *reinterpret_cast<const uint32_t*>(dt + ((off_lo >> (8 * t)) & 0xFFu));
-      const uint32_t e1 = *reinterpret_cast<const uint32_t*>(dt + ((off_hi >> (8 * t)) & 0xFFu));
-      u32x4 wv;
-      wv[0] = __builtin_amdgcn_perm(0u, e0, 0x010C000Cu);
-      wv[1] = __builtin_amdgcn_perm(0u, e0, 0x030C020Cu);
-      wv[2] = __builtin_amdgcn_perm(0u, e1, 0x010C000Cu);
-      wv[3] = __builtin_amdgcn_perm(0u, e1, 0x030C020Cu);
-      u32x4 xv = {0u, 0u, 0u, 0u};
-      if (has_x) xv = *reinterpret_cast<const u32x4*>(xrow + g * kSuperblock + 32 * t + 8 * q);
-      if constexpr (GRAN == SHERRY_PER_GROUP) {
-        accg = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, xv),
-                                                       __builtin_bit_cast(bf16x8, wv), accg, 0, 0, 0);
-      } else {
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, xv),
-                                                      __builtin_bit_cast(bf16x8, wv), acc, 0, 0, 0);
+  for (int i = 0; i < kMfmaTiles; ++i) {
+    const int64_t rr = row0 + i * 16;
+    rows[i] = (uint32_t)(rr < n ? rr : n - 1);  // clamped rows are not stored
+  }
+
+  f32x4 acc[kMfmaTiles], accg[kMfmaTiles];
+#pragma unroll
+  for (int i = 0; i < kMfmaTiles; ++i) {
+    acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+    accg[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+  int gpos = 0;
+
+  for (int64_t g0 = sb_begin; g0 < sb_end; g0 += kMfmaWin) {
+    const int wn = (int)((sb_end - g0) < kMfmaWin ? (sb_end - g0) : kMfmaWin);  // last window may be short
+    uint32_t nd[kMfmaWin][kMfmaTiles], sg[kMfmaWin][kMfmaTiles];
+    float av[kMfmaWin][kGroup ? kMfmaTiles : 1];
+#pragma unroll
+    for (int gi = 0; gi < kMfmaWin; ++gi) {
+      const int64_t g = g0 + (gi < wn ? gi : 0);  // short window: repeat a valid record, unused
+#pragma unroll
+      for (int i = 0; i < kMfmaTiles; ++i) {
+        nd[gi][i] = stream_load(reinterpret_cast<const uint32_t*>(pk + g * n * 16 + rows[i] * 16u + q * 4u));
+        sg[gi][i] = stream_load(reinterpret_cast<const uint32_t*>(sgn_base + g * n * 4 + rows[i] * 4u));
+        if constexpr (MODE == kGroup1) av[gi][i] = stream_load(al + g * n + rows[i]);
+        if constexpr (MODE == kGroupN) av[gi][i] = stream_load(al + (g / group_sbs) * n + rows[i]);
       }
     }
-    if constexpr (GRAN == SHERRY_PER_GROUP) {
-      if (++gpos == group_sbs) {
-        const float a2 = valid ? 2.f * al[(g / group_sbs) * n + row] : 0.f;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) acc[e] += a2 * accg[e];
-        accg = f32x4{0.f, 0.f, 0.f, 0.f};
-        gpos = 0;
+    for (int gi = 0; gi < kMfmaWin; ++gi) {
+      if (gi >= wn) break;
+      const int64_t g = g0 + gi;
+      uint32_t off_lo[kMfmaTiles], off_hi[kMfmaTiles];
+#pragma unroll
+      for (int i = 0; i < kMfmaTiles; ++i) {
+        off_lo[i] = quad_offsets(nd[gi][i], sg[gi][i], 2 * q);      // blocks 2q + 8t
+        off_hi[i] = quad_offsets(nd[gi][i], sg[gi][i], 2 * q + 1);  // blocks 2q + 1 + 8t
+      }
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        u32x4 xv = {0u, 0u, 0u, 0u};
+        if (has_x) xv = *reinterpret_cast<const u32x4*>(xrow + g * kSuperblock + 32 * t + 8 * q);
+#pragma unroll
+        for (int i = 0; i < kMfmaTiles; ++i) {
+          const uint32_t e0 = *reinterpret_cast<const uint32_t*>(dt + __builtin_amdgcn_ubfe(off_lo[i], 8 * t, 8));
+          const uint32_t e1 = *reinterpret_cast<const uint32_t*>(dt + __builtin_amdgcn_ubfe(off_hi[i], 8 * t, 8));
+          u32x4 wv;
+          wv[0] = __builtin_amdgcn_perm(0u, e0, 0x010C000Cu);
+          wv[1] = __builtin_amdgcn_perm(0u, e0, 0x030C020Cu);
+          wv[2] = __builtin_amdgcn_perm(0u, e1, 0x010C000Cu);
+          wv[3] = __builtin_amdgcn_perm(0u, e1, 0x030C020Cu);
+          if constexpr (kGroup) {
+            accg[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, xv),
+                                                             __builtin_bit_cast(bf16x8, wv), accg[i], 0, 0, 0);
+          } else {
+            acc[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, xv),
+                                                            __builtin_bit_cast(bf16x8, wv), acc[i], 0, 0, 0);
+          }
+        }
+      }
+      if constexpr (kGroup) {
+        if (++gpos == group_sbs) {
+#pragma unroll
+          for (int i = 0; i < kMfmaTiles; ++i) {
+            const float a2 = 2.f * av[gi][i];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) acc[i][e] += a2 * accg[i][e];
+            accg[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+          }
+          gpos = 0;
+        }
       }
     }
   }
 
-  if (!valid) return;
-  float scale = 1.f;
-  if constexpr (GRAN != SHERRY_PER_GROUP) scale = 2.f;
+  // lane holds D[batch 4q + e][row r] of each tile
 #pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    const int b = 4 * q + e;  // output row of the MFMA = batch index
-    if (b >= batch) continue;
-    float v = acc[e] * scale;
-    if (ksplit == 1) {
-      if constexpr (GRAN == SHERRY_PER_CHANNEL) v *= al[row];
-      if constexpr (GRAN == SHERRY_PER_TENSOR) v *= al[0];
-      store_y<YBF16>(y, c * y_stride + (int64_t)b * n + row, v);
-    } else {
-      partial[((c * ksplit + kz) * batch + b) * n + row] = v;
+  for (int i = 0; i < kMfmaTiles; ++i) {
+    const int64_t row = row0 + i * 16;
+    if (row >= n) continue;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int b = 4 * q + e;
+      if (b >= batch) continue;
+      float v = acc[i][e];
+      if constexpr (!kGroup) v *= 2.f;
+      if (ksplit == 1) {
+        if constexpr (MODE == kChannel) v *= al[row];
+        if constexpr (MODE == kTensor) v *= al[0];
+        store_y<YBF16>(y, c * y_stride + (int64_t)b * n + row, v);
+      } else {
+        partial[((c * ksplit + kz) * batch + b) * n + row] = v;
+      }
     }
   }
 }
@@ -436,8 +484,17 @@ hipError_t launch_gemv_t(const GemvPlan& p, int64_t n, int64_t k, int group_size
     launch_lut<YBF16>(mode, p.window_sbs, p.rows_per_thread, grid, lds, s, packed, alpha, x, y, ws, n, k,
                       group_sbs, p.ksplit, packed_stride, alpha_stride, y_stride);
   } else {
-    hipLaunchKernelGGL((gemv_mfma_kernel<GRAN, YBF16>), grid, dim3(256), 0, s, packed, alpha, x, y, ws, n,
-                       k, group_sbs, batch, p.ksplit, packed_stride, alpha_stride, y_stride);
+    const int mode = GRAN == SHERRY_PER_CHANNEL ? kChannel
+                   : GRAN == SHERRY_PER_TENSOR  ? kTensor
+                   : (group_sbs == 1 ? kGroup1 : kGroupN);
+#define SHERRY_MFMA_CASE(MD)                                                                                \
+  hipLaunchKernelGGL((gemv_mfma_kernel<MD, YBF16>), grid, dim3(256), 0, s, packed, alpha, x, y, ws, n, k, \
+                     group_sbs, batch, p.ksplit, packed_stride, alpha_stride, y_stride)
+    if (mode == kGroup1) SHERRY_MFMA_CASE(kGroup1);
+    else if (mode == kGroupN) SHERRY_MFMA_CASE(kGroupN);
+    else if (mode == kChannel) SHERRY_MFMA_CASE(kChannel);
+    else SHERRY_MFMA_CASE(kTensor);
+#undef SHERRY_MFMA_CASE
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || p.ksplit == 1) return e;
@@ -462,7 +519,7 @@ GemvPlan plan_gemv(int64_t n, int64_t k, int gran, int group_size, int batch, in
     rows_per_wg = (int64_t)kLutThreads * p.rows_per_thread;
   } else {
     p.rows_per_thread = 1;
-    rows_per_wg = 64;
+    rows_per_wg = 256;
   }
   p.panels = (n + rows_per_wg - 1) / rows_per_wg;
   // Split K (in whole groups) until the launch has ~1024 workgroups.

@@ -186,23 +186,76 @@ __global__ void alpha_channel_kernel(const float* __restrict__ sb, int64_t n, in
   alpha[row] = (float)((double)s / ((double)k / 4.0 * 3.0));
 }
 
-// per_tensor, stage 1: aligned chunks of the row-major sequence of all
-// superblock sums (which is the flat weight order cut at 128).
-__global__ void alpha_tensor_stage1(const float* __restrict__ sb, int64_t total, int64_t chunk,
-                                    int64_t chunks, float* __restrict__ part) {
-  const int64_t c = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (c >= chunks) return;
-  const int64_t begin = c * chunk;
-  const int64_t real = (total - begin < chunk) ? total - begin : chunk;
-  part[c] = tree_sum(sb + begin, real, chunk);
+// per_channel, one wave per row: lane l holds superblock sums E*l .. E*l+E-1
+// of the row (+0 past nsb), reduces them pairwise in registers, and the XOR
+// butterfly over 1..32 continues the tree: the index-order tree over 64*E
+// values, which equals the tree over the row padded to a power of two.
+template <int E>
+__global__ __launch_bounds__(256) void alpha_channel_wave_kernel(const float* __restrict__ sb, int64_t n,
+                                                                 int64_t nsb, int64_t k,
+                                                                 float* __restrict__ alpha) {
+  const int lane = threadIdx.x & 63;
+  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= n) return;
+  float v[E];
+#pragma unroll
+  for (int i = 0; i < E; ++i) {
+    const int64_t idx = (int64_t)lane * E + i;
+    v[i] = idx < nsb ? sb[row * nsb + idx] : 0.f;
+  }
+#pragma unroll
+  for (int w = E; w > 1; w >>= 1)
+#pragma unroll
+    for (int i = 0; i < w / 2; ++i) v[i] = v[2 * i] + v[2 * i + 1];
+  float sum = v[0];
+  sum += __shfl_xor(sum, 1);
+  sum += __shfl_xor(sum, 2);
+  sum += __shfl_xor(sum, 4);
+  sum += __shfl_xor(sum, 8);
+  sum += __shfl_xor(sum, 16);
+  sum += __shfl_xor(sum, 32);
+  if (lane == 0) alpha[row] = (float)((double)sum / ((double)k / 4.0 * 3.0));
 }
 
-// per_tensor, stage 2: tree over the chunk partials (padded with +0).
-__global__ void alpha_tensor_stage2(const float* __restrict__ part, int64_t chunks, int64_t width,
-                                    double denom, float* __restrict__ alpha) {
-  if (blockIdx.x != 0 || threadIdx.x != 0) return;
-  const float s = tree_sum(part, chunks, width);
-  alpha[0] = (float)((double)s / denom);
+// per_tensor: one level of the pairwise tree over the row-major sequence of
+// superblock sums (the flat weight order cut at 128).  Each workgroup reduces
+// one aligned chunk of 4096 values: lane l of wave w holds values
+// 16*(64w + l) .. +15 and reduces them level by level in registers, the XOR
+// butterfly over offsets 1..32 continues the same tree across lanes, and the
+// four wave sums are added as (w0 + w1) + (w2 + w3).  Values past `real` are
+// +0, which leaves every sum unchanged, so chunks of 4096 reproduce the tree
+// over the padded power-of-two width exactly.  With `denom` > 0 the single
+// chunk's sum is turned into the scale.
+constexpr int kTreeChunk = 4096;
+__global__ __launch_bounds__(256) void tree_level_kernel(const float* __restrict__ in, int64_t real,
+                                                         float* __restrict__ out, double denom) {
+  __shared__ float wsum[4];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int64_t base = (int64_t)blockIdx.x * kTreeChunk + (int64_t)(wave * 64 + lane) * 16;
+  float v[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) v[i] = (base + i < real) ? in[base + i] : 0.f;
+#pragma unroll
+  for (int w = 16; w > 1; w >>= 1)
+#pragma unroll
+    for (int i = 0; i < w / 2; ++i) v[i] = v[2 * i] + v[2 * i + 1];
+  float sum = v[0];
+  sum += __shfl_xor(sum, 1);
+  sum += __shfl_xor(sum, 2);
+  sum += __shfl_xor(sum, 4);
+  sum += __shfl_xor(sum, 8);
+  sum += __shfl_xor(sum, 16);
+  sum += __shfl_xor(sum, 32);
+  if (lane == 0) wsum[wave] = sum;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const float total = (wsum[0] + wsum[1]) + (wsum[2] + wsum[3]);
+    if (denom > 0.0) {
+      out[0] = (float)((double)total / denom);
+    } else {
+      out[blockIdx.x] = total;
+    }
+  }
 }
 
 }  // namespace
@@ -214,9 +267,8 @@ QuantizePlan plan_quantize(int64_t n, int64_t k, int gran, int group_size) {
   if (p.direct_alpha) return p;
   p.sb_sums = n * nsb;
   if (gran == SHERRY_PER_TENSOR) {
-    const int64_t width = next_pow2(p.sb_sums);
-    p.chunk = width < 256 ? width : 256;
-    p.chunks = (p.sb_sums + p.chunk - 1) / p.chunk;
+    p.chunk = kTreeChunk;
+    p.chunks = 2 * ((p.sb_sums + kTreeChunk - 1) / kTreeChunk);  // two level buffers
   }
   p.workspace_bytes = (size_t)(p.sb_sums + p.chunks) * sizeof(float);
   return p;
@@ -242,15 +294,30 @@ hipError_t launch_quantize_pack(const QuantizePlan& p, int64_t n, int64_t k, int
     hipLaunchKernelGGL(alpha_group_kernel, dim3((unsigned)((items + 255) / 256)), dim3(256), 0, s,
                        ws, n, nsb, r, alpha);
   } else if (gran == SHERRY_PER_CHANNEL) {
-    hipLaunchKernelGGL(alpha_channel_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s,
-                       ws, n, nsb, k, alpha);
+    const dim3 g4((unsigned)((n + 3) / 4)), b256(256);
+    if (nsb <= 64) hipLaunchKernelGGL(alpha_channel_wave_kernel<1>, g4, b256, 0, s, ws, n, nsb, k, alpha);
+    else if (nsb <= 128) hipLaunchKernelGGL(alpha_channel_wave_kernel<2>, g4, b256, 0, s, ws, n, nsb, k, alpha);
+    else if (nsb <= 256) hipLaunchKernelGGL(alpha_channel_wave_kernel<4>, g4, b256, 0, s, ws, n, nsb, k, alpha);
+    else if (nsb <= 512) hipLaunchKernelGGL(alpha_channel_wave_kernel<8>, g4, b256, 0, s, ws, n, nsb, k, alpha);
+    else if (nsb <= 1024) hipLaunchKernelGGL(alpha_channel_wave_kernel<16>, g4, b256, 0, s, ws, n, nsb, k, alpha);
+    else hipLaunchKernelGGL(alpha_channel_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s,
+                            ws, n, nsb, k, alpha);
   } else {
-    float* part = ws + p.sb_sums;
-    hipLaunchKernelGGL(alpha_tensor_stage1, dim3((unsigned)((p.chunks + 255) / 256)), dim3(256), 0, s,
-                       ws, p.sb_sums, p.chunk, p.chunks, part);
-    const int64_t width = next_pow2(p.sb_sums) / p.chunk;
     const double denom = (double)n * (double)k / 4.0 * 3.0;
-    hipLaunchKernelGGL(alpha_tensor_stage2, dim3(1), dim3(64), 0, s, part, p.chunks, width, denom, alpha);
+    const float* in = ws;
+    float* bufs[2] = {ws + p.sb_sums, ws + p.sb_sums + p.chunks / 2};
+    int64_t real = p.sb_sums;
+    for (int level = 0;; ++level) {
+      const int64_t chunks = (real + kTreeChunk - 1) / kTreeChunk;
+      if (chunks == 1) {
+        hipLaunchKernelGGL(tree_level_kernel, dim3(1), dim3(256), 0, s, in, real, alpha, denom);
+        break;
+      }
+      float* out = bufs[level & 1];
+      hipLaunchKernelGGL(tree_level_kernel, dim3((unsigned)chunks), dim3(256), 0, s, in, real, out, 0.0);
+      in = out;
+      real = chunks;
+    }
   }
   return hipGetLastError();
 }

@@ -59,7 +59,8 @@ def test_size_queries(lib):
     # quantize workspace: none for G=128, N*K/128 sums otherwise (+ chunk partials per tensor)
     assert lib.sherry_workspace_bytes(L.OP_QUANTIZE_PACK, 64, 512, L.PER_GROUP, 128, 1, 1) == 0
     assert lib.sherry_workspace_bytes(L.OP_QUANTIZE_PACK, 64, 512, L.PER_CHANNEL, 128, 1, 1) == 64 * 4 * 4
-    assert lib.sherry_workspace_bytes(L.OP_QUANTIZE_PACK, 64, 512, L.PER_TENSOR, 128, 1, 1) == (256 + 1) * 4
+    # per_tensor: 256 superblock sums + two level buffers of ceil(256/4096) partials
+    assert lib.sherry_workspace_bytes(L.OP_QUANTIZE_PACK, 64, 512, L.PER_TENSOR, 128, 1, 1) == (256 + 2) * 4
     assert lib.sherry_workspace_bytes(L.OP_UNPACK, 64, 512, L.PER_TENSOR, 128, 1, 1) == 0
     assert lib.sherry_workspace_bytes(L.OP_GEMV, 64, 512, L.PER_GROUP, 128, 17, 1) == (1 << 64) - 1
     assert lib.sherry_workspace_bytes(9, 64, 512, L.PER_GROUP, 128, 1, 1) == (1 << 64) - 1

@@ -332,3 +332,18 @@ def test_gemm_one_hot_exact():
     for r, c in enumerate(cols):
         expect = O.round_to_bf16_bits((t[:, c].astype(np.float32) * a[c // 128]).astype(np.float32))
         assert np.array_equal(y[r], expect)
+
+
+@pytest.mark.parametrize("n,nsb", [(5, 65), (3, 600), (2, 1030), (9, 64), (7, 1)])
+def test_quantize_per_channel_reduction_paths(n, nsb):
+    """Rows of 65, 600 and 1030 superblocks exercise the lane-blocked wave
+    reductions and the sequential fallback."""
+    w = WL.latent_weight(n, 128 * nsb, 70 + nsb)
+    check_quantize(dev_f32(w), w, "per_channel")
+
+
+@pytest.mark.parametrize("n,k", [(1000, 128 * 9), (4096, 128), (33, 128 * 131)])
+def test_quantize_per_tensor_multi_level(n, k):
+    """More than 4096 superblock sums: the tree runs over two or three levels."""
+    w = WL.latent_weight(n, k, 90 + n)
+    check_quantize(dev_f32(w), w, "per_tensor")

@@ -62,7 +62,8 @@ typedef enum {
   SHERRY_ERR_GRANULARITY = 4, /* granularity is not one of sherry_granularity */
   SHERRY_ERR_DTYPE = 5,       /* a dtype argument not allowed for that operand */
   SHERRY_ERR_UNSUPPORTED = 6, /* legal for the method but not built here:
-                                 K % 128 != 0, or per_group with G % 128 != 0 */
+                                 K % 128 != 0, per_group with G % 128 != 0,
+                                 or a GEMM with K > 2^21 */
   SHERRY_ERR_ALIGN = 7,       /* a device pointer or stride is not 16-byte aligned */
   SHERRY_ERR_WORKSPACE = 8,   /* workspace NULL or smaller than sherry_workspace_bytes */
   SHERRY_ERR_BATCH = 9,       /* batch outside 1..16, m < 1, count < 1, or a
@@ -185,6 +186,7 @@ int32_t sherry_gemv(int64_t n, int64_t k, int32_t granularity, int32_t group_siz
  *
  *   x   [M, K] bf16 row-major;  y [M, N] bf16 row-major (round to nearest even).
  *   m   >= 1.
+ *   K   at most 2^21 (SHERRY_ERR_UNSUPPORTED above).
  *   workspace: sherry_workspace_bytes(SHERRY_OP_GEMM, ...) bytes (may be 0).
  * Result within 1e-3 * sum_k |X[m,k] * alpha(n,k)| of the exact product.
  */

@@ -40,6 +40,9 @@ constexpr int kStageK = 64;                 // k per LDS stage
 constexpr int kRowBytes = kStageK * 2;      // one LDS row: 64 bf16
 constexpr int kChunks = kRowBytes / 16;     // 8 chunks of 8 k per row
 
+#ifndef SHERRY_GEMM_WAVES
+#define SHERRY_GEMM_WAVES 8  // waves per workgroup for 256-row tiles (8: 2 per SIMD, 64 x 64 each)
+#endif
 #ifndef SHERRY_GEMM_SWZ
 #define SHERRY_GEMM_SWZ 1  // 0: chunk ^ (row & 7); 1: chunk ^ ((row >> 1) & 7)
 #endif
@@ -63,13 +66,20 @@ __device__ inline uint2 decode_bf16(uint32_t code) {
   return make_uint2(h[0] | (h[1] << 16), h[2] | (h[3] << 16));
 }
 
-template <int GRAN, int BM, int BN>
+template <int GRAN, int BM, int BN, int WAVES>
 struct GemmCfg {
-  static constexpr int WM = BM / 2, WN = BN / 2;   // wave tile (m, n)
-  static constexpr int TM = WM / 16, TN = WN / 16; // MFMA tiles per wave
-  static constexpr int XLOADS = BM / 32;           // 1 KB X copies per wave per stage (8 rows each)
-  static constexpr int VM_PER_STAGE = XLOADS + 2;  // + nibble and sign record copies
+  static constexpr int THREADS = 64 * WAVES;
+  static constexpr int WAVES_N = 2, WAVES_M = WAVES / 2;  // wave grid (m x n)
+  static constexpr int WM = BM / WAVES_M, WN = BN / WAVES_N;  // wave tile (m, n)
+  static constexpr int TM = WM / 16, TN = WN / 16;  // MFMA tiles per wave
+  static constexpr int XLOADS = BM / 8 / WAVES;     // 1 KB X copies per wave per stage (8 rows each)
+  static constexpr int ROWS_PER_WAVE = BN / WAVES;  // weight rows each wave copies and decodes
+  static constexpr int THREADS_PER_ROW = THREADS / BN;
+  static constexpr int CHUNKS_PER_THREAD = 8 / THREADS_PER_ROW;  // of the stage's 8 chunks per row
   static constexpr bool kGroup = GRAN == SHERRY_PER_GROUP;
+  // copies per wave per stage: X pieces, nibble and sign records, and for
+  // per_group the scales of the stage's group
+  static constexpr int VM_PER_STAGE = XLOADS + 2 + (kGroup ? 1 : 0);
 };
 
 // s_waitcnt with only a vmcnt limit (expcnt / lgkmcnt left at their maxima).
@@ -82,6 +92,9 @@ __device__ inline void wait_vmcnt() {
 // Direct global -> LDS copy: lane l of the wave writes lds_wave_base + size*l
 // (the LDS base is wave-uniform; inactive lanes write nothing).
 typedef __attribute__((address_space(3))) void lds_void;
+// Word 3 of a raw buffer resource on gfx9-class parts: 32-bit data format
+// (a zero format would make every access read zero), no swizzle, no stride.
+constexpr int kBufferWord3 = 0x00020000;
 __device__ inline void g2l_16(const void* g, void* lds_wave_base) {
   __builtin_amdgcn_global_load_lds(const_cast<void*>(g), (lds_void*)lds_wave_base, 16, 0, 0);
 }
@@ -103,15 +116,18 @@ __device__ inline void lds_barrier() {
 template <int J>
 using Slot = std::integral_constant<int, J>;
 
-template <int GRAN, int BM, int BN>
-__global__ __launch_bounds__(256, 1) void gemm_kernel(const uint8_t* __restrict__ packed,
+template <int GRAN, int BM, int BN, int WAVES>
+__global__ __launch_bounds__(64 * WAVES, 1) void gemm_kernel(const uint8_t* __restrict__ packed,
                                                       const float* __restrict__ alpha,
                                                       const uint16_t* __restrict__ x,
                                                       uint16_t* __restrict__ y, int64_t n, int64_t k,
                                                       int64_t m, int group_sbs, int tiles_m, int tiles_n) {
-  using C = GemmCfg<GRAN, BM, BN>;
+  using C = GemmCfg<GRAN, BM, BN, WAVES>;
   static_assert(BN == 128, "the record copies and the decode assume 128 weight rows");
-  constexpr int kRecBytes = BN * 16 + BN * 4;  // nibble records + sign dwords of one superblock
+  // record slot: nibble records + sign dwords of one superblock (+ per_group:
+  // the scales of its group)
+  constexpr int kAlphaOff = BN * 16 + BN * 4;
+  constexpr int kRecBytes = kAlphaOff + (C::kGroup ? BN * 4 : 0);
   // Three-deep rings, one __shared__ object per slot: the compiler's wait
   // insertion then knows an LDS read of one slot never aliases the direct
   // copies in flight into another.
@@ -133,7 +149,7 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(const uint8_t* __restrict_
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  const int wm = wave & 1, wn = wave >> 1;
+  const int wm = wave % C::WAVES_M, wn = wave / C::WAVES_M;
   const int r = lane & 15, q = lane >> 4;
 
   // XCD-aware tile order: consecutive workgroup ids land on different XCDs;
@@ -152,51 +168,72 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(const uint8_t* __restrict_
   const uint8_t* __restrict__ nib_plane = packed;
   const uint8_t* __restrict__ sgn_plane = packed + nibble_plane_bytes(n, k);
 
-  // this thread decodes weight row tid/2 (wave w owns rows 32w .. 32w+31)
-  const int wrow = tid >> 1;
+  // this thread decodes weight row tid / THREADS_PER_ROW; wave w owns rows
+  // ROWS_PER_WAVE*w .. +ROWS_PER_WAVE-1, which it also copies
+  const int wrow = tid / C::THREADS_PER_ROW;
+  const int wsub = tid % C::THREADS_PER_ROW;
 
   // Direct copies of stage st into ring slot J.  X: wave w copies rows
-  // [w*BM/4, (w+1)*BM/4) in pieces of 8 rows; lane l -> physical chunk l%8 of
-  // row l/8, which holds logical chunk (l%8) ^ swz_key(row).  Records: each
-  // wave copies the 32 rows it decodes (lanes 32..63 idle).
+  // [w*BM/WAVES, (w+1)*BM/WAVES) in pieces of 8 rows; lane l -> physical chunk
+  // l%8 of row l/8, which holds logical chunk (l%8) ^ swz_key(row).  Records:
+  // each wave copies the rows it decodes (the other lanes idle).
+  // X copies are buffer loads: the per-stage base is wave-uniform (a buffer
+  // resource in SGPRs), the lane offset a 32-bit VGPR, and rows past m fall
+  // outside the resource's range, so they read zeros (the host keeps
+  // (m + BM) * k * 2 below 2^31).  The lane part of the offset only depends
+  // on the parity of the 8-row piece (the swizzle key has period 16 rows).
+  static_assert(C::XLOADS % 2 == 0, "pieces of one wave alternate parity");
+  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+  uint32_t xlane[2];
+#pragma unroll
+  for (int p = 0; p < 2; ++p) {
+    const int prow = p * 8 + (lane >> 3);
+    xlane[p] = (uint32_t)((lane >> 3) * k * 2) + (uint32_t)((((lane & 7) ^ swz_key(prow))) * 16);
+  }
+  const uint32_t xbytes = (uint32_t)(m * k * 2);
+  int64_t rrow = n0 + wave * C::ROWS_PER_WAVE + (lane % C::ROWS_PER_WAVE);
+  rrow = rrow < n ? rrow : n - 1;
+  const uint32_t nrow_off = (uint32_t)(rrow * 16), srow_off = (uint32_t)(rrow * 4);
   auto issue = [&](auto J, int st) {
-    const int64_t kbase = (int64_t)st * kStageK;
+    const uint32_t sbyte = (uint32_t)st * (kStageK * 2);
+    const __amdgpu_buffer_rsrc_t xr = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<char*>(reinterpret_cast<const char*>(x)) + sbyte, (short)0, (int)(xbytes - sbyte), kBufferWord3);
     char* xb = XS(J);
 #pragma unroll
     for (int i = 0; i < C::XLOADS; ++i) {
-      const int row = (wave * C::XLOADS + i) * 8 + (lane >> 3);
-      const int ch = (lane & 7) ^ swz_key(row);
-      int64_t gm = m0 + row;
-      gm = gm < m ? gm : m - 1;  // clamped rows feed only outputs that are not stored
-      g2l_16(x + gm * k + kbase + ch * 8, xb + (wave * C::XLOADS + i) * 1024);
+      const int piece = wave_u * C::XLOADS + i;
+      const uint32_t voff = xlane[i & 1] + (uint32_t)((m0 + piece * 8) * k * 2);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(xr, (lds_void*)(xb + piece * 1024), 16, voff, 0, 0, 0);
     }
     char* rb = RC(J);
     const int64_t g = st >> 1;
-    int64_t gn = n0 + wave * 32 + (lane & 31);
-    gn = gn < n ? gn : n - 1;
-    if (lane < 32) {
-      g2l_16(nib_plane + (g * n + gn) * 16, rb + wave * 512);
-      g2l_4(sgn_plane + (g * n + gn) * 4, rb + BN * 16 + wave * 128);
+    if (lane < C::ROWS_PER_WAVE) {
+      g2l_16(nib_plane + g * n * 16 + nrow_off, rb + wave * C::ROWS_PER_WAVE * 16);
+      g2l_4(sgn_plane + g * n * 4 + srow_off, rb + BN * 16 + wave * C::ROWS_PER_WAVE * 4);
+      if constexpr (C::kGroup)
+        g2l_4(alpha + (g / group_sbs) * n + (srow_off >> 2), rb + kAlphaOff + wave * C::ROWS_PER_WAVE * 4);
     }
   };
-  // Decode stage st from record slot J into the bf16 tile slot J: byte
-  // cb = 2*(st&1) + (tid&1) of nibble dword d holds blocks 8cb + 2d and
-  // 8cb + 2d + 1 = the 8 weights of chunk d + 4cb.
+  // Decode stage st from record slot J into the bf16 tile slot J.  Byte cb
+  // of nibble dword d holds blocks 8cb + 2d and 8cb + 2d + 1 = the 8 weights
+  // of chunk d + 4cb; stage st covers cb = 2*(st&1) + {0, 1}, i.e. 8 chunks
+  // per row, CHUNKS_PER_THREAD of them per thread.
   auto decode = [&](auto J, int st) {
     const char* rb = RC(J);
     char* wb = WS(J);
-    const int cb = 2 * (st & 1) + (tid & 1);
     const uint4 nr = *reinterpret_cast<const uint4*>(rb + wrow * 16);
     const uint32_t sg = *reinterpret_cast<const uint32_t*>(rb + BN * 16 + wrow * 4);
     const uint32_t nd[4] = {nr.x, nr.y, nr.z, nr.w};
 #pragma unroll
-    for (int d = 0; d < 4; ++d) {
+    for (int cc = 0; cc < C::CHUNKS_PER_THREAD; ++cc) {
+      const int lc = wsub * C::CHUNKS_PER_THREAD + cc;  // 0..7: (cb & 1, d)
+      const int d = lc & 3;
+      const int cb = 2 * (st & 1) + (lc >> 2);
       const uint32_t byte = __builtin_amdgcn_ubfe(nd[d], 8 * cb, 8);
       const uint32_t s2 = __builtin_amdgcn_ubfe(sg, 2 * d + 8 * cb, 2);
       const uint2 lo = dtab[(byte & 15u) | ((s2 & 1u) << 4)];
       const uint2 hi = dtab[(byte >> 4) | ((s2 >> 1) << 4)];
-      const int ch = d + 4 * (cb & 1);  // chunk inside this stage's 8
-      *reinterpret_cast<u32x4*>(wb + swz(wrow, ch)) = u32x4{lo.x, lo.y, hi.x, hi.y};
+      *reinterpret_cast<u32x4*>(wb + swz(wrow, lc)) = u32x4{lo.x, lo.y, hi.x, hi.y};
     }
   };
 
@@ -206,74 +243,64 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(const uint8_t* __restrict_
   for (int i = 0; i < C::TN; ++i)
 #pragma unroll
     for (int j = 0; j < C::TM; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-  if constexpr (C::kGroup) {
-#pragma unroll
-    for (int i = 0; i < C::TN; ++i)
-#pragma unroll
-      for (int j = 0; j < C::TM; ++j) accg[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-  }
-  int gpos = 0;
+  int gpos = 0;  // superblocks done in the current group (its first stage zeroes accg)
 
   // One stage: stage st sits in slot J = st % 3.
   auto stage = [&](auto J, int st) {
     constexpr int j = decltype(J)::value;
     constexpr int j1 = (j + 1) % 3, j2 = (j + 2) % 3;
-    // per_group: this stage ends a group -> load the group's scales first, so
-    // the wait for them does not include the copies issued below
     const bool group_end = C::kGroup && (st & 1) == 1 && gpos + 1 == group_sbs;
-    float av[C::kGroup ? C::TN : 1][4];
-    if constexpr (C::kGroup) {
-      if (group_end) {
-        const int64_t gg = (st >> 1) / group_sbs;
-#pragma unroll
-        for (int i = 0; i < C::TN; ++i)
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            int64_t gn = n0 + wn * C::WN + i * 16 + 4 * q + e;
-            gn = gn < n ? gn : n - 1;  // clamped rows are not stored
-            av[i][e] = alpha[gg * n + gn];
-          }
-      }
-    }
     // copies two stages ahead (slot j2 was consumed in the previous stage)
     const bool ahead = st + 2 < stages;
     if (ahead) issue(Slot<j2>{}, st + 2);
 
     const char* xb = XS(J);
     const char* wb = WS(J);
+    // per_group: the first k-step of a group starts its accumulators from 0
+    auto mma = [&](auto zero_c) {
 #pragma unroll
-    for (int kk = 0; kk < kStageK / 32; ++kk) {
-      const int ch = kk * 4 + q;
-      bf16x8 a[C::TN], b[C::TM];
+      for (int kk = 0; kk < kStageK / 32; ++kk) {
+        const int ch = kk * 4 + q;
+        bf16x8 a[C::TN], b[C::TM];
 #pragma unroll
-      for (int i = 0; i < C::TN; ++i)
-        a[i] = *reinterpret_cast<const bf16x8*>(wb + swz(wn * C::WN + i * 16 + r, ch));
+        for (int i = 0; i < C::TN; ++i)
+          a[i] = *reinterpret_cast<const bf16x8*>(wb + swz(wn * C::WN + i * 16 + r, ch));
 #pragma unroll
-      for (int jj = 0; jj < C::TM; ++jj)
-        b[jj] = *reinterpret_cast<const bf16x8*>(xb + swz(wm * C::WM + jj * 16 + r, ch));
+        for (int jj = 0; jj < C::TM; ++jj)
+          b[jj] = *reinterpret_cast<const bf16x8*>(xb + swz(wm * C::WM + jj * 16 + r, ch));
 #pragma unroll
-      for (int i = 0; i < C::TN; ++i)
+        for (int i = 0; i < C::TN; ++i)
 #pragma unroll
-        for (int jj = 0; jj < C::TM; ++jj) {
-          if constexpr (C::kGroup) {
-            accg[i][jj] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i], b[jj], accg[i][jj], 0, 0, 0);
-          } else {
-            acc[i][jj] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i], b[jj], acc[i][jj], 0, 0, 0);
+          for (int jj = 0; jj < C::TM; ++jj) {
+            if constexpr (C::kGroup) {
+              const f32x4 c_in = (decltype(zero_c)::value && kk == 0) ? f32x4{0.f, 0.f, 0.f, 0.f} : accg[i][jj];
+              accg[i][jj] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i], b[jj], c_in, 0, 0, 0);
+            } else {
+              acc[i][jj] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i], b[jj], acc[i][jj], 0, 0, 0);
+            }
           }
-        }
+      }
+    };
+    if (C::kGroup && (st & 1) == 0 && gpos == 0) {
+      mma(std::true_type{});
+    } else {
+      mma(std::false_type{});
     }
 
     if constexpr (C::kGroup) {
       if ((st & 1) == 1) {
         if (group_end) {
+          // the group's scales came with this stage's record copy
+          const char* rb = RC(J);
 #pragma unroll
-          for (int i = 0; i < C::TN; ++i)
+          for (int i = 0; i < C::TN; ++i) {
+            const f32x4 av = *reinterpret_cast<const f32x4*>(rb + kAlphaOff + (wn * C::WN + i * 16 + 4 * q) * 4);
 #pragma unroll
             for (int jj = 0; jj < C::TM; ++jj) {
 #pragma unroll
-              for (int e = 0; e < 4; ++e) acc[i][jj][e] += av[i][e] * accg[i][jj][e];
-              accg[i][jj] = f32x4{0.f, 0.f, 0.f, 0.f};
+              for (int e = 0; e < 4; ++e) acc[i][jj][e] += av[e] * accg[i][jj][e];
             }
+          }
           gpos = 0;
         } else {
           ++gpos;
@@ -332,23 +359,31 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(const uint8_t* __restrict_
   }
 }
 
-template <int GRAN, int BM>
+template <int GRAN, int BM, int WAVES>
 hipError_t launch_t(int64_t n, int64_t k, int group_sbs, const uint8_t* packed, const float* alpha,
                     const uint16_t* x, int64_t m, uint16_t* y, hipStream_t s) {
   constexpr int BN = 128;
-  const int tiles_m = (int)((m + BM - 1) / BM), tiles_n = (int)((n + BN - 1) / BN);
-  hipLaunchKernelGGL((gemm_kernel<GRAN, BM, BN>), dim3((unsigned)(tiles_m * tiles_n)), dim3(256), 0, s, packed,
-                     alpha, x, y, n, k, m, group_sbs, tiles_m, tiles_n);
-  return hipGetLastError();
+  // one launch covers at most `chunk` rows of X so that its buffer offsets,
+  // including the tail tile's rows past the end, stay below 2^31 bytes
+  const int64_t chunk = ((((int64_t)1 << 31) / (2 * k) - BM) / BM) * BM;
+  if (chunk < BM) return hipErrorInvalidValue;
+  const int tiles_n = (int)((n + BN - 1) / BN);
+  for (int64_t r0 = 0; r0 < m; r0 += chunk) {
+    const int64_t mc = m - r0 < chunk ? m - r0 : chunk;
+    const int tiles_m = (int)((mc + BM - 1) / BM);
+    hipLaunchKernelGGL((gemm_kernel<GRAN, BM, BN, WAVES>), dim3((unsigned)(tiles_m * tiles_n)), dim3(64 * WAVES), 0,
+                       s, packed, alpha, x + r0 * k, y + r0 * n, n, k, mc, group_sbs, tiles_m, tiles_n);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
 }
 
 template <int GRAN>
-hipError_t launch_g(int tile_m, int64_t n, int64_t k, int group_sbs, const uint8_t* packed, const float* alpha,
-                    const uint16_t* x, int64_t m, uint16_t* y, hipStream_t s) {
-  if constexpr (GRAN != SHERRY_PER_GROUP) {
-    if (tile_m == 256) return launch_t<GRAN, 256>(n, k, group_sbs, packed, alpha, x, m, y, s);
-  }
-  return launch_t<GRAN, 128>(n, k, group_sbs, packed, alpha, x, m, y, s);
+hipError_t launch_g(const GemmPlan& p, int64_t n, int64_t k, int group_sbs, const uint8_t* packed,
+                    const float* alpha, const uint16_t* x, int64_t m, uint16_t* y, hipStream_t s) {
+  if (p.tile_m == 256) return launch_t<GRAN, 256, SHERRY_GEMM_WAVES>(n, k, group_sbs, packed, alpha, x, m, y, s);
+  return launch_t<GRAN, 128, 4>(n, k, group_sbs, packed, alpha, x, m, y, s);
 }
 
 }  // namespace
@@ -357,10 +392,9 @@ GemmPlan plan_gemm(int64_t n, int64_t k, int gran, int group_size, int64_t m) {
   (void)k; (void)group_size;
   GemmPlan p{};
   p.tile_n = 128;
-  // 256-row tiles once they still give >= 2 tiles per CU; per_group keeps a
-  // second accumulator set per wave, which only fits at 128 rows
+  // 256-row tiles (8 waves of 64 x 64) once they still give >= 2 tiles per CU
   const int64_t big = ((m + 255) / 256) * ((n + 127) / 128);
-  p.tile_m = (big >= 512 && gran != SHERRY_PER_GROUP) ? 256 : 128;
+  p.tile_m = (big >= 512 && (gran != SHERRY_PER_GROUP || SHERRY_GEMM_WAVES == 8)) ? 256 : 128;
   p.workspace_bytes = 0;
   return p;
 }
@@ -369,9 +403,9 @@ hipError_t launch_gemm(const GemmPlan& p, int64_t n, int64_t k, int gran, int gr
                        const uint8_t* packed, const float* alpha, const uint16_t* x, int64_t m,
                        uint16_t* y, hipStream_t s) {
   const int group_sbs = gran == SHERRY_PER_GROUP ? group_size / kSuperblock : 1;
-  if (gran == SHERRY_PER_GROUP) return launch_g<SHERRY_PER_GROUP>(p.tile_m, n, k, group_sbs, packed, alpha, x, m, y, s);
-  if (gran == SHERRY_PER_CHANNEL) return launch_g<SHERRY_PER_CHANNEL>(p.tile_m, n, k, group_sbs, packed, alpha, x, m, y, s);
-  return launch_g<SHERRY_PER_TENSOR>(p.tile_m, n, k, group_sbs, packed, alpha, x, m, y, s);
+  if (gran == SHERRY_PER_GROUP) return launch_g<SHERRY_PER_GROUP>(p, n, k, group_sbs, packed, alpha, x, m, y, s);
+  if (gran == SHERRY_PER_CHANNEL) return launch_g<SHERRY_PER_CHANNEL>(p, n, k, group_sbs, packed, alpha, x, m, y, s);
+  return launch_g<SHERRY_PER_TENSOR>(p, n, k, group_sbs, packed, alpha, x, m, y, s);
 }
 
 }  // namespace sherry

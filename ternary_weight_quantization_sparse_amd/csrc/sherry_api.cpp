@@ -17,6 +17,8 @@ using namespace sherry;
 namespace {
 
 constexpr int64_t kMaxElems = (int64_t)1 << 46;
+// GEMM: 32-bit buffer offsets into X need 512 rows of K bf16 below 2^31 bytes
+constexpr int64_t kGemmMaxK = (int64_t)1 << 21;
 
 int check_shape(int64_t n, int64_t k, int32_t gran, int32_t group_size) {
   if (n <= 0 || k <= 0 || k % kBlock != 0) return SHERRY_ERR_SHAPE;
@@ -159,6 +161,7 @@ int32_t sherry_gemm(int64_t n, int64_t k, int32_t granularity, int32_t group_siz
                     void* y, void* workspace, size_t workspace_bytes, void* stream) {
   int st = check_shape(n, k, granularity, group_size);
   if (st != SHERRY_OK) return st;
+  if (k > kGemmMaxK) return SHERRY_ERR_UNSUPPORTED;
   if (!packed || !alpha || !x || !y) return SHERRY_ERR_NULL;
   if (!aligned16(packed) || !aligned16(alpha) || !aligned16(x) || !aligned16(y)) return SHERRY_ERR_ALIGN;
   if (m < 1 || m > kMaxElems / k || (m + 127) / 128 > 65535) return SHERRY_ERR_BATCH;

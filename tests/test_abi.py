@@ -137,6 +137,7 @@ def gm(lib, n=64, k=512, gran=L.PER_GROUP, g=128, packed=FAKE, alpha=FAKE2, x=FA
     (dict(k=2), L.ERR_SHAPE), (dict(gran=9), L.ERR_GRANULARITY), (dict(g=1000), L.ERR_GROUP),
     (dict(x=None), L.ERR_NULL), (dict(y=None), L.ERR_NULL), (dict(y=MIS), L.ERR_ALIGN),
     (dict(m=0), L.ERR_BATCH), (dict(m=-5), L.ERR_BATCH), (dict(k=516, gran=L.PER_TENSOR), L.ERR_UNSUPPORTED),
+    (dict(n=8, k=(1 << 21) + 128, gran=L.PER_TENSOR, m=1), L.ERR_UNSUPPORTED),
 ])
 def test_gemm_rejects(lib, kw, code):
     assert gm(lib, **kw) == code

@@ -134,30 +134,34 @@ def within_tol(y, y_ref, bound):
     return bool(np.all(err <= bound)), float(np.max(err / bound))
 
 
-def timed_launches(launches, steps, warmup):
+def timed_launches(launches, steps, warmup, per_launch=True):
     """Run ``steps`` passes over ``launches`` (callables) after ``warmup``
     passes.  Returns (total ms from events around the whole region, per-launch
-    ms list of lists [launch][step])."""
+    ms list of lists [launch][step] or None when ``per_launch`` is False, host
+    wall ms).  The per-launch events sit between the launches, so the total of
+    a region without them is the clean whole-job time."""
     torch = _torch()
     for _ in range(warmup):
         for fn in launches:
             fn()
     torch.cuda.synchronize()
     ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(steps)] for _ in launches]
+           for _ in range(steps)] for _ in launches] if per_launch else None
     t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     wall0 = time.perf_counter()
     t0.record()
     for s in range(steps):
         for i, fn in enumerate(launches):
-            ev[i][s][0].record()
+            if per_launch:
+                ev[i][s][0].record()
             fn()
-            ev[i][s][1].record()
+            if per_launch:
+                ev[i][s][1].record()
     t1.record()
     torch.cuda.synchronize()
     wall = (time.perf_counter() - wall0) * 1e3
-    per = [[a.elapsed_time(b) for (a, b) in row] for row in ev]
+    per = [[a.elapsed_time(b) for (a, b) in row] for row in ev] if per_launch else None
     return t0.elapsed_time(t1), per, wall
 
 
@@ -206,7 +210,12 @@ def bench_gemv_1b(args, dev):
         pws.append((name, n, k, pw, w))
 
     launches = [(lambda r=rep, xx=x: r.gemv(xx)) for (_, rep, x) in reps]
-    total_ms, per, wall = timed_launches(launches, args.steps, args.warmup)
+    # the timed region: W warm-up steps, then exactly K steps with nothing
+    # but the launches between the bracketing events
+    total_ms, _, wall = timed_launches(launches, args.steps, args.warmup, per_launch=False)
+    # then the same K steps again with an event pair around every launch, for
+    # the per-kernel durations the roofline uses
+    _, per, _ = timed_launches(launches, args.steps, 0)
     bytes_step = sum(rep.algo_bytes() for (_, rep, _) in reps)
     ms_step = total_ms / args.steps
     gbs = bytes_step / (ms_step * 1e-3) / 1e9
@@ -421,8 +430,8 @@ def cpu_baseline(pws, min_seconds=10.0):
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--sections", default="gemv,single,gemm,quantize,gemv3b,cpu",
                     help="comma list of: gemv (always), single, gemm, quantize, gemv3b, cpu, "
                          "copycal (a 1 GiB device copy for scaling HBM counters)")

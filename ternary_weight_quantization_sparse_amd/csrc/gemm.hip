@@ -4,27 +4,35 @@
 // F.linear with the dequantized ternary weight); activations stay bf16 (same
 // section, and the agihunt digest's limits paragraph).
 //
-// Tiling: one workgroup of 4 waves (2 x 2) per BM (m) x BN (n) output tile;
-// a wave owns (BM/2) x (BN/2) as 16 x 16 tiles of v_mfma_f32_16x16x32_bf16
-// with the weight tile as the A operand (MFMA row = n) and the activations as
-// B (MFMA column = m), so each lane's four accumulators are four consecutive n
-// of one output row: one 8-byte bf16 store per tile.
+// Tiling: a workgroup of 4 waves owns a 128 (m) x 128 (n) output tile; wave w
+// owns all 128 m and the 32 n starting at 32w, as 8 x 2 tiles of
+// v_mfma_f32_16x16x32_bf16 with the weights as the A operand (MFMA row = n)
+// and the activations as B (MFMA column = m), so each lane's four
+// accumulators are four consecutive n of one output row.  Two workgroups
+// share a CU and run out of step, so one's copies and barrier waits overlap
+// the other's MFMAs.
 //
-// K loop: stages of 64 (half a 128-weight superblock), double-buffered in
-// LDS.  While the MFMAs of stage s run, the threads fetch stage s+1 into
-// registers: X with dwordx4 loads, and the packed weight record of their row.
-// After the MFMAs they store X to LDS and decode the weights: a byte of a
-// nibble dword holds two consecutive blocks (8 consecutive k), and with their
-// two adjacent sign bits it forms a 10-bit index into a 16 KB LDS table of
-// ready-made 16-byte bf16 chunks {-1, 0, +1}; one ds_read_b128 + one
-// ds_write_b128 decode 8 weights.  LDS rows are 128 bytes (64 bf16); 16-byte
-// chunks are XOR-swizzled by (row & 7) so MFMA operand loads are
-// conflict-free.
+// K loop: stages of 64 k (half a 128-weight superblock) in a three-deep ring.
+// The activation tile of a stage (128 rows x 128 bytes) is copied straight
+// from global memory into LDS by buffer loads (no registers), two stages
+// ahead; 16-byte chunks are XOR-swizzled so MFMA operand reads are
+// conflict-free.  The weights never sit in LDS as bf16: each lane loads the
+// nibble dword and sign dword of its two weight rows into registers (also two
+// stages ahead) and decodes its own A operands right before the MFMAs: byte
+// cb of nibble dword q holds the lookup nibbles of two consecutive blocks (8
+// consecutive k), and each nibble with its block's sign bit indexes a
+// 32-entry LDS table of the block's 4 bf16 weights {-1, 0, +1}.  One barrier
+// per stage publishes the copied activation tile.
 //
-// Scales: per_group keeps an fp32 accumulator per group (over its 2 or more
-// stages) and adds alpha(n, group) * acc_g to the output accumulator in fp32
-// when the group ends; per_channel / per_tensor accumulate directly and scale
-// once in the epilogue.
+// Scales: per_group keeps an fp32 accumulator set per group (the group's first
+// MFMA starts from zero) and adds alpha(n, group) * acc_g to the output
+// accumulators when the group ends; the group's scales ride along with the
+// activation copies into a small LDS ring.  per_channel / per_tensor
+// accumulate directly and scale once at the end.
+//
+// Split K: launches with few tiles split K into `splits` ranges of whole
+// groups; each writes fp32 partial tiles to the workspace, and a second
+// kernel sums them in split order (deterministic), scales and rounds to bf16.
 #include <type_traits>
 
 #include "sherry_internal.h"
@@ -38,18 +46,28 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kStageK = 64;                 // k per LDS stage
 constexpr int kRowBytes = kStageK * 2;      // one LDS row: 64 bf16
-constexpr int kChunks = kRowBytes / 16;     // 8 chunks of 8 k per row
+constexpr int kWaves = 4;
+constexpr int kThreads = 64 * kWaves;
+constexpr int kTN = 2;                      // MFMA tiles per wave along n
+constexpr int kWN = 16 * kTN;               // 32 weight rows per wave
+constexpr int kBN = kWN * kWaves;           // 128 weight rows per tile
+constexpr int kMaxBM = 128;                 // largest activation tile (rows)
+// Per-wave record area of a ring slot: lane l copies the records of weight
+// row 32 wave + l % 32 (lanes >= 32 duplicate, so the copies need no branch):
+// 64 nibble records (16 B), 64 sign dwords, and for per_group 64 scales.
+constexpr int kRecNib = 0, kRecSgn = 64 * 16, kRecAlpha = kRecSgn + 64 * 4;
+constexpr int kRecWave = kRecAlpha + 64 * 4;
+constexpr int kMaxSplits = 16;
 
-#ifndef SHERRY_GEMM_WAVES
-#define SHERRY_GEMM_WAVES 8  // waves per workgroup for 256-row tiles (8: 2 per SIMD, 64 x 64 each)
-#endif
-#ifndef SHERRY_GEMM_SWZ
-#define SHERRY_GEMM_SWZ 1  // 0: chunk ^ (row & 7); 1: chunk ^ ((row >> 1) & 7)
-#endif
-__device__ inline int swz_key(int row) { return SHERRY_GEMM_SWZ ? ((row >> 1) & 7) : (row & 7); }
+// Activation LDS rows are 128 bytes = 8 chunks of 16 bytes; chunk c of row r
+// sits at physical chunk c ^ ((r >> 1) & 7).  An MFMA operand read (16 rows x
+// 4 chunks per quarter wave) then touches every bank once.
+__device__ inline int swz_key(int row) { return (row >> 1) & 7; }
 __device__ inline int swz(int row, int ch) { return row * kRowBytes + ((ch ^ swz_key(row)) << 4); }
 
-// bf16 patterns of one block (4 weights) from its 5-bit code.
+// bf16 patterns of one block (4 weights) from its 5-bit code: code =
+// s<<4 | z<<2 | p1<<1 | p0; the kept positions in order carry the signs
+// s, s^p0, s^p1; position z is 0.
 __device__ inline uint2 decode_bf16(uint32_t code) {
   const uint32_t z = (code >> 2) & 3;
   const uint32_t neg0 = (code >> 4) & 1;
@@ -66,20 +84,17 @@ __device__ inline uint2 decode_bf16(uint32_t code) {
   return make_uint2(h[0] | (h[1] << 16), h[2] | (h[3] << 16));
 }
 
-template <int GRAN, int BM, int BN, int WAVES>
+// TM = MFMA tiles per wave along m: 8 (128-row tiles), or 4 (64-row tiles)
+// for per_group, whose second accumulator set would not fit otherwise.
+template <int GRAN, int TM>
 struct GemmCfg {
-  static constexpr int THREADS = 64 * WAVES;
-  static constexpr int WAVES_N = 2, WAVES_M = WAVES / 2;  // wave grid (m x n)
-  static constexpr int WM = BM / WAVES_M, WN = BN / WAVES_N;  // wave tile (m, n)
-  static constexpr int TM = WM / 16, TN = WN / 16;  // MFMA tiles per wave
-  static constexpr int XLOADS = BM / 8 / WAVES;     // 1 KB X copies per wave per stage (8 rows each)
-  static constexpr int ROWS_PER_WAVE = BN / WAVES;  // weight rows each wave copies and decodes
-  static constexpr int THREADS_PER_ROW = THREADS / BN;
-  static constexpr int CHUNKS_PER_THREAD = 8 / THREADS_PER_ROW;  // of the stage's 8 chunks per row
   static constexpr bool kGroup = GRAN == SHERRY_PER_GROUP;
-  // copies per wave per stage: X pieces, nibble and sign records, and for
-  // per_group the scales of the stage's group
-  static constexpr int VM_PER_STAGE = XLOADS + 2 + (kGroup ? 1 : 0);
+  static constexpr int kTM = TM;
+  static constexpr int kBM = 16 * TM;              // rows of X per tile
+  static constexpr int kXLoads = kBM / 8 / kWaves;  // 1 KB activation copies per wave per stage
+  // vector-memory operations per wave per stage: activation pieces, nibble
+  // and sign records, and for per_group the scales
+  static constexpr int VM_PER_STAGE = kXLoads + 2 + (kGroup ? 1 : 0);
 };
 
 // s_waitcnt with only a vmcnt limit (expcnt / lgkmcnt left at their maxima).
@@ -89,25 +104,17 @@ __device__ inline void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((VM & 15) | (7 << 4) | (15 << 8) | ((VM >> 4) << 14));
 }
 
-// Direct global -> LDS copy: lane l of the wave writes lds_wave_base + size*l
-// (the LDS base is wave-uniform; inactive lanes write nothing).
 typedef __attribute__((address_space(3))) void lds_void;
 // Word 3 of a raw buffer resource on gfx9-class parts: 32-bit data format
 // (a zero format would make every access read zero), no swizzle, no stride.
 constexpr int kBufferWord3 = 0x00020000;
-__device__ inline void g2l_16(const void* g, void* lds_wave_base) {
-  __builtin_amdgcn_global_load_lds(const_cast<void*>(g), (lds_void*)lds_wave_base, 16, 0, 0);
-}
-__device__ inline void g2l_4(const void* g, void* lds_wave_base) {
-  __builtin_amdgcn_global_load_lds(const_cast<void*>(g), (lds_void*)lds_wave_base, 4, 0, 0);
-}
 
 // Workgroup barrier that orders LDS only: this wave's LDS reads and writes
 // are complete (lgkmcnt 0) before it arrives.  Unlike __syncthreads it does
-// not wait for vector-memory operations, so direct copies for later stages
-// stay in flight; their completion is waited for explicitly (vmcnt) before
-// the barrier that publishes them.  The memory clobber keeps the compiler
-// from moving LDS accesses across it.
+// not wait for vector-memory operations, so copies for later stages stay in
+// flight; their completion is waited for explicitly (vmcnt) before the
+// barrier that publishes them.  The memory clobber keeps the compiler from
+// moving LDS accesses across it.
 __device__ inline void lds_barrier() {
   __builtin_amdgcn_s_waitcnt(15 | (7 << 4) | (0 << 8) | (3 << 14));
   asm volatile("s_barrier" ::: "memory");
@@ -116,40 +123,33 @@ __device__ inline void lds_barrier() {
 template <int J>
 using Slot = std::integral_constant<int, J>;
 
-template <int GRAN, int BM, int BN, int WAVES>
-__global__ __launch_bounds__(64 * WAVES, 1) void gemm_kernel(const uint8_t* __restrict__ packed,
-                                                      const float* __restrict__ alpha,
-                                                      const uint16_t* __restrict__ x,
-                                                      uint16_t* __restrict__ y, int64_t n, int64_t k,
-                                                      int64_t m, int group_sbs, int tiles_m, int tiles_n) {
-  using C = GemmCfg<GRAN, BM, BN, WAVES>;
-  static_assert(BN == 128, "the record copies and the decode assume 128 weight rows");
-  // record slot: nibble records + sign dwords of one superblock (+ per_group:
-  // the scales of its group)
-  constexpr int kAlphaOff = BN * 16 + BN * 4;
-  constexpr int kRecBytes = kAlphaOff + (C::kGroup ? BN * 4 : 0);
-  // Three-deep rings, one __shared__ object per slot: the compiler's wait
-  // insertion then knows an LDS read of one slot never aliases the direct
-  // copies in flight into another.
-  __shared__ __attribute__((aligned(16))) char xs0[BM * kRowBytes], xs1[BM * kRowBytes], xs2[BM * kRowBytes];
-  __shared__ __attribute__((aligned(16))) char ws0[BN * kRowBytes], ws1[BN * kRowBytes], ws2[BN * kRowBytes];
-  __shared__ __attribute__((aligned(16))) char rc0[kRecBytes], rc1[kRecBytes], rc2[kRecBytes];
+// grid: x = tiles (tiles_m * tiles_n), y = K splits.  partial == nullptr:
+// write bf16 Y; else write fp32 partial[split][m][n] (per_group already
+// scaled, per_channel / per_tensor not yet).
+template <int GRAN, int TM>
+__global__ __launch_bounds__(kThreads, 2) void gemm_kernel(const uint8_t* packed,
+                                                     const float* __restrict__ alpha,
+                                                     const uint16_t* __restrict__ x,
+                                                     uint16_t* __restrict__ y, float* __restrict__ partial,
+                                                     int64_t n, int64_t k, int64_t m, int group_sbs,
+                                                     int tiles_m, int tiles_n, int sb_per_split) {
+  using C = GemmCfg<GRAN, TM>;
+  constexpr int kTM = C::kTM, kBM = C::kBM, kXLoads = C::kXLoads;
+  // one __shared__ object per ring slot: the compiler's wait insertion then
+  // knows an LDS read of one slot never aliases the copies in flight into
+  // another
+  constexpr int kSlot = kBM * kRowBytes + kRecWave * kWaves;  // activation tile, then the records
+  __shared__ __attribute__((aligned(16))) char sl0[kSlot], sl1[kSlot], sl2[kSlot];
   __shared__ __attribute__((aligned(16))) uint2 dtab[32];
 
   auto XS = [&](auto J) -> char* {
-    if constexpr (decltype(J)::value == 0) return xs0; else if constexpr (decltype(J)::value == 1) return xs1; else return xs2;
+    if constexpr (decltype(J)::value == 0) return sl0; else if constexpr (decltype(J)::value == 1) return sl1; else return sl2;
   };
-  auto WS = [&](auto J) -> char* {
-    if constexpr (decltype(J)::value == 0) return ws0; else if constexpr (decltype(J)::value == 1) return ws1; else return ws2;
-  };
-  auto RC = [&](auto J) -> char* {
-    if constexpr (decltype(J)::value == 0) return rc0; else if constexpr (decltype(J)::value == 1) return rc1; else return rc2;
-  };
+  auto RC = [&](auto J) -> char* { return XS(J) + kBM * kRowBytes; };
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
-  const int wm = wave % C::WAVES_M, wn = wave / C::WAVES_M;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int r = lane & 15, q = lane >> 4;
 
   // XCD-aware tile order: consecutive workgroup ids land on different XCDs;
@@ -158,127 +158,160 @@ __global__ __launch_bounds__(64 * WAVES, 1) void gemm_kernel(const uint8_t* __re
   int bid = blockIdx.x;
   if ((tiles & 7) == 0) bid = (bid & 7) * (tiles >> 3) + (bid >> 3);
   const int tm = bid / tiles_n, tn = bid % tiles_n;
-  const int64_t m0 = (int64_t)tm * BM;
-  const int64_t n0 = (int64_t)tn * BN;
+  const int64_t m0 = (int64_t)tm * kBM;
+  const int64_t n0 = (int64_t)tn * kBN;
+  const int kz = blockIdx.y;
+  const int64_t sb0 = (int64_t)kz * sb_per_split;  // first superblock of this split
+  const int stages = 2 * sb_per_split;
 
   if (tid < 32) dtab[tid] = decode_bf16(tid);
 
-  const int64_t nsb = k / kSuperblock;
-  const int stages = (int)(nsb * 2);
-  const uint8_t* __restrict__ nib_plane = packed;
-  const uint8_t* __restrict__ sgn_plane = packed + nibble_plane_bytes(n, k);
+  // (no __restrict__ on the weight pointers: the record loads must stay where
+  // they are issued, not float across the LDS barriers)
+  const uint8_t* nib_plane = packed;
+  const uint8_t* sgn_plane = packed + nibble_plane_bytes(n, k);
 
-  // this thread decodes weight row tid / THREADS_PER_ROW; wave w owns rows
-  // ROWS_PER_WAVE*w .. +ROWS_PER_WAVE-1, which it also copies
-  const int wrow = tid / C::THREADS_PER_ROW;
-  const int wsub = tid % C::THREADS_PER_ROW;
-
-  // Direct copies of stage st into ring slot J.  X: wave w copies rows
-  // [w*BM/WAVES, (w+1)*BM/WAVES) in pieces of 8 rows; lane l -> physical chunk
-  // l%8 of row l/8, which holds logical chunk (l%8) ^ swz_key(row).  Records:
-  // each wave copies the rows it decodes (the other lanes idle).
-  // X copies are buffer loads: the per-stage base is wave-uniform (a buffer
-  // resource in SGPRs), the lane offset a 32-bit VGPR, and rows past m fall
-  // outside the resource's range, so they read zeros (the host keeps
-  // (m + BM) * k * 2 below 2^31).  The lane part of the offset only depends
-  // on the parity of the 8-row piece (the swizzle key has period 16 rows).
-  static_assert(C::XLOADS % 2 == 0, "pieces of one wave alternate parity");
-  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+  // Activation copies: piece p (8 rows) of a stage goes to LDS bytes
+  // [1024p, 1024p + 1024); lane l of the copy fetches physical chunk l%8 of
+  // row 8p + l/8, i.e. logical chunk (l%8) ^ swz_key(row).  The key has a
+  // period of 16 rows, so the lane part of the offset depends only on the
+  // piece's parity.  Rows past m fall outside the buffer resource's range and
+  // read zeros (the host keeps (m + 128) * k * 2 below 2^31).
+  static_assert(kXLoads % 2 == 0, "pieces of one wave alternate parity");
   uint32_t xlane[2];
 #pragma unroll
-  for (int p = 0; p < 2; ++p) {
-    const int prow = p * 8 + (lane >> 3);
-    xlane[p] = (uint32_t)((lane >> 3) * k * 2) + (uint32_t)((((lane & 7) ^ swz_key(prow))) * 16);
-  }
+  for (int p = 0; p < 2; ++p)
+    xlane[p] = (uint32_t)((lane >> 3) * k * 2) + (uint32_t)(((lane & 7) ^ swz_key(p * 8 + (lane >> 3))) * 16);
   const uint32_t xbytes = (uint32_t)(m * k * 2);
-  int64_t rrow = n0 + wave * C::ROWS_PER_WAVE + (lane % C::ROWS_PER_WAVE);
-  rrow = rrow < n ? rrow : n - 1;
-  const uint32_t nrow_off = (uint32_t)(rrow * 16), srow_off = (uint32_t)(rrow * 4);
+
+  // weight row whose records this lane copies: n0 + 32 wave + lane % 32
+  // (clamped rows feed only outputs that are not stored)
+  int64_t crow = n0 + wave * kWN + (lane & 31);
+  crow = crow < n ? crow : n - 1;
+
   auto issue = [&](auto J, int st) {
-    const uint32_t sbyte = (uint32_t)st * (kStageK * 2);
+    const int64_t sb = sb0 + (st >> 1);
+    const uint32_t sbyte = (uint32_t)((sb * 2 + (st & 1)) * (kStageK * 2));
     const __amdgpu_buffer_rsrc_t xr = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<char*>(reinterpret_cast<const char*>(x)) + sbyte, (short)0, (int)(xbytes - sbyte), kBufferWord3);
     char* xb = XS(J);
 #pragma unroll
-    for (int i = 0; i < C::XLOADS; ++i) {
-      const int piece = wave_u * C::XLOADS + i;
+    for (int i = 0; i < kXLoads; ++i) {
+      const int piece = wave * kXLoads + i;
       const uint32_t voff = xlane[i & 1] + (uint32_t)((m0 + piece * 8) * k * 2);
       __builtin_amdgcn_raw_ptr_buffer_load_lds(xr, (lds_void*)(xb + piece * 1024), 16, voff, 0, 0, 0);
     }
-    char* rb = RC(J);
-    const int64_t g = st >> 1;
-    if (lane < C::ROWS_PER_WAVE) {
-      g2l_16(nib_plane + g * n * 16 + nrow_off, rb + wave * C::ROWS_PER_WAVE * 16);
-      g2l_4(sgn_plane + g * n * 4 + srow_off, rb + BN * 16 + wave * C::ROWS_PER_WAVE * 4);
-      if constexpr (C::kGroup)
-        g2l_4(alpha + (g / group_sbs) * n + (srow_off >> 2), rb + kAlphaOff + wave * C::ROWS_PER_WAVE * 4);
-    }
-  };
-  // Decode stage st from record slot J into the bf16 tile slot J.  Byte cb
-  // of nibble dword d holds blocks 8cb + 2d and 8cb + 2d + 1 = the 8 weights
-  // of chunk d + 4cb; stage st covers cb = 2*(st&1) + {0, 1}, i.e. 8 chunks
-  // per row, CHUNKS_PER_THREAD of them per thread.
-  auto decode = [&](auto J, int st) {
-    const char* rb = RC(J);
-    char* wb = WS(J);
-    const uint4 nr = *reinterpret_cast<const uint4*>(rb + wrow * 16);
-    const uint32_t sg = *reinterpret_cast<const uint32_t*>(rb + BN * 16 + wrow * 4);
-    const uint32_t nd[4] = {nr.x, nr.y, nr.z, nr.w};
-#pragma unroll
-    for (int cc = 0; cc < C::CHUNKS_PER_THREAD; ++cc) {
-      const int lc = wsub * C::CHUNKS_PER_THREAD + cc;  // 0..7: (cb & 1, d)
-      const int d = lc & 3;
-      const int cb = 2 * (st & 1) + (lc >> 2);
-      const uint32_t byte = __builtin_amdgcn_ubfe(nd[d], 8 * cb, 8);
-      const uint32_t s2 = __builtin_amdgcn_ubfe(sg, 2 * d + 8 * cb, 2);
-      const uint2 lo = dtab[(byte & 15u) | ((s2 & 1u) << 4)];
-      const uint2 hi = dtab[(byte >> 4) | ((s2 >> 1) << 4)];
-      *reinterpret_cast<u32x4*>(wb + swz(wrow, lc)) = u32x4{lo.x, lo.y, hi.x, hi.y};
-    }
+    char* rb = RC(J) + wave * kRecWave;
+    __builtin_amdgcn_global_load_lds(const_cast<uint8_t*>(nib_plane + sb * n * 16 + crow * 16),
+                                     (lds_void*)(rb + kRecNib), 16, 0, 0);
+    __builtin_amdgcn_global_load_lds(const_cast<uint8_t*>(sgn_plane + sb * n * 4 + crow * 4),
+                                     (lds_void*)(rb + kRecSgn), 4, 0, 0);
+    if constexpr (C::kGroup)
+      __builtin_amdgcn_global_load_lds(const_cast<float*>(alpha + (int64_t)((int)sb / group_sbs) * n + crow),
+                                       (lds_void*)(rb + kRecAlpha), 4, 0, 0);
   };
 
-  f32x4 acc[C::TN][C::TM];
-  f32x4 accg[C::kGroup ? C::TN : 1][C::kGroup ? C::TM : 1];
+  // This lane's records of the next stage: nibble dword q and the sign dword
+  // of rows r and 16 + r of its wave's rows, and for per_group the scales of
+  // rows 4q .. 4q+3 and 16 + 4q .. .  Each wave copies its own records, so
+  // they are read right after its own wait for the copies, before the
+  // barrier.  The reads are one asm block that waits for its own results:
+  // the compiler cannot tell these LDS reads from ones that might overlap
+  // copies still in flight and would otherwise wait for every copy.
+  static_assert(kTN == 2, "the record reads below cover two row tiles");
+  uint32_t nd[kTN], sg[kTN];
+  f32x4 av[C::kGroup ? kTN : 1];
+  auto read_records = [&](auto J) {
+    const uint32_t rb = (uint32_t)(size_t)(__attribute__((address_space(3))) char*)(RC(J) + wave * kRecWave);
+    const uint32_t a_nib = rb + kRecNib + r * 16 + q * 4;
+    const uint32_t a_sgn = rb + kRecSgn + r * 4;
+    uint32_t n0v, n1v, s0v, s1v;
+    if constexpr (C::kGroup) {
+      const uint32_t a_al = rb + kRecAlpha + q * 16;
+      f32x4 a0v, a1v;
+      asm volatile(
+          "ds_read_b32 %0, %6\n"
+          "ds_read_b32 %1, %6 offset:256\n"
+          "ds_read_b32 %2, %7\n"
+          "ds_read_b32 %3, %7 offset:64\n"
+          "ds_read_b128 %4, %8\n"
+          "ds_read_b128 %5, %8 offset:64\n"
+          "s_waitcnt lgkmcnt(0)"
+          : "=&v"(n0v), "=&v"(n1v), "=&v"(s0v), "=&v"(s1v), "=&v"(a0v), "=&v"(a1v)
+          : "v"(a_nib), "v"(a_sgn), "v"(a_al)
+          : "memory");
+      av[0] = a0v;
+      av[C::kGroup ? 1 : 0] = a1v;
+    } else {
+      asm volatile(
+          "ds_read_b32 %0, %4\n"
+          "ds_read_b32 %1, %4 offset:256\n"
+          "ds_read_b32 %2, %5\n"
+          "ds_read_b32 %3, %5 offset:64\n"
+          "s_waitcnt lgkmcnt(0)"
+          : "=&v"(n0v), "=&v"(n1v), "=&v"(s0v), "=&v"(s1v)
+          : "v"(a_nib), "v"(a_sgn)
+          : "memory");
+    }
+    nd[0] = n0v; nd[1] = n1v; sg[0] = s0v; sg[1] = s1v;
+  };
+
+  f32x4 acc[kTN][kTM];
+  f32x4 accg[C::kGroup ? kTN : 1][C::kGroup ? kTM : 1];
 #pragma unroll
-  for (int i = 0; i < C::TN; ++i)
+  for (int i = 0; i < kTN; ++i)
 #pragma unroll
-    for (int j = 0; j < C::TM; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int jj = 0; jj < kTM; ++jj) acc[i][jj] = f32x4{0.f, 0.f, 0.f, 0.f};
   int gpos = 0;  // superblocks done in the current group (its first stage zeroes accg)
 
   // One stage: stage st sits in slot J = st % 3.
   auto stage = [&](auto J, int st) {
-    constexpr int j = decltype(J)::value;
-    constexpr int j1 = (j + 1) % 3, j2 = (j + 2) % 3;
+    constexpr int j2 = (decltype(J)::value + 2) % 3;
     const bool group_end = C::kGroup && (st & 1) == 1 && gpos + 1 == group_sbs;
-    // copies two stages ahead (slot j2 was consumed in the previous stage)
-    const bool ahead = st + 2 < stages;
-    if (ahead) issue(Slot<j2>{}, st + 2);
+    // copies two stages ahead into slot j2 (consumed in the previous stage).
+    // Issued unconditionally, so every stage has the same number of memory
+    // operations in flight and the compiler's waits for the weight records
+    // stay two stages behind; past the end they repeat the last stage into a
+    // slot nobody reads.
+    issue(Slot<j2>{}, st + 2 < stages ? st + 2 : stages - 1);
 
     const char* xb = XS(J);
-    const char* wb = WS(J);
-    // per_group: the first k-step of a group starts its accumulators from 0
+    const char* dt = reinterpret_cast<const char*>(dtab);
     auto mma = [&](auto zero_c) {
 #pragma unroll
       for (int kk = 0; kk < kStageK / 32; ++kk) {
+        // byte cb of nibble dword q: blocks 8cb + 2q (low nibble) and
+        // 8cb + 2q + 1 (high) = k 32cb + 8q .. +7 of the superblock, which is
+        // chunk q of k-step kk of this stage
+        const int cb = 2 * (st & 1) + kk;
+        bf16x8 a[kTN];
+#pragma unroll
+        for (int i = 0; i < kTN; ++i) {
+          const uint32_t byte = __builtin_amdgcn_ubfe(nd[i], 8 * cb, 8);
+          const uint32_t s2 = __builtin_amdgcn_ubfe(sg[i], 8 * cb + 2 * q, 2);
+          const uint32_t lo = ((byte & 15u) | ((s2 & 1u) << 4)) * 8u;
+          const uint32_t hi = ((byte >> 4) | ((s2 >> 1) << 4)) * 8u;
+          const uint2 wl = *reinterpret_cast<const uint2*>(dt + lo);
+          const uint2 wh = *reinterpret_cast<const uint2*>(dt + hi);
+          a[i] = __builtin_bit_cast(bf16x8, u32x4{wl.x, wl.y, wh.x, wh.y});
+        }
         const int ch = kk * 4 + q;
-        bf16x8 a[C::TN], b[C::TM];
+        bf16x8 bv[kTM];
 #pragma unroll
-        for (int i = 0; i < C::TN; ++i)
-          a[i] = *reinterpret_cast<const bf16x8*>(wb + swz(wn * C::WN + i * 16 + r, ch));
+        for (int jj = 0; jj < kTM; ++jj) bv[jj] = *reinterpret_cast<const bf16x8*>(xb + swz(jj * 16 + r, ch));
 #pragma unroll
-        for (int jj = 0; jj < C::TM; ++jj)
-          b[jj] = *reinterpret_cast<const bf16x8*>(xb + swz(wm * C::WM + jj * 16 + r, ch));
+        for (int jj = 0; jj < kTM; ++jj) {
+          const bf16x8 b = bv[jj];
 #pragma unroll
-        for (int i = 0; i < C::TN; ++i)
-#pragma unroll
-          for (int jj = 0; jj < C::TM; ++jj) {
+          for (int i = 0; i < kTN; ++i) {
             if constexpr (C::kGroup) {
               const f32x4 c_in = (decltype(zero_c)::value && kk == 0) ? f32x4{0.f, 0.f, 0.f, 0.f} : accg[i][jj];
-              accg[i][jj] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i], b[jj], c_in, 0, 0, 0);
+              accg[i][jj] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i], b, c_in, 0, 0, 0);
             } else {
-              acc[i][jj] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i], b[jj], acc[i][jj], 0, 0, 0);
+              acc[i][jj] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i], b, acc[i][jj], 0, 0, 0);
             }
           }
+        }
       }
     };
     if (C::kGroup && (st & 1) == 0 && gpos == 0) {
@@ -290,15 +323,13 @@ __global__ __launch_bounds__(64 * WAVES, 1) void gemm_kernel(const uint8_t* __re
     if constexpr (C::kGroup) {
       if ((st & 1) == 1) {
         if (group_end) {
-          // the group's scales came with this stage's record copy
-          const char* rb = RC(J);
+          // the group's scales came with this stage's copies
 #pragma unroll
-          for (int i = 0; i < C::TN; ++i) {
-            const f32x4 av = *reinterpret_cast<const f32x4*>(rb + kAlphaOff + (wn * C::WN + i * 16 + 4 * q) * 4);
+          for (int i = 0; i < kTN; ++i) {
 #pragma unroll
-            for (int jj = 0; jj < C::TM; ++jj) {
+            for (int jj = 0; jj < kTM; ++jj) {
 #pragma unroll
-              for (int e = 0; e < 4; ++e) acc[i][jj][e] += av[e] * accg[i][jj][e];
+              for (int e = 0; e < 4; ++e) acc[i][jj][e] += av[i][e] * accg[i][jj][e];
             }
           }
           gpos = 0;
@@ -308,33 +339,54 @@ __global__ __launch_bounds__(64 * WAVES, 1) void gemm_kernel(const uint8_t* __re
       }
     }
 
-    if (st + 1 < stages) {
-      // this wave's copies of stage st+1 (issued one stage ago) have landed;
-      // only this stage's copies may still be in flight
-      if (ahead) wait_vmcnt<C::VM_PER_STAGE>(); else wait_vmcnt<0>();
-      decode(Slot<j1>{}, st + 1);
-    }
+    // this wave's copies of stage st+1 (issued one stage ago) have landed;
+    // only this stage's copies may still be in flight
+    wait_vmcnt<C::VM_PER_STAGE>();
+    read_records(Slot<(decltype(J)::value + 1) % 3>{});
     lds_barrier();
   };
 
-  // prologue: stages 0 and 1 copied, stage 0 decoded
+  // prologue: stages 0 and 1 in flight, stage 0 landed
   issue(Slot<0>{}, 0);
-  if (stages > 1) issue(Slot<1>{}, 1);
-  if (stages > 1) wait_vmcnt<C::VM_PER_STAGE>(); else wait_vmcnt<0>();
-  lds_barrier();  // decode table written
-  decode(Slot<0>{}, 0);
-  lds_barrier();
+  issue(Slot<1>{}, stages > 1 ? 1 : 0);
+  wait_vmcnt<C::VM_PER_STAGE>();
+  read_records(Slot<0>{});
+  lds_barrier();  // decode table and stage 0 visible
 
-  for (int st = 0; st < stages; st += 3) {
+  // (every early exit leaves the loop, so each path into a stage passes
+  // through the stage before it: that keeps the compiler's own waits for the
+  // weight records two stages behind)
+  for (int st = 0;; st += 3) {
     stage(Slot<0>{}, st);
-    if (st + 1 < stages) stage(Slot<1>{}, st + 1);
-    if (st + 2 < stages) stage(Slot<2>{}, st + 2);
+    if (st + 1 >= stages) break;
+    stage(Slot<1>{}, st + 1);
+    if (st + 2 >= stages) break;
+    stage(Slot<2>{}, st + 2);
+    if (st + 3 >= stages) break;
   }
+  wait_vmcnt<0>();  // the trailing repeat copies have landed before the wave ends
 
-  // epilogue: lane holds Y[m0 + wm*WM + 16j + r][n0 + wn*WN + 16i + 4q + e]
+  // epilogue: lane holds Y[m0 + 16jj + r][n0 + 32 wave + 16i + 4q + e]
 #pragma unroll
-  for (int i = 0; i < C::TN; ++i) {
-    const int64_t gn0 = n0 + wn * C::WN + i * 16 + 4 * q;
+  for (int i = 0; i < kTN; ++i) {
+    const int64_t gn0 = n0 + wave * kWN + i * 16 + 4 * q;
+    const bool full4 = gn0 + 3 < n && (n & 3) == 0;
+    if (partial != nullptr) {
+      float* pz = partial + (int64_t)kz * m * n;
+#pragma unroll
+      for (int jj = 0; jj < kTM; ++jj) {
+        const int64_t gm = m0 + jj * 16 + r;
+        if (gm >= m) continue;
+        float* dst = pz + gm * n + gn0;
+        if (full4) {
+          *reinterpret_cast<f32x4*>(dst) = acc[i][jj];
+        } else {
+          for (int e = 0; e < 4; ++e)
+            if (gn0 + e < n) dst[e] = acc[i][jj][e];
+        }
+      }
+      continue;
+    }
     float sc[4] = {1.f, 1.f, 1.f, 1.f};
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
@@ -342,14 +394,14 @@ __global__ __launch_bounds__(64 * WAVES, 1) void gemm_kernel(const uint8_t* __re
       if constexpr (GRAN == SHERRY_PER_TENSOR) sc[e] = alpha[0];
     }
 #pragma unroll
-    for (int jj = 0; jj < C::TM; ++jj) {
-      const int64_t gm = m0 + wm * C::WM + jj * 16 + r;
+    for (int jj = 0; jj < kTM; ++jj) {
+      const int64_t gm = m0 + jj * 16 + r;
       if (gm >= m) continue;
       uint16_t h[4];
 #pragma unroll
       for (int e = 0; e < 4; ++e) h[e] = f32_to_bf16_rne(acc[i][jj][e] * sc[e]);
       uint16_t* dst = y + gm * n + gn0;
-      if (gn0 + 3 < n && (n & 3) == 0) {
+      if (full4) {
         *reinterpret_cast<uint2*>(dst) = make_uint2(h[0] | ((uint32_t)h[1] << 16), h[2] | ((uint32_t)h[3] << 16));
       } else {
         for (int e = 0; e < 4; ++e)
@@ -359,53 +411,120 @@ __global__ __launch_bounds__(64 * WAVES, 1) void gemm_kernel(const uint8_t* __re
   }
 }
 
-template <int GRAN, int BM, int WAVES>
-hipError_t launch_t(int64_t n, int64_t k, int group_sbs, const uint8_t* packed, const float* alpha,
-                    const uint16_t* x, int64_t m, uint16_t* y, hipStream_t s) {
-  constexpr int BN = 128;
-  // one launch covers at most `chunk` rows of X so that its buffer offsets,
-  // including the tail tile's rows past the end, stay below 2^31 bytes
-  const int64_t chunk = ((((int64_t)1 << 31) / (2 * k) - BM) / BM) * BM;
-  if (chunk < BM) return hipErrorInvalidValue;
-  const int tiles_n = (int)((n + BN - 1) / BN);
+// Y = bf16(scale(n) * sum over splits, in split order, of partial[z][m][n]).
+template <int GRAN>
+__global__ __launch_bounds__(256) void gemm_split_reduce(const float* __restrict__ partial,
+                                                         const float* __restrict__ alpha,
+                                                         uint16_t* __restrict__ y, int64_t mn, int64_t n,
+                                                         int splits) {
+  const int64_t i0 = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) * 4;
+  if (i0 >= mn) return;
+  float s[4] = {0.f, 0.f, 0.f, 0.f};
+  if ((mn & 3) == 0) {
+    for (int z = 0; z < splits; ++z) {
+      const f32x4 v = *reinterpret_cast<const f32x4*>(partial + z * mn + i0);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) s[e] += v[e];
+    }
+  } else {
+    for (int z = 0; z < splits; ++z)
+      for (int e = 0; e < 4; ++e)
+        if (i0 + e < mn) s[e] += partial[z * mn + i0 + e];
+  }
+  uint16_t h[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    float sc = 1.f;
+    if constexpr (GRAN == SHERRY_PER_CHANNEL) sc = (i0 + e < mn) ? alpha[(i0 + e) % n] : 0.f;
+    if constexpr (GRAN == SHERRY_PER_TENSOR) sc = alpha[0];
+    h[e] = f32_to_bf16_rne(s[e] * sc);
+  }
+  if ((mn & 3) == 0) {
+    *reinterpret_cast<uint2*>(y + i0) = make_uint2(h[0] | ((uint32_t)h[1] << 16), h[2] | ((uint32_t)h[3] << 16));
+  } else {
+    for (int e = 0; e < 4; ++e)
+      if (i0 + e < mn) y[i0 + e] = h[e];
+  }
+}
+
+// Rows of X per launch: buffer offsets, including the tail tile's rows past
+// the end, stay below 2^31 bytes.
+int64_t gemm_chunk_rows(int64_t k) { return ((((int64_t)1 << 31) / (2 * k) - kMaxBM) / kMaxBM) * kMaxBM; }
+
+template <int GRAN, int TM>
+hipError_t launch_g(const GemmPlan& p, int64_t n, int64_t k, int group_sbs, const uint8_t* packed,
+                    const float* alpha, const uint16_t* x, int64_t m, uint16_t* y, float* ws, hipStream_t s) {
+  constexpr int kBM = GemmCfg<GRAN, TM>::kBM;
+  const int64_t chunk = gemm_chunk_rows(k);
+  if (chunk < kMaxBM) return hipErrorInvalidValue;
+  const int tiles_n = (int)((n + kBN - 1) / kBN);
+  const int64_t nsb = k / kSuperblock;
+  const int splits = p.splits;
+  const int sb_per_split = (int)(nsb / splits);
   for (int64_t r0 = 0; r0 < m; r0 += chunk) {
     const int64_t mc = m - r0 < chunk ? m - r0 : chunk;
-    const int tiles_m = (int)((mc + BM - 1) / BM);
-    hipLaunchKernelGGL((gemm_kernel<GRAN, BM, BN, WAVES>), dim3((unsigned)(tiles_m * tiles_n)), dim3(64 * WAVES), 0,
-                       s, packed, alpha, x + r0 * k, y + r0 * n, n, k, mc, group_sbs, tiles_m, tiles_n);
-    const hipError_t e = hipGetLastError();
+    const int tiles_m = (int)((mc + kBM - 1) / kBM);
+    hipLaunchKernelGGL((gemm_kernel<GRAN, TM>), dim3((unsigned)(tiles_m * tiles_n), (unsigned)splits), dim3(kThreads), 0,
+                       s, packed, alpha, x + r0 * k, y + r0 * n, splits > 1 ? ws : nullptr, n, k, mc, group_sbs,
+                       tiles_m, tiles_n, sb_per_split);
+    hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
+    if (splits > 1) {
+      const int64_t mn = mc * n;
+      const int64_t threads = (mn + 3) / 4;
+      hipLaunchKernelGGL((gemm_split_reduce<GRAN>), dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, s, ws,
+                         alpha, y + r0 * n, mn, n, splits);
+      e = hipGetLastError();
+      if (e != hipSuccess) return e;
+    }
   }
   return hipSuccess;
 }
 
-template <int GRAN>
-hipError_t launch_g(const GemmPlan& p, int64_t n, int64_t k, int group_sbs, const uint8_t* packed,
-                    const float* alpha, const uint16_t* x, int64_t m, uint16_t* y, hipStream_t s) {
-  if (p.tile_m == 256) return launch_t<GRAN, 256, SHERRY_GEMM_WAVES>(n, k, group_sbs, packed, alpha, x, m, y, s);
-  return launch_t<GRAN, 128, 4>(n, k, group_sbs, packed, alpha, x, m, y, s);
-}
-
 }  // namespace
 
+// Splits of K for launches with few tiles.  Model: a CU runs `per_cu`
+// workgroups at a time, so a launch takes ceil(workgroups / (256 per_cu))
+// rounds of (2 * superblocks per split + 3) stage times; a split adds its
+// partial traffic (written once, read once) at HBM speed plus one small
+// launch.
 GemmPlan plan_gemm(int64_t n, int64_t k, int gran, int group_size, int64_t m) {
-  (void)k; (void)group_size;
   GemmPlan p{};
-  p.tile_n = 128;
-  // 256-row tiles (8 waves of 64 x 64) once they still give >= 2 tiles per CU
-  const int64_t big = ((m + 255) / 256) * ((n + 127) / 128);
-  p.tile_m = (big >= 512 && (gran != SHERRY_PER_GROUP || SHERRY_GEMM_WAVES == 8)) ? 256 : 128;
-  p.workspace_bytes = 0;
+  const bool group = gran == SHERRY_PER_GROUP;
+  p.tile_n = kBN;
+  p.tile_m = group ? GemmCfg<SHERRY_PER_GROUP, 4>::kBM : GemmCfg<SHERRY_PER_CHANNEL, 8>::kBM;
+  p.splits = 1;
+  const int64_t nsb = k / kSuperblock;
+  const int64_t group_sbs = group ? group_size / kSuperblock : 1;
+  const int64_t chunk = gemm_chunk_rows(k);
+  const int64_t mc = chunk > 0 && m > chunk ? chunk : m;
+  const int64_t tiles = ((mc + p.tile_m - 1) / p.tile_m) * ((n + kBN - 1) / kBN);
+  const int64_t slots = 256 * (group ? 3 : 2);  // workgroups resident at once
+  const double stage_us = group ? 0.75 : 1.0;   // one 64-k stage of a round
+  const double hbm_bytes_per_us = 5.0e6;        // partial traffic
+  double best = -1.0;
+  for (int s = 1; s <= kMaxSplits; s *= 2) {
+    if (nsb % s != 0 || (nsb / s) % group_sbs != 0) continue;
+    if (s > 1 && nsb / s < 2) continue;  // at least 256 k per split
+    const double rounds = (double)((tiles * s + slots - 1) / slots);
+    double t = rounds * (2.0 * (double)(nsb / s) + 3.0) * stage_us;
+    if (s > 1) t += (double)(s + 1) * (double)mc * (double)n * 4.0 / hbm_bytes_per_us + 3.0;
+    if (best < 0.0 || t < best) {
+      best = t;
+      p.splits = s;
+    }
+  }
+  p.workspace_bytes = p.splits > 1 ? (size_t)p.splits * (size_t)mc * (size_t)n * sizeof(float) : 0;
   return p;
 }
 
 hipError_t launch_gemm(const GemmPlan& p, int64_t n, int64_t k, int gran, int group_size,
                        const uint8_t* packed, const float* alpha, const uint16_t* x, int64_t m,
-                       uint16_t* y, hipStream_t s) {
+                       uint16_t* y, float* ws, hipStream_t s) {
   const int group_sbs = gran == SHERRY_PER_GROUP ? group_size / kSuperblock : 1;
-  if (gran == SHERRY_PER_GROUP) return launch_g<SHERRY_PER_GROUP>(p, n, k, group_sbs, packed, alpha, x, m, y, s);
-  if (gran == SHERRY_PER_CHANNEL) return launch_g<SHERRY_PER_CHANNEL>(p, n, k, group_sbs, packed, alpha, x, m, y, s);
-  return launch_g<SHERRY_PER_TENSOR>(p, n, k, group_sbs, packed, alpha, x, m, y, s);
+  if (gran == SHERRY_PER_GROUP) return launch_g<SHERRY_PER_GROUP, 4>(p, n, k, group_sbs, packed, alpha, x, m, y, ws, s);
+  if (gran == SHERRY_PER_CHANNEL) return launch_g<SHERRY_PER_CHANNEL, 8>(p, n, k, group_sbs, packed, alpha, x, m, y, ws, s);
+  return launch_g<SHERRY_PER_TENSOR, 8>(p, n, k, group_sbs, packed, alpha, x, m, y, ws, s);
 }
 
 }  // namespace sherry

@@ -168,9 +168,10 @@ int32_t sherry_gemm(int64_t n, int64_t k, int32_t granularity, int32_t group_siz
   const GemmPlan plan = plan_gemm(n, k, granularity, group_size, m);
   if (plan.workspace_bytes > 0 && (!workspace || workspace_bytes < plan.workspace_bytes))
     return SHERRY_ERR_WORKSPACE;
+  if (plan.workspace_bytes > 0 && !aligned16(workspace)) return SHERRY_ERR_ALIGN;
   return hip_status(launch_gemm(plan, n, k, granularity, group_size, static_cast<const uint8_t*>(packed), alpha,
                                 static_cast<const uint16_t*>(x), m, static_cast<uint16_t*>(y),
-                                static_cast<hipStream_t>(stream)));
+                                static_cast<float*>(workspace), static_cast<hipStream_t>(stream)));
 }
 
 }  // extern "C"

@@ -52,12 +52,13 @@ hipError_t launch_gemv(const GemvPlan& p, int64_t n, int64_t k, int gran, int gr
 // ---------------------------------------------------------------- gemm
 struct GemmPlan {
   int tile_n, tile_m;
-  size_t workspace_bytes;
+  int splits;              // K ranges per output tile (1 = none)
+  size_t workspace_bytes;  // splits > 1: fp32 partials [splits][M][N]
 };
 GemmPlan plan_gemm(int64_t n, int64_t k, int gran, int group_size, int64_t m);
 hipError_t launch_gemm(const GemmPlan& p, int64_t n, int64_t k, int gran, int group_size,
                        const uint8_t* packed, const float* alpha, const uint16_t* x, int64_t m,
-                       uint16_t* y, hipStream_t s);
+                       uint16_t* y, float* ws, hipStream_t s);
 
 // ---------------------------------------------------------------- device helpers
 // Round an fp32 value to bf16, nearest-even (inputs are finite).

@@ -51,13 +51,12 @@ constexpr int kThreads = 64 * kWaves;
 constexpr int kTN = 2;                      // MFMA tiles per wave along n
 constexpr int kWN = 16 * kTN;               // 32 weight rows per wave
 constexpr int kBN = kWN * kWaves;           // 128 weight rows per tile
-constexpr int kMaxBM = 128;                 // largest activation tile (rows)
+constexpr int kMaxBM = 128;                 // largest activation tile (rows) the host chunking allows for
+constexpr int kGemmTM = 4;                  // MFMA tiles per wave along m: 64-row tiles
 // Per-wave record area of a ring slot: lane l copies the records of weight
 // row 32 wave + l % 32 (lanes >= 32 duplicate, so the copies need no branch):
 // 64 nibble records (16 B), 64 sign dwords, and for per_group 64 scales.
 constexpr int kRecNib = 0, kRecSgn = 64 * 16, kRecAlpha = kRecSgn + 64 * 4;
-constexpr int kRecWave = kRecAlpha + 64 * 4;
-constexpr int kMaxSplits = 16;
 
 // Activation LDS rows are 128 bytes = 8 chunks of 16 bytes; chunk c of row r
 // sits at physical chunk c ^ ((r >> 1) & 7).  An MFMA operand read (16 rows x
@@ -92,6 +91,7 @@ struct GemmCfg {
   static constexpr int kTM = TM;
   static constexpr int kBM = 16 * TM;              // rows of X per tile
   static constexpr int kXLoads = kBM / 8 / kWaves;  // 1 KB activation copies per wave per stage
+  static constexpr int kRecWave = kRecAlpha + (kGroup ? 64 * 4 : 0);  // record bytes per wave
   // vector-memory operations per wave per stage: activation pieces, nibble
   // and sign records, and for per_group the scales
   static constexpr int VM_PER_STAGE = kXLoads + 2 + (kGroup ? 1 : 0);
@@ -127,14 +127,14 @@ using Slot = std::integral_constant<int, J>;
 // write bf16 Y; else write fp32 partial[split][m][n] (per_group already
 // scaled, per_channel / per_tensor not yet).
 template <int GRAN, int TM>
-__global__ __launch_bounds__(kThreads, 2) void gemm_kernel(const uint8_t* packed,
+__global__ __launch_bounds__(kThreads, 3) void gemm_kernel(const uint8_t* packed,
                                                      const float* __restrict__ alpha,
                                                      const uint16_t* __restrict__ x,
                                                      uint16_t* __restrict__ y, float* __restrict__ partial,
                                                      int64_t n, int64_t k, int64_t m, int group_sbs,
                                                      int tiles_m, int tiles_n, int sb_per_split) {
   using C = GemmCfg<GRAN, TM>;
-  constexpr int kTM = C::kTM, kBM = C::kBM, kXLoads = C::kXLoads;
+  constexpr int kTM = C::kTM, kBM = C::kBM, kXLoads = C::kXLoads, kRecWave = C::kRecWave;
   // one __shared__ object per ring slot: the compiler's wait insertion then
   // knows an LDS read of one slot never aliases the copies in flight into
   // another
@@ -483,37 +483,23 @@ hipError_t launch_g(const GemmPlan& p, int64_t n, int64_t k, int group_sbs, cons
 
 }  // namespace
 
-// Splits of K for launches with few tiles.  Model: a CU runs `per_cu`
-// workgroups at a time, so a launch takes ceil(workgroups / (256 per_cu))
-// rounds of (2 * superblocks per split + 3) stage times; a split adds its
-// partial traffic (written once, read once) at HBM speed plus one small
-// launch.
+// Splits of K for launches with few tiles: the smallest power of two (at most
+// 8) that brings the launch to 512 workgroups (two per CU), over whole groups
+// and at least two superblocks per split.  Measured on the LLaMA-3.2-1B
+// shapes at M = 512 and 2048, fuller launches gain nothing from splitting and
+// deeper splits lose to their shorter K loops and partial traffic.
 GemmPlan plan_gemm(int64_t n, int64_t k, int gran, int group_size, int64_t m) {
   GemmPlan p{};
-  const bool group = gran == SHERRY_PER_GROUP;
   p.tile_n = kBN;
-  p.tile_m = group ? GemmCfg<SHERRY_PER_GROUP, 4>::kBM : GemmCfg<SHERRY_PER_CHANNEL, 8>::kBM;
+  p.tile_m = GemmCfg<SHERRY_PER_GROUP, kGemmTM>::kBM;
   p.splits = 1;
   const int64_t nsb = k / kSuperblock;
-  const int64_t group_sbs = group ? group_size / kSuperblock : 1;
+  const int64_t group_sbs = gran == SHERRY_PER_GROUP ? group_size / kSuperblock : 1;
   const int64_t chunk = gemm_chunk_rows(k);
   const int64_t mc = chunk > 0 && m > chunk ? chunk : m;
   const int64_t tiles = ((mc + p.tile_m - 1) / p.tile_m) * ((n + kBN - 1) / kBN);
-  const int64_t slots = 256 * (group ? 3 : 2);  // workgroups resident at once
-  const double stage_us = group ? 0.75 : 1.0;   // one 64-k stage of a round
-  const double hbm_bytes_per_us = 5.0e6;        // partial traffic
-  double best = -1.0;
-  for (int s = 1; s <= kMaxSplits; s *= 2) {
-    if (nsb % s != 0 || (nsb / s) % group_sbs != 0) continue;
-    if (s > 1 && nsb / s < 2) continue;  // at least 256 k per split
-    const double rounds = (double)((tiles * s + slots - 1) / slots);
-    double t = rounds * (2.0 * (double)(nsb / s) + 3.0) * stage_us;
-    if (s > 1) t += (double)(s + 1) * (double)mc * (double)n * 4.0 / hbm_bytes_per_us + 3.0;
-    if (best < 0.0 || t < best) {
-      best = t;
-      p.splits = s;
-    }
-  }
+  auto valid = [&](int64_t s) { return nsb % s == 0 && (nsb / s) % group_sbs == 0 && nsb / s >= 2; };
+  while (tiles * p.splits < 512 && p.splits < 8 && valid(2 * p.splits)) p.splits *= 2;
   p.workspace_bytes = p.splits > 1 ? (size_t)p.splits * (size_t)mc * (size_t)n * sizeof(float) : 0;
   return p;
 }
@@ -522,9 +508,9 @@ hipError_t launch_gemm(const GemmPlan& p, int64_t n, int64_t k, int gran, int gr
                        const uint8_t* packed, const float* alpha, const uint16_t* x, int64_t m,
                        uint16_t* y, float* ws, hipStream_t s) {
   const int group_sbs = gran == SHERRY_PER_GROUP ? group_size / kSuperblock : 1;
-  if (gran == SHERRY_PER_GROUP) return launch_g<SHERRY_PER_GROUP, 4>(p, n, k, group_sbs, packed, alpha, x, m, y, ws, s);
-  if (gran == SHERRY_PER_CHANNEL) return launch_g<SHERRY_PER_CHANNEL, 8>(p, n, k, group_sbs, packed, alpha, x, m, y, ws, s);
-  return launch_g<SHERRY_PER_TENSOR, 8>(p, n, k, group_sbs, packed, alpha, x, m, y, ws, s);
+  if (gran == SHERRY_PER_GROUP) return launch_g<SHERRY_PER_GROUP, kGemmTM>(p, n, k, group_sbs, packed, alpha, x, m, y, ws, s);
+  if (gran == SHERRY_PER_CHANNEL) return launch_g<SHERRY_PER_CHANNEL, kGemmTM>(p, n, k, group_sbs, packed, alpha, x, m, y, ws, s);
+  return launch_g<SHERRY_PER_TENSOR, kGemmTM>(p, n, k, group_sbs, packed, alpha, x, m, y, ws, s);
 }
 
 }  // namespace sherry

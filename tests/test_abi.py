@@ -143,6 +143,18 @@ def test_gemm_rejects(lib, kw, code):
     assert gm(lib, **kw) == code
 
 
+def test_gemm_workspace_rejected_when_needed(lib):
+    # 128 rows against a 512x2048 weight give 8 output tiles: the plan splits
+    # K, which needs a workspace
+    need = lib.sherry_workspace_bytes(L.OP_GEMM, 512, 2048, L.PER_GROUP, 128, 128, 1)
+    assert need > 0 and need % (512 * 128 * 4) == 0
+    assert gm(lib, n=512, k=2048, m=128) == L.ERR_WORKSPACE
+    assert lib.sherry_gemm(512, 2048, L.PER_GROUP, 128, FAKE, FAKE2, FAKE, 128, FAKE2, FAKE, need - 4,
+                           None) == L.ERR_WORKSPACE
+    assert lib.sherry_gemm(512, 2048, L.PER_GROUP, 128, FAKE, FAKE2, FAKE, 128, FAKE2, MIS, need,
+                           None) == L.ERR_ALIGN
+
+
 def test_binding_raises_value_error():
     with pytest.raises(ValueError):
         L.check(L.ERR_SHAPE)

@@ -314,6 +314,48 @@ def test_gemm_correlated_inputs(gran):
     gemm_case(130, 384, 129, 1030, 1030, gran, 128)
 
 
+@pytest.mark.parametrize("n,k,m", [(512, 2048, 128), (300, 1024, 70), (2048, 8192, 64)])
+@pytest.mark.parametrize("gran", ["per_group", "per_channel", "per_tensor"])
+def test_gemm_split_k(n, k, m, gran):
+    """Few output tiles: the plan splits K into fp32 partials summed by a
+    second kernel; the result is checked and must repeat bit for bit."""
+    from ternary_weight_quantization_sparse_amd import _lib as L
+    need = L.load().sherry_workspace_bytes(L.OP_GEMM, n, k, L.GRANULARITY[gran], 128, m, 1)
+    assert need > 0, "expected a split-K plan for this shape"
+    print(f"[gemm] split-K {n}x{k} M={m} {gran}", flush=True)
+    gemm_case(n, k, m, 960 + n, 961 + m, gran, 128)
+    w = WL.latent_weight(n, k, 960 + n)
+    pw = S.quantize_pack(dev_f32(w), gran, 128)
+    xb, _ = WL.activations_bf16(m, k, 961 + m)
+    x = dev_bf16(xb)
+    y1 = to_np(S.gemm(pw, x))
+    y2 = to_np(S.gemm(pw, x))
+    assert np.array_equal(y1, y2)
+
+
+def test_gemm_rows_past_one_launch():
+    """X larger than 2^31 bytes: the host runs the rows in several launches
+    (32-bit buffer offsets).  Rows on both sides of each launch boundary and
+    the last rows are checked against the oracle."""
+    n, k, m = 64, 8192, 140000
+    print(f"[gemm] {n}x{k} M={m} (two launches)", flush=True)
+    w = WL.latent_weight(n, k, 970)
+    pw = S.quantize_pack(dev_f32(w))
+    gen = torch.Generator(device="cuda").manual_seed(971)
+    x = torch.randn((m, k), generator=gen, device="cuda", dtype=torch.float32).to(torch.bfloat16)
+    y = S.gemm(pw, x)
+    chunk = ((2 ** 31 // (2 * k) - 128) // 128) * 128
+    rows = np.array(sorted({0, 1, chunk - 2, chunk - 1, chunk, chunk + 1, m - 2, m - 1}))
+    xr = x[torch.from_numpy(rows).cuda()].float().cpu().numpy().astype(np.float64)
+    yr = y[torch.from_numpy(rows).cuda()].float().cpu().numpy()
+    del x, y
+    a = to_np(pw.alpha)
+    wq = O.dequant(O.ternary(w), a, "per_group", 128)
+    y_ref = O.gemm(xr, wq)
+    bound = O.tolerance_bound(xr, O.alpha_per_weight(a, n, k, "per_group", 128), y_ref)
+    check_close(yr, y_ref, bound, f"gemm {n}x{k} M={m}")
+
+
 def test_gemm_group_256():
     gemm_case(256, 1024, 192, 950, 951, "per_group", 256)
 

@@ -233,24 +233,59 @@ def bench_gemv_1b(args, dev):
         "value": gbs, "ms_per_step": ms_step, "bytes_per_step": bytes_step,
         "shapes": shape_rows, "checks": checks, "kernel_ms": kernel_ms, "achieved": achieved,
         "launches_per_step": len(launches), "wall_ms_per_step": wall / args.steps,
-    }, pws
+    }, pws, reps
 
 
-def bench_gemv_single_and_warm(pws, dev, steps=50):
-    """Single-call (count=1) latency per shape, warm in cache: context only."""
-    import workloads as WL
-    import ternary_weight_quantization_sparse_amd as S
+def bench_gemv_single_call(reps, dev, warm_calls=256, replays=5):
+    """Single-call (count=1) GEMV per shape, launches captured in a HIP graph
+    so host overhead is out of the picture: context only, not the headline.
+    cold: one call per distinct copy (>= 1 GiB rotation, every byte from HBM);
+    warm: the same copy again and again (L2/Infinity Cache resident)."""
+    import numpy as np
     torch = _torch()
+    import ternary_weight_quantization_sparse_amd as S
     out = []
-    for (name, n, k, pw, _) in pws:
-        xb, _ = WL.activations_bf16(1, k, 200)
-        x = dev_bf16(xb, dev)
-        y = torch.empty((1, n), dtype=torch.bfloat16, device=dev)
-        total, per, _ = timed_launches([lambda: S.gemv(pw, x, out=y)], steps, 5)
-        import numpy as np
-        t = float(np.median(per[0]))
-        nbytes = matrix_bytes(n, k) + 2 * k + 2 * n
-        out.append({"shape": name, "us": t * 1e3, "gbs_warm": nbytes / (t * 1e-3) / 1e9})
+    for (name, rep, x) in reps:
+        n, k = rep.n, rep.k
+        wsb = S.workspace_bytes(2, n, k, rep.pw.granularity, rep.pw.group_size, 1, 1)
+        ws = torch.empty(max(wsb, 16), dtype=torch.uint8, device=dev) if wsb else None
+
+        def call(i):
+            S.gemv_batched(rep.packed_all[i], rep.alpha_all[i], n, k, x, 1, rep.ps, rep.as_,
+                           rep.pw.granularity, rep.pw.group_size, "bfloat16", rep.y[i], rep.y_stride, ws)
+
+        eager = rep.y[0].clone()
+        call(0)
+        torch.cuda.synchronize()
+        eager.copy_(rep.y[0])
+        res = {"shape": name}
+        for mode, idx in (("cold", range(rep.count)), ("warm", [0] * warm_calls)):
+            side = torch.cuda.Stream()
+            side.wait_stream(torch.cuda.current_stream())
+            with torch.cuda.stream(side):
+                call(0)  # warm the allocator / code objects outside capture
+            torch.cuda.current_stream().wait_stream(side)
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                for i in idx:
+                    call(i)
+            g.replay()
+            torch.cuda.synchronize()
+            ok = bool(torch.equal(rep.y[0], eager))
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(replays):
+                g.replay()
+            e1.record()
+            torch.cuda.synchronize()
+            us = e0.elapsed_time(e1) * 1e3 / (replays * len(idx))
+            nbytes = matrix_bytes(n, k) + 2 * k + 2 * n
+            res[mode] = {"us_per_call": us, "gbs": nbytes / (us * 1e-6) / 1e9, "calls_per_replay": len(idx),
+                         "replay_matches_eager": ok}
+            del g
+        log(f"[gemv-single] {name}: cold {res['cold']['us_per_call']:.2f} us "
+            f"({res['cold']['gbs']:.0f} GB/s), warm {res['warm']['us_per_call']:.2f} us")
+        out.append(res)
     return out
 
 
@@ -332,7 +367,7 @@ def bench_quantize(dev, reps=10):
     return res
 
 
-def bench_gemv_3b(dev, batches, steps=10):
+def bench_gemv_3b(dev, batches, steps=50):
     import numpy as np
     import oracle as O
     import workloads as WL
@@ -386,7 +421,7 @@ def bench_gemv_3b(dev, batches, steps=10):
                                    O.tolerance_bound(xv, O.alpha_per_weight(a, n, k, "per_group", 128), y_ref))
             ok_all &= ok
             worst = max(worst, ratio)
-        total, per, _ = timed_launches(launches, steps, 2)
+        total, _, _ = timed_launches(launches, steps, 5, per_launch=False)
         ms = total / steps
         nbytes = sum(rb.algo_bytes() for (_, _, _, rb, _, _, _, _) in reps_b)
         res[f"B{b}"] = {"ms_per_sweep": ms, "bytes": nbytes, "gbs": nbytes / (ms * 1e-3) / 1e9,
@@ -448,10 +483,10 @@ def main():
     dev = torch.device("cuda:0")
     log(f"[bench] {torch.cuda.get_device_name(0)}; steps={args.steps} warmup={args.warmup}")
 
-    gemv, pws = bench_gemv_1b(args, dev)
+    gemv, pws, reps = bench_gemv_1b(args, dev)
     extra = {}
     if "single" in sections:
-        extra["gemv_single_call_warm"] = bench_gemv_single_and_warm(pws, dev)
+        extra["gemv_single_call"] = bench_gemv_single_call(reps, dev)
     if "gemm" in sections:
         extra["gemm"] = bench_gemm(pws, dev, (512, 2048))
     if "quantize" in sections:

@@ -35,6 +35,9 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kLutThreads = 256;
+#ifndef SHERRY_GEMV_SPLIT_TARGET
+#define SHERRY_GEMV_SPLIT_TARGET 2048
+#endif
 #ifndef SHERRY_LUT_WIN_MAX
 #define SHERRY_LUT_WIN_MAX 4  // superblocks per LDS table window (4 -> 16 KB)
 #endif
@@ -303,8 +306,10 @@ __global__ __launch_bounds__(256) void gemv_mfma_kernel(
   const uint8_t* pk = packed + c * packed_stride;
   const uint8_t* __restrict__ sgn_base = pk + nibble_plane_bytes(n, k);
   const float* __restrict__ al = alpha + c * alpha_stride;
-  const bool has_x = r < batch;
-  const uint16_t* xrow = x + (int64_t)(has_x ? r : 0) * k;
+  // lanes past the batch read row 0: they only feed output rows that are not
+  // stored, and an unconditional load lets the compiler issue the window's
+  // activation loads ahead of the MFMAs
+  const uint16_t* xrow = x + (int64_t)(r < batch ? r : 0) * k;
   const char* dt = reinterpret_cast<const char*>(dtbl);
   constexpr bool kGroup = MODE == kGroup1 || MODE == kGroupN;
 
@@ -350,8 +355,7 @@ __global__ __launch_bounds__(256) void gemv_mfma_kernel(
       }
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
-        u32x4 xv = {0u, 0u, 0u, 0u};
-        if (has_x) xv = *reinterpret_cast<const u32x4*>(xrow + g * kSuperblock + 32 * t + 8 * q);
+        const u32x4 xv = *reinterpret_cast<const u32x4*>(xrow + g * kSuperblock + 32 * t + 8 * q);
 #pragma unroll
         for (int i = 0; i < kMfmaTiles; ++i) {
           const uint32_t e0 = *reinterpret_cast<const uint32_t*>(dt + __builtin_amdgcn_ubfe(off_lo[i], 8 * t, 8));
@@ -522,11 +526,13 @@ GemvPlan plan_gemv(int64_t n, int64_t k, int gran, int group_size, int batch, in
     rows_per_wg = 256;
   }
   p.panels = (n + rows_per_wg - 1) / rows_per_wg;
-  // Split K (in whole groups) until the launch has ~1024 workgroups.
+  // Split K (in whole groups) until the launch has ~2048 workgroups (batch 1;
+  // the table kernel keeps 8 per CU resident) or ~1024 (batch > 1).
   const int64_t wgs = p.panels * count;
   const int64_t groups = nsb / group_sbs;
   int64_t split = 1;
-  while (wgs * split * 2 <= 1024 && groups % (split * 2) == 0) split *= 2;
+  const int64_t target = p.kind == 0 ? SHERRY_GEMV_SPLIT_TARGET : 1024;
+  while (wgs * split * 2 <= target && groups % (split * 2) == 0) split *= 2;
   p.ksplit = (int)split;
   const int64_t sb_per_split = nsb / split;
   int win = SHERRY_LUT_WIN_MAX;

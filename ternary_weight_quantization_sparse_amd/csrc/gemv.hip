@@ -25,6 +25,8 @@
 // hold the high bytes of the four bf16 weights (+-0.5 or 0, so the low bytes
 // are 0 and the result is rescaled by 2, exactly); two v_perm_b32 spread a
 // dword into the two bf16x2 operand registers.
+#include <type_traits>
+
 #include "sherry_internal.h"
 
 namespace sherry {
@@ -272,14 +274,19 @@ __device__ inline uint32_t decode_table_entry(uint32_t code) {
 }
 
 // Batch 2..16.  Workgroup = 4 waves; a wave owns 4 tiles of 16 rows (64
-// rows) so every activation fragment feeds 4 MFMAs.  Per window of MWIN
-// superblocks, a lane first loads, for each of its 4 rows, nibble dword q and
-// the sign dword of every superblock (and the group scales), then runs the
-// MFMAs: lane (r, q) supplies blocks 2q+8t and 2q+1+8t (t = 0..3) of row r,
-// i.e. k = 32t + 8q .. +7 of the superblock, and the activations of batch row
-// r at the same k.
+// rows) so every activation fragment feeds 4 MFMAs.  The K loop walks one
+// superblock at a time through a ring of kMfmaDepth register sets: while the
+// MFMAs of superblock g run, the lane's records (nibble dword q and sign dword
+// of its 4 rows, and the group scales) for g + kMfmaDepth - 1 and the
+// activation fragments for g + 1 are already on their way, so the weight
+// stream never waits for a compute phase.  Lane (r, q) supplies blocks 2q+8t
+// and 2q+1+8t (t = 0..3) of row r, i.e. k = 32t + 8q .. +7 of the
+// superblock, and the activations of batch row r at the same k.
 constexpr int kMfmaTiles = 4;
-constexpr int kMfmaWin = 4;
+constexpr int kMfmaDepth = 4;
+
+template <int J>
+using RingSlot = std::integral_constant<int, J>;
 
 template <int MODE, bool YBF16>
 __global__ __launch_bounds__(256) void gemv_mfma_kernel(
@@ -295,7 +302,7 @@ __global__ __launch_bounds__(256) void gemv_mfma_kernel(
   const int wave = threadIdx.x >> 6;
   const int r = lane & 15;  // weight row inside a 16-row tile / batch row of x
   const int q = lane >> 4;  // nibble dword q of each superblock record
-  const int64_t row0 = (int64_t)blockIdx.x * 256 + wave * 64 + r;
+  const int64_t row0 = (int64_t)blockIdx.x * (64 * kMfmaTiles) + wave * (16 * kMfmaTiles) + r;
   const int64_t c = blockIdx.y;
   const int kz = blockIdx.z;
   const int64_t nsb = k / kSuperblock;
@@ -307,8 +314,7 @@ __global__ __launch_bounds__(256) void gemv_mfma_kernel(
   const uint8_t* __restrict__ sgn_base = pk + nibble_plane_bytes(n, k);
   const float* __restrict__ al = alpha + c * alpha_stride;
   // lanes past the batch read row 0: they only feed output rows that are not
-  // stored, and an unconditional load lets the compiler issue the window's
-  // activation loads ahead of the MFMAs
+  // stored, and an unconditional load needs no branch
   const uint16_t* xrow = x + (int64_t)(r < batch ? r : 0) * k;
   const char* dt = reinterpret_cast<const char*>(dtbl);
   constexpr bool kGroup = MODE == kGroup1 || MODE == kGroupN;
@@ -328,65 +334,93 @@ __global__ __launch_bounds__(256) void gemv_mfma_kernel(
   }
   int gpos = 0;
 
-  for (int64_t g0 = sb_begin; g0 < sb_end; g0 += kMfmaWin) {
-    const int wn = (int)((sb_end - g0) < kMfmaWin ? (sb_end - g0) : kMfmaWin);  // last window may be short
-    uint32_t nd[kMfmaWin][kMfmaTiles], sg[kMfmaWin][kMfmaTiles];
-    float av[kMfmaWin][kGroup ? kMfmaTiles : 1];
+  uint32_t nd[kMfmaDepth][kMfmaTiles], sg[kMfmaDepth][kMfmaTiles];
+  float av[kMfmaDepth][kGroup ? kMfmaTiles : 1];
+  u32x4 xf[2][4];
+  // fetches past the split's end repeat its last superblock (never used)
+  auto fetch = [&](auto J, int64_t g) {
+    constexpr int j = decltype(J)::value;
+    g = g < sb_end ? g : sb_end - 1;
 #pragma unroll
-    for (int gi = 0; gi < kMfmaWin; ++gi) {
-      const int64_t g = g0 + (gi < wn ? gi : 0);  // short window: repeat a valid record, unused
+    for (int i = 0; i < kMfmaTiles; ++i) {
+      nd[j][i] = stream_load(reinterpret_cast<const uint32_t*>(pk + g * n * 16 + rows[i] * 16u + q * 4u));
+      sg[j][i] = stream_load(reinterpret_cast<const uint32_t*>(sgn_base + g * n * 4 + rows[i] * 4u));
+      if constexpr (MODE == kGroup1) av[j][i] = stream_load(al + g * n + rows[i]);
+      if constexpr (MODE == kGroupN) av[j][i] = stream_load(al + (g / group_sbs) * n + rows[i]);
+    }
+  };
+  auto fetch_x = [&](auto X, int64_t g) {
+    constexpr int xs = decltype(X)::value;
+    g = g < sb_end ? g : sb_end - 1;
 #pragma unroll
-      for (int i = 0; i < kMfmaTiles; ++i) {
-        nd[gi][i] = stream_load(reinterpret_cast<const uint32_t*>(pk + g * n * 16 + rows[i] * 16u + q * 4u));
-        sg[gi][i] = stream_load(reinterpret_cast<const uint32_t*>(sgn_base + g * n * 4 + rows[i] * 4u));
-        if constexpr (MODE == kGroup1) av[gi][i] = stream_load(al + g * n + rows[i]);
-        if constexpr (MODE == kGroupN) av[gi][i] = stream_load(al + (g / group_sbs) * n + rows[i]);
-      }
+    for (int t = 0; t < 4; ++t) xf[xs][t] = *reinterpret_cast<const u32x4*>(xrow + g * kSuperblock + 32 * t + 8 * q);
+  };
+  auto compute = [&](auto J, auto X) {
+    constexpr int j = decltype(J)::value;
+    constexpr int xs = decltype(X)::value;
+    uint32_t off_lo[kMfmaTiles], off_hi[kMfmaTiles];
+#pragma unroll
+    for (int i = 0; i < kMfmaTiles; ++i) {
+      off_lo[i] = quad_offsets(nd[j][i], sg[j][i], 2 * q);      // blocks 2q + 8t
+      off_hi[i] = quad_offsets(nd[j][i], sg[j][i], 2 * q + 1);  // blocks 2q + 1 + 8t
     }
 #pragma unroll
-    for (int gi = 0; gi < kMfmaWin; ++gi) {
-      if (gi >= wn) break;
-      const int64_t g = g0 + gi;
-      uint32_t off_lo[kMfmaTiles], off_hi[kMfmaTiles];
+    for (int t = 0; t < 4; ++t) {
+      const bf16x8 xv = __builtin_bit_cast(bf16x8, xf[xs][t]);
 #pragma unroll
       for (int i = 0; i < kMfmaTiles; ++i) {
-        off_lo[i] = quad_offsets(nd[gi][i], sg[gi][i], 2 * q);      // blocks 2q + 8t
-        off_hi[i] = quad_offsets(nd[gi][i], sg[gi][i], 2 * q + 1);  // blocks 2q + 1 + 8t
+        const uint32_t e0 = *reinterpret_cast<const uint32_t*>(dt + __builtin_amdgcn_ubfe(off_lo[i], 8 * t, 8));
+        const uint32_t e1 = *reinterpret_cast<const uint32_t*>(dt + __builtin_amdgcn_ubfe(off_hi[i], 8 * t, 8));
+        u32x4 wv;
+        wv[0] = __builtin_amdgcn_perm(0u, e0, 0x010C000Cu);
+        wv[1] = __builtin_amdgcn_perm(0u, e0, 0x030C020Cu);
+        wv[2] = __builtin_amdgcn_perm(0u, e1, 0x010C000Cu);
+        wv[3] = __builtin_amdgcn_perm(0u, e1, 0x030C020Cu);
+        if constexpr (kGroup) {
+          accg[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xv, __builtin_bit_cast(bf16x8, wv), accg[i], 0, 0, 0);
+        } else {
+          acc[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xv, __builtin_bit_cast(bf16x8, wv), acc[i], 0, 0, 0);
+        }
       }
-#pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        const u32x4 xv = *reinterpret_cast<const u32x4*>(xrow + g * kSuperblock + 32 * t + 8 * q);
+    }
+    if constexpr (kGroup) {
+      if (++gpos == group_sbs) {
 #pragma unroll
         for (int i = 0; i < kMfmaTiles; ++i) {
-          const uint32_t e0 = *reinterpret_cast<const uint32_t*>(dt + __builtin_amdgcn_ubfe(off_lo[i], 8 * t, 8));
-          const uint32_t e1 = *reinterpret_cast<const uint32_t*>(dt + __builtin_amdgcn_ubfe(off_hi[i], 8 * t, 8));
-          u32x4 wv;
-          wv[0] = __builtin_amdgcn_perm(0u, e0, 0x010C000Cu);
-          wv[1] = __builtin_amdgcn_perm(0u, e0, 0x030C020Cu);
-          wv[2] = __builtin_amdgcn_perm(0u, e1, 0x010C000Cu);
-          wv[3] = __builtin_amdgcn_perm(0u, e1, 0x030C020Cu);
-          if constexpr (kGroup) {
-            accg[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, xv),
-                                                             __builtin_bit_cast(bf16x8, wv), accg[i], 0, 0, 0);
-          } else {
-            acc[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, xv),
-                                                            __builtin_bit_cast(bf16x8, wv), acc[i], 0, 0, 0);
-          }
-        }
-      }
-      if constexpr (kGroup) {
-        if (++gpos == group_sbs) {
+          const float a2 = 2.f * av[j][i];
 #pragma unroll
-          for (int i = 0; i < kMfmaTiles; ++i) {
-            const float a2 = 2.f * av[gi][i];
-#pragma unroll
-            for (int e = 0; e < 4; ++e) acc[i][e] += a2 * accg[i][e];
-            accg[i] = f32x4{0.f, 0.f, 0.f, 0.f};
-          }
-          gpos = 0;
+          for (int e = 0; e < 4; ++e) acc[i][e] += a2 * accg[i][e];
+          accg[i] = f32x4{0.f, 0.f, 0.f, 0.f};
         }
+        gpos = 0;
       }
     }
+  };
+  // one superblock: prefetch, then compute slot J with activations X
+  auto step = [&](auto J, auto X, int64_t g) {
+    constexpr int j = decltype(J)::value;
+    constexpr int xs = decltype(X)::value;
+    fetch(RingSlot<(j + kMfmaDepth - 1) % kMfmaDepth>{}, g + kMfmaDepth - 1);
+    fetch_x(RingSlot<1 - xs>{}, g + 1);
+    compute(J, X);
+  };
+
+  static_assert(kMfmaDepth == 4, "the loop below is unrolled by the ring depth");
+  fetch(RingSlot<0>{}, sb_begin);
+  fetch(RingSlot<1>{}, sb_begin + 1);
+  fetch(RingSlot<2>{}, sb_begin + 2);
+  fetch_x(RingSlot<0>{}, sb_begin);
+  // (every early exit leaves the loop, so each path into a step passes
+  // through the step before it and the compiler's waits stay exact)
+  for (int64_t g = sb_begin;; g += 4) {
+    step(RingSlot<0>{}, RingSlot<0>{}, g);
+    if (g + 1 >= sb_end) break;
+    step(RingSlot<1>{}, RingSlot<1>{}, g + 1);
+    if (g + 2 >= sb_end) break;
+    step(RingSlot<2>{}, RingSlot<0>{}, g + 2);
+    if (g + 3 >= sb_end) break;
+    step(RingSlot<3>{}, RingSlot<1>{}, g + 3);
+    if (g + 4 >= sb_end) break;
   }
 
   // lane holds D[batch 4q + e][row r] of each tile
@@ -523,7 +557,7 @@ GemvPlan plan_gemv(int64_t n, int64_t k, int gran, int group_size, int batch, in
     rows_per_wg = (int64_t)kLutThreads * p.rows_per_thread;
   } else {
     p.rows_per_thread = 1;
-    rows_per_wg = 256;
+    rows_per_wg = 64 * kMfmaTiles;
   }
   p.panels = (n + rows_per_wg - 1) / rows_per_wg;
   // Split K (in whole groups) until the launch has ~2048 workgroups (batch 1;

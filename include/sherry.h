@@ -91,7 +91,8 @@ typedef enum {
   SHERRY_OP_QUANTIZE_PACK = 0,
   SHERRY_OP_UNPACK = 1,
   SHERRY_OP_GEMV = 2,
-  SHERRY_OP_GEMM = 3
+  SHERRY_OP_GEMM = 3,
+  SHERRY_OP_FAKE_QUANT = 4
 } sherry_op;
 
 /* Library ABI version (SHERRY_ABI_VERSION of the build). */
@@ -193,6 +194,29 @@ int32_t sherry_gemv(int64_t n, int64_t k, int32_t granularity, int32_t group_siz
 int32_t sherry_gemm(int64_t n, int64_t k, int32_t granularity, int32_t group_size,
                     const void* packed, const float* alpha, const void* x, int64_t m,
                     void* y, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * sherry_fake_quant -- the quantize -> dequantize forward used in
+ * quantization-aware training: out = T * alpha, dense, from the latent weight
+ * ("Sherry, Tequila and Fairies in Python", section 1.1: SherryNMQuant.forward
+ * returns the ternary signs times the scale, and its backward passes the
+ * gradient through unchanged, the straight-through estimator; the identity
+ * backward needs no kernel and lives in the Python binding).
+ *
+ *   w        [N, K] latent weight, row-major, SHERRY_F32 or SHERRY_BF16.
+ *   out      [N, K] row-major, out_dtype SHERRY_F32 (exact T*alpha) or
+ *            SHERRY_BF16 (T*alpha rounded to nearest even).  May not alias w.
+ *   alpha    out, sherry_num_scales(...) fp32, the same scales (and layout)
+ *            sherry_quantize_pack writes.
+ *   Codes and scales are those of sherry_quantize_pack, bit for bit.
+ *   workspace: sherry_workspace_bytes(SHERRY_OP_FAKE_QUANT, ...) bytes: 0 for
+ *            per_group with G == 128 (one fused kernel); otherwise room for
+ *            the packed planes plus the quantize workspace (quantize + pack,
+ *            then a dense decode).
+ */
+int32_t sherry_fake_quant(int64_t n, int64_t k, int32_t granularity, int32_t group_size,
+                          const void* w, int32_t w_dtype, void* out, int32_t out_dtype, float* alpha,
+                          void* workspace, size_t workspace_bytes, void* stream);
 
 #ifdef __cplusplus
 }

@@ -65,7 +65,7 @@ __all__ = [
     "encode_block", "decode_code", "encode", "decode_codes",
     "pack", "unpack", "packed_bytes",
     "pairwise_sum_f32", "alpha", "alpha_per_weight", "dequant",
-    "quantize_pack", "gemv", "gemm", "tolerance_bound", "bf16_half_ulp", "round_to_bf16_bits",
+    "quantize_pack", "fake_quant", "gemv", "gemm", "tolerance_bound", "bf16_half_ulp", "round_to_bf16_bits",
     "bf16_bits_to_f32",
 ]
 
@@ -341,6 +341,17 @@ def quantize_pack(w: np.ndarray, granularity: str = "per_group",
     w = np.asarray(w, dtype=np.float32)
     validate(w.shape, granularity, group_size)
     return pack(encode(w)), alpha(w, granularity, group_size)
+
+
+def fake_quant(w: np.ndarray, granularity: str = "per_group",
+               group_size: int = 128):
+    """Quantization-aware training forward: (T * alpha in fp64, alpha)
+    [P1 1.1 SherryNMQuant.forward returns ``signed*scale``].  Its backward is
+    the identity (straight-through), which has no arithmetic to check."""
+    w = np.asarray(w, dtype=np.float32)
+    validate(w.shape, granularity, group_size)
+    a = alpha(w, granularity, group_size)
+    return dequant(ternary(w), a, granularity, group_size), a
 
 
 # --------------------------------------------------------------------------

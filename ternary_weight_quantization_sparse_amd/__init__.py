@@ -20,7 +20,7 @@ from ._lib import SherryError, check, load  # noqa: F401
 
 __all__ = [
     "PackedWeight", "quantize_pack", "unpack", "gemv", "gemm", "packed_bytes", "num_scales",
-    "workspace_bytes", "SherryError", "load",
+    "workspace_bytes", "SherryError", "load", "fake_quant", "fake_quant_ste", "gemv_batched",
 ]
 
 
@@ -104,6 +104,68 @@ def quantize_pack(w, granularity: str = "per_group", group_size: int = 128, stre
     check(lib.sherry_quantize_pack(n, k, gran, group_size, _ptr(w), dtype, _ptr(packed), _ptr(alpha),
                                    _ptr(ws), 0 if ws is None else ws.numel(), _stream(stream)))
     return PackedWeight(packed[:nbytes], alpha[:nsc], n, k, granularity, group_size)
+
+
+def fake_quant(w, granularity: str = "per_group", group_size: int = 128, out_dtype=None, stream=None):
+    """Quantize -> dequantize forward of a latent weight ``w`` [N, K] (fp32 or
+    bf16, CUDA): returns (T*alpha dense [N, K], alpha).  ``out_dtype`` defaults
+    to w's dtype (fp32 exact, bf16 rounded to nearest even)."""
+    torch = _torch()
+    if w.dim() != 2:
+        raise ValueError("Sherry quantization expects a 2-D weight")
+    n, k = w.shape
+    gran = _gran(granularity)
+    dtype = {torch.float32: _lib.F32, torch.bfloat16: _lib.BF16}.get(w.dtype)
+    if dtype is None:
+        raise ValueError("w must be float32 or bfloat16")
+    odt = w.dtype if out_dtype is None else out_dtype
+    ocode = {torch.float32: _lib.F32, torch.bfloat16: _lib.BF16}.get(odt)
+    if ocode is None:
+        raise ValueError("out_dtype must be float32 or bfloat16")
+    w = w.contiguous()
+    lib = load()
+    nsc = int(lib.sherry_num_scales(n, k, gran, group_size))
+    out = torch.empty((n, k), dtype=odt, device=w.device)
+    alpha = torch.empty(max(nsc, 1), dtype=torch.float32, device=w.device)
+    ws_bytes = int(lib.sherry_workspace_bytes(_lib.OP_FAKE_QUANT, n, k, gran, group_size, 1, 1))
+    ws = _workspace(ws_bytes if ws_bytes != (1 << 64) - 1 else 0, w.device)
+    check(lib.sherry_fake_quant(n, k, gran, group_size, _ptr(w), dtype, _ptr(out), ocode, _ptr(alpha),
+                                _ptr(ws), 0 if ws is None else ws.numel(), _stream(stream)))
+    return out, alpha[:nsc]
+
+
+def _make_ste():
+    torch = _torch()
+
+    class SherryFakeQuantSTE(torch.autograd.Function):
+        """Forward: T*alpha from the latent weight (one fused kernel for
+        per_group 128).  Backward: the straight-through estimator -- the
+        gradient of the dequantized weight is passed to the latent weight
+        unchanged ("Sherry, Tequila and Fairies in Python", section 1.1,
+        SherryNMQuant.backward)."""
+
+        @staticmethod
+        def forward(ctx, w, granularity="per_group", group_size=128):
+            out, _ = fake_quant(w, granularity, group_size)
+            return out
+
+        @staticmethod
+        def backward(ctx, grad_out):
+            return grad_out, None, None
+
+    return SherryFakeQuantSTE
+
+
+_STE = None
+
+
+def fake_quant_ste(w, granularity: str = "per_group", group_size: int = 128):
+    """Differentiable fake quantization for quantization-aware training:
+    forward T*alpha, backward identity (straight-through)."""
+    global _STE
+    if _STE is None:
+        _STE = _make_ste()
+    return _STE.apply(w, granularity, group_size)
 
 
 def unpack(pw: PackedWeight, out_dtype="int8", stream=None):

@@ -70,10 +70,14 @@ __device__ inline uint32_t quantize_block(const float v[4], float& kept_sum) {
   return (s << 4) | (z << 2) | (p1 << 1) | p0;
 }
 
-template <bool BF16>
+// DENSE = 0: write the packed planes (and the scale or the superblock sum).
+// DENSE = SHERRY_F32 + 1 / SHERRY_BF16 + 1 (per_group G = 128 only): the
+// fused fake-quant forward -- write T * alpha densely in fp32 (exact) or bf16
+// (round to nearest even) and the scales, no planes.
+template <bool BF16, int DENSE = 0>
 __global__ __launch_bounds__(256) void quantize_pack_kernel(
     const void* __restrict__ w, int64_t n, int64_t k, uint8_t* __restrict__ packed,
-    float* __restrict__ alpha_direct, float* __restrict__ sb_sums) {
+    float* __restrict__ alpha_direct, float* __restrict__ sb_sums, void* __restrict__ dense = nullptr) {
   const int64_t nsb = k / kSuperblock;
   const int64_t g = blockIdx.y;
   const int64_t row0 = (int64_t)blockIdx.x * kRowsPerTile;
@@ -121,6 +125,27 @@ __global__ __launch_bounds__(256) void quantize_pack_kernel(
     sum += __shfl_xor(sum, 8);
     sum += __shfl_xor(sum, 16);
 
+    if constexpr (DENSE != 0) {
+      // every lane holds the superblock's sum after the butterfly
+      const float a = (float)((double)sum / 96.0);
+      if (row < n) {
+        if (j == 3) alpha_direct[g * n + row] = a;
+        const uint32_t z = (code >> 2) & 3u;
+        float f[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) f[i] = (uint32_t)i == z ? 0.f : (blk[it].v[i] > 0.f ? a : -a);
+        if constexpr (DENSE == SHERRY_F32 + 1) {
+          *reinterpret_cast<float4*>(reinterpret_cast<float*>(dense) + row * k + col) =
+              make_float4(f[0], f[1], f[2], f[3]);
+        } else {
+          uint2 v;
+          v.x = (uint32_t)f32_to_bf16_rne(f[0]) | ((uint32_t)f32_to_bf16_rne(f[1]) << 16);
+          v.y = (uint32_t)f32_to_bf16_rne(f[2]) | ((uint32_t)f32_to_bf16_rne(f[3]) << 16);
+          *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(dense) + row * k + col) = v;
+        }
+      }
+      continue;
+    }
     if (row < n) {
       const int64_t rec = g * n + row;  // (superblock, row) record index
       if (j < 8 && (j & 1) == 0) nib_plane[rec * 4 + (j >> 1)] = nib;
@@ -320,6 +345,42 @@ hipError_t launch_quantize_pack(const QuantizePlan& p, int64_t n, int64_t k, int
     }
   }
   return hipGetLastError();
+}
+
+FakeQuantPlan plan_fake_quant(int64_t n, int64_t k, int gran, int group_size) {
+  FakeQuantPlan p{};
+  p.fused = gran == SHERRY_PER_GROUP && group_size == kSuperblock;
+  if (p.fused) return p;
+  p.packed_offset = 0;
+  p.quant_ws_offset = ((size_t)(n * k / 32 * 5) + 255) / 256 * 256;
+  p.workspace_bytes = p.quant_ws_offset + plan_quantize(n, k, gran, group_size).workspace_bytes;
+  return p;
+}
+
+hipError_t launch_fake_quant(const FakeQuantPlan& p, int64_t n, int64_t k, int gran, int group_size,
+                             const void* w, bool w_bf16, void* out, int out_dtype, float* alpha,
+                             uint8_t* ws, hipStream_t s) {
+  if (p.fused) {
+    const int64_t nsb = k / kSuperblock;
+    dim3 grid((unsigned)((n + kRowsPerTile - 1) / kRowsPerTile), (unsigned)nsb);
+#define SHERRY_FQ(B, D) \
+  hipLaunchKernelGGL((quantize_pack_kernel<B, D>), grid, dim3(256), 0, s, w, n, k, nullptr, alpha, nullptr, out)
+    if (w_bf16) {
+      if (out_dtype == SHERRY_F32) SHERRY_FQ(true, SHERRY_F32 + 1); else SHERRY_FQ(true, SHERRY_BF16 + 1);
+    } else {
+      if (out_dtype == SHERRY_F32) SHERRY_FQ(false, SHERRY_F32 + 1); else SHERRY_FQ(false, SHERRY_BF16 + 1);
+    }
+#undef SHERRY_FQ
+    return hipGetLastError();
+  }
+  // other granularities: the scale needs sums beyond one superblock, so
+  // quantize + pack into the workspace, then decode densely
+  uint8_t* packed = ws + p.packed_offset;
+  const QuantizePlan qp = plan_quantize(n, k, gran, group_size);
+  hipError_t e = launch_quantize_pack(qp, n, k, gran, group_size, w, w_bf16, packed, alpha,
+                                      reinterpret_cast<float*>(ws + p.quant_ws_offset), s);
+  if (e != hipSuccess) return e;
+  return launch_unpack(n, k, gran, group_size, packed, alpha, out, out_dtype, s);
 }
 
 }  // namespace sherry

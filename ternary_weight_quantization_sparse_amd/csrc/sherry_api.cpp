@@ -91,6 +91,8 @@ size_t sherry_workspace_bytes(int32_t op, int64_t n, int64_t k, int32_t granular
     case SHERRY_OP_GEMM:
       if (batch_or_m < 1) return (size_t)-1;
       return plan_gemm(n, k, granularity, group_size, batch_or_m).workspace_bytes;
+    case SHERRY_OP_FAKE_QUANT:
+      return plan_fake_quant(n, k, granularity, group_size).workspace_bytes;
     default:
       return (size_t)-1;
   }
@@ -172,6 +174,24 @@ int32_t sherry_gemm(int64_t n, int64_t k, int32_t granularity, int32_t group_siz
   return hip_status(launch_gemm(plan, n, k, granularity, group_size, static_cast<const uint8_t*>(packed), alpha,
                                 static_cast<const uint16_t*>(x), m, static_cast<uint16_t*>(y),
                                 static_cast<float*>(workspace), static_cast<hipStream_t>(stream)));
+}
+
+int32_t sherry_fake_quant(int64_t n, int64_t k, int32_t granularity, int32_t group_size,
+                          const void* w, int32_t w_dtype, void* out, int32_t out_dtype, float* alpha,
+                          void* workspace, size_t workspace_bytes, void* stream) {
+  int st = check_shape(n, k, granularity, group_size);
+  if (st != SHERRY_OK) return st;
+  if (w_dtype != SHERRY_F32 && w_dtype != SHERRY_BF16) return SHERRY_ERR_DTYPE;
+  if (out_dtype != SHERRY_F32 && out_dtype != SHERRY_BF16) return SHERRY_ERR_DTYPE;
+  if (!w || !out || !alpha) return SHERRY_ERR_NULL;
+  if (!aligned16(w) || !aligned16(out) || !aligned16(alpha)) return SHERRY_ERR_ALIGN;
+  const FakeQuantPlan plan = plan_fake_quant(n, k, granularity, group_size);
+  if (plan.workspace_bytes > 0 && (!workspace || workspace_bytes < plan.workspace_bytes))
+    return SHERRY_ERR_WORKSPACE;
+  if (plan.workspace_bytes > 0 && !aligned16(workspace)) return SHERRY_ERR_ALIGN;
+  return hip_status(launch_fake_quant(plan, n, k, granularity, group_size, w, w_dtype == SHERRY_BF16, out,
+                                      out_dtype, alpha, static_cast<uint8_t*>(workspace),
+                                      static_cast<hipStream_t>(stream)));
 }
 
 }  // extern "C"

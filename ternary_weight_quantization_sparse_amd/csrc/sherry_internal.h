@@ -30,6 +30,18 @@ hipError_t launch_quantize_pack(const QuantizePlan& p, int64_t n, int64_t k, int
                                 int group_size, const void* w, bool w_bf16, uint8_t* packed,
                                 float* alpha, float* ws, hipStream_t s);
 
+// ---------------------------------------------------------------- fake quant
+struct FakeQuantPlan {
+  bool fused;              // per_group G = 128: one kernel writes T*alpha and the scales
+  size_t packed_offset;    // otherwise: packed planes, then the quantize workspace
+  size_t quant_ws_offset;
+  size_t workspace_bytes;
+};
+FakeQuantPlan plan_fake_quant(int64_t n, int64_t k, int gran, int group_size);
+hipError_t launch_fake_quant(const FakeQuantPlan& p, int64_t n, int64_t k, int gran, int group_size,
+                             const void* w, bool w_bf16, void* out, int out_dtype, float* alpha,
+                             uint8_t* ws, hipStream_t s);
+
 // ---------------------------------------------------------------- unpack
 hipError_t launch_unpack(int64_t n, int64_t k, int gran, int group_size, const uint8_t* packed,
                          const float* alpha, void* out, int out_dtype, hipStream_t s);

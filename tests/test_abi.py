@@ -35,7 +35,7 @@ def _declared_symbols():
 
 def test_exports_every_declared_symbol(lib):
     declared = _declared_symbols()
-    assert len(declared) == 9
+    assert len(declared) == 10
     assert set(declared) == set(L.SYMBOLS)
     for name in declared:
         assert hasattr(lib, name), name
@@ -153,6 +153,30 @@ def test_gemm_workspace_rejected_when_needed(lib):
                            None) == L.ERR_WORKSPACE
     assert lib.sherry_gemm(512, 2048, L.PER_GROUP, 128, FAKE, FAKE2, FAKE, 128, FAKE2, MIS, need,
                            None) == L.ERR_ALIGN
+
+
+def fq(lib, n=64, k=512, gran=L.PER_GROUP, g=128, w=FAKE, wdt=L.F32, out=FAKE2, odt=L.BF16, alpha=FAKE,
+       ws=None, wsb=0):
+    return lib.sherry_fake_quant(n, k, gran, g, w, wdt, out, odt, alpha, ws, wsb, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(k=2), L.ERR_SHAPE), (dict(gran=9), L.ERR_GRANULARITY), (dict(g=1000), L.ERR_GROUP),
+    (dict(wdt=L.I8), L.ERR_DTYPE), (dict(odt=L.I8), L.ERR_DTYPE), (dict(odt=7), L.ERR_DTYPE),
+    (dict(w=None), L.ERR_NULL), (dict(out=None), L.ERR_NULL), (dict(alpha=None), L.ERR_NULL),
+    (dict(out=MIS), L.ERR_ALIGN), (dict(k=516, gran=L.PER_TENSOR), L.ERR_UNSUPPORTED),
+    (dict(gran=L.PER_CHANNEL), L.ERR_WORKSPACE), (dict(g=256), L.ERR_WORKSPACE),
+])
+def test_fake_quant_rejects(lib, kw, code):
+    assert fq(lib, **kw) == code
+
+
+def test_fake_quant_workspace_sizes(lib):
+    # per_group 128 is one fused kernel; the rest pack into the workspace first
+    assert lib.sherry_workspace_bytes(L.OP_FAKE_QUANT, 64, 512, L.PER_GROUP, 128, 1, 1) == 0
+    need = lib.sherry_workspace_bytes(L.OP_FAKE_QUANT, 64, 512, L.PER_CHANNEL, 128, 1, 1)
+    assert need >= 64 * 512 * 5 // 32 + 64 * 4 * 4
+    assert fq(lib, gran=L.PER_CHANNEL, ws=FAKE, wsb=need - 4) == L.ERR_WORKSPACE
 
 
 def test_binding_raises_value_error():

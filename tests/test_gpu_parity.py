@@ -389,3 +389,45 @@ def test_quantize_per_tensor_multi_level(n, k):
     """More than 4096 superblock sums: the tree runs over two or three levels."""
     w = WL.latent_weight(n, k, 90 + n)
     check_quantize(dev_f32(w), w, "per_tensor")
+
+
+# ------------------------------------------------------------------ fake quant
+@pytest.mark.parametrize("n,k", [(256, 512), (130, 384), (1, 128)])
+@pytest.mark.parametrize("gran,g", [("per_group", 128), ("per_group", 256), ("per_channel", 128),
+                                    ("per_tensor", 128)])
+@pytest.mark.parametrize("odt", ["float32", "bfloat16"])
+def test_fake_quant_matches_oracle(n, k, gran, g, odt):
+    """Dense T * alpha and the scales, bit for bit: fp32 exactly, bf16 as the
+    nearest-even rounding of the fp32 product."""
+    if k % g:
+        pytest.skip("group does not divide K")
+    w = WL.latent_weight(n, k, 40 + n)
+    out, a = S.fake_quant(dev_f32(w), gran, g, out_dtype=getattr(torch, odt))
+    ref, ref_a = O.fake_quant(w, gran, g)
+    assert np.array_equal(to_np(a).view(np.uint32), ref_a.reshape(-1).view(np.uint32))
+    ref32 = ref.astype(np.float32)
+    if odt == "float32":
+        assert np.array_equal(to_np(out).view(np.uint32), ref32.view(np.uint32))
+    else:
+        assert np.array_equal(to_np(out), O.round_to_bf16_bits(ref32))
+
+
+def test_fake_quant_bf16_outliers_8192():
+    """The 8192x8192 bf16 weight with 1% outliers x10, per_group 128 (the
+    fused kernel), bf16 out; ties at the block minimum occur here."""
+    wb, wv = WL.latent_weight_outliers_bf16(8192, 8192, 5000)
+    print("[fake-quant] 8192x8192 bf16 outliers", flush=True)
+    out, a = S.fake_quant(dev_bf16(wb), "per_group", 128)
+    ref, ref_a = O.fake_quant(wv, "per_group", 128)
+    assert np.array_equal(to_np(a).view(np.uint32), ref_a.reshape(-1).view(np.uint32))
+    assert np.array_equal(to_np(out), O.round_to_bf16_bits(ref.astype(np.float32)))
+
+
+def test_fake_quant_ste_gradient_passes_through():
+    w = dev_f32(WL.latent_weight(64, 256, 44)).requires_grad_(True)
+    gy = torch.randn((64, 256), device=DEV, generator=torch.Generator(device=DEV).manual_seed(45))
+    y = S.fake_quant_ste(w, "per_group", 128)
+    ref, _ = O.fake_quant(w.detach().cpu().numpy(), "per_group", 128)
+    assert np.array_equal(to_np(y.detach()).view(np.uint32), ref.astype(np.float32).view(np.uint32))
+    (y * gy).sum().backward()
+    assert torch.equal(w.grad, gy)

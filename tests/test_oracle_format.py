@@ -216,3 +216,23 @@ def test_validation_accepts_page_rules():
     O.validate((3, 12), "per_channel", 0)
     O.validate((3, 24), "per_group", 12)
     O.validate((3, 24), "per_group", 4)
+
+
+# ---------------------------------------------------------------- fake quant
+def test_hand_blocks_fake_quant():
+    """T * alpha of the hand-worked row, per_tensor (alpha = 38.5 / 27) and
+    per_group G = 12 (three blocks per group, denominator 9, group sums
+    from the hand-worked kept sums)."""
+    rows, (s_tensor, d_tensor) = _read_blocks()
+    w = np.array([r[0] for r in rows], dtype=np.float32).reshape(1, -1)
+    t = np.array([r[2] for r in rows], dtype=np.float64).reshape(1, -1)
+    out, a = O.fake_quant(w, "per_tensor")
+    expect_a = np.float32(s_tensor / d_tensor)
+    assert a.reshape(-1)[0] == expect_a
+    assert np.array_equal(out, t * np.float64(expect_a))
+    ksum = [r[4] for r in rows]
+    out, a = O.fake_quant(w, "per_group", 12)
+    for g in range(3):
+        ag = np.float32(sum(ksum[3 * g:3 * g + 3]) / 9.0)
+        assert a.reshape(-1)[g] == ag
+        assert np.array_equal(out[0, 12 * g:12 * g + 12], t[0, 12 * g:12 * g + 12] * np.float64(ag))

@@ -11,10 +11,14 @@ planes + fp32 scales of every copy, the activations once per launch, and the
 bf16 outputs of every copy.
 
 Also reported, each timed with HIP events on the launch stream:
+  single    single-call GEMV per shape from HIP-graph replays, cold and warm
+  layer     one token through the 1B layer's linears, cold: 7 launches, or 4
+            with q/k/v and gate/up each packed as one weight
   gemm      prefill GEMM on the 1B layer, M = 512 and 2048 (TFLOP/s on 2MNK)
   quantize  Sparse-AbsMean quantize+pack of an 8192x8192 bf16 weight with 1%
             outliers x10, per_tensor / per_channel / per_group-128, rotating 4
-            input copies (GB/s on bytes read + written)
+            input copies (GB/s on bytes read + written); and the fused
+            fake-quant forward (dense bf16 T*alpha) of the same weight
   gemv_3b   the 28-layer LLaMA-3.2-3B linear stack at batch 1, 4, 16 (each
             shape one launch over its 28 layers)
   cpu_baseline  the CPU oracle (NumPy, one thread) on a bounded sample of the
@@ -289,6 +293,73 @@ def bench_gemv_single_call(reps, dev, warm_calls=256, replays=5):
     return out
 
 
+def bench_layer_step(pws, dev, replays=5):
+    """One token through the 1B layer's linears at batch 1, weights cold: a
+    HIP graph of L layer steps, step i on the i-th distinct copy of every
+    weight (L copies of the layer >= 1 GiB).  separate: 7 launches per step;
+    fused: q/k/v and gate/up each packed as one weight (they read the same
+    activations), 4 launches per step.  Context for the multi-matrix decode,
+    not the headline."""
+    import numpy as np
+    import workloads as WL
+    import ternary_weight_quantization_sparse_amd as S
+    torch = _torch()
+    by = {name: (n, k, pw, w) for (name, n, k, pw, w) in pws}
+    layer_bytes = sum(matrix_bytes(n, k) for (n, k, _, _) in by.values())
+    L = -(-GIB // layer_bytes)
+    xs = {k: dev_bf16(WL.activations_bf16(1, k, 200)[0], dev) for k in (2048, 8192)}
+    qkv = S.quantize_pack_fused([dev_f32(by[m][3], dev) for m in ("q", "k", "v")], "per_group", 128)
+    gu = S.quantize_pack_fused([dev_f32(by[m][3], dev) for m in ("gate", "up")], "per_group", 128)
+    plans = {
+        "separate": [(by[m][2], xs[by[m][1]]) for m in ("q", "k", "v", "o", "gate", "up", "down")],
+        "fused": [(qkv.pw, xs[2048]), (by["o"][2], xs[2048]), (gu.pw, xs[2048]), (by["down"][2], xs[8192])],
+    }
+    res = {"layers_per_replay": L, "layer_bytes": layer_bytes}
+    outs = {}
+    for mode, mats in plans.items():
+        calls = []
+        for pw, x in mats:
+            rep = Replicated(pw, L)
+            wsb = S.workspace_bytes(2, pw.n, pw.k, "per_group", 128, 1, 1)
+            ws = torch.empty(max(wsb, 16), dtype=torch.uint8, device=dev) if wsb else None
+            calls.append((rep, x, ws))
+
+        def step(i):
+            for rep, x, ws in calls:
+                S.gemv_batched(rep.packed_all[i], rep.alpha_all[i], rep.n, rep.k, x, 1, rep.ps, rep.as_,
+                               "per_group", 128, "bfloat16", rep.y[i], rep.y_stride, ws)
+
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            step(0)
+        torch.cuda.current_stream().wait_stream(side)
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for i in range(L):
+                step(i)
+        g.replay()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(replays):
+            g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / (replays * L)
+        outs[mode] = torch.cat([rep.y[0, :rep.n].float() for rep, _, _ in calls])
+        res[mode] = {"launches_per_step": len(calls), "us_per_step": us,
+                     "gbs": layer_bytes / (us * 1e-6) / 1e9}
+        del g, calls
+    # same rows in the same order (q k v o gate up down); the fused launches
+    # split K differently, so compare within a few bf16 ulps
+    d = (outs["separate"] - outs["fused"]).abs().max().item()
+    res["max_abs_diff_separate_vs_fused"] = d
+    log(f"[layer-step] separate {res['separate']['us_per_step']:.1f} us, fused "
+        f"{res['fused']['us_per_step']:.1f} us per 1B layer step (cold); max |diff| {d:.3g}")
+    return res
+
+
 def bench_gemm(pws, dev, ms, reps=10):
     import numpy as np
     import oracle as O
@@ -364,6 +435,30 @@ def bench_quantize(dev, reps=10):
         res[gran] = {"bit_exact": ok, "ms": t, "gbs": (rd + wr) / (t * 1e-3) / 1e9,
                      "gweights_per_s": n * k / (t * 1e-3) / 1e9}
         log(f"[quantize] {gran}: bit_exact={ok} {t * 1e3:.1f} us, {res[gran]['gbs']:.0f} GB/s")
+    # quantization-aware-training forward: dense bf16 T*alpha from the same
+    # weight (per_group 128: the fused kernel)
+    out, a = S.fake_quant(w0, "per_group", 128)
+    ref, ref_a = O.fake_quant(vals, "per_group", 128)
+    ok = bool(np.array_equal(to_np(out), O.round_to_bf16_bits(ref.astype(np.float32))) and
+              np.array_equal(to_np(a).view(np.uint32), ref_a.reshape(-1).view(np.uint32)))
+    del ref
+    outs = [torch.empty_like(w0) for _ in range(2)]
+    alpha = torch.empty(S.num_scales(n, k, "per_group", 128), dtype=torch.float32, device=dev)
+    lib = S.load()
+
+    def fq(i=[0]):
+        w, o = copies[i[0] % 4], outs[i[0] % 2]
+        i[0] += 1
+        S.check(lib.sherry_fake_quant(n, k, S._lib.PER_GROUP, 128, w.data_ptr(), S._lib.BF16, o.data_ptr(),
+                                      S._lib.BF16, alpha.data_ptr(), None, 0,
+                                      torch.cuda.current_stream().cuda_stream))
+    total, per, _ = timed_launches([fq], reps, 2)
+    t = float(np.median(per[0]))
+    nbytes = n * k * 2 + n * k * 2 + 4 * alpha.numel()
+    res["fake_quant_per_group_bf16"] = {"bit_exact": ok, "ms": t, "gbs": nbytes / (t * 1e-3) / 1e9,
+                                        "gweights_per_s": n * k / (t * 1e-3) / 1e9}
+    log(f"[fake-quant] per_group bf16->bf16: bit_exact={ok} {t * 1e3:.1f} us, "
+        f"{res['fake_quant_per_group_bf16']['gbs']:.0f} GB/s")
     return res
 
 
@@ -467,8 +562,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=50)
-    ap.add_argument("--sections", default="gemv,single,gemm,quantize,gemv3b,cpu",
-                    help="comma list of: gemv (always), single, gemm, quantize, gemv3b, cpu, "
+    ap.add_argument("--sections", default="gemv,single,layer,gemm,quantize,gemv3b,cpu",
+                    help="comma list of: gemv (always), single, layer, gemm, quantize, gemv3b, cpu, "
                          "copycal (a 1 GiB device copy for scaling HBM counters)")
     args = ap.parse_args()
     if args.gpus != 1:
@@ -487,6 +582,8 @@ def main():
     extra = {}
     if "single" in sections:
         extra["gemv_single_call"] = bench_gemv_single_call(reps, dev)
+    if "layer" in sections:
+        extra["layer_step"] = bench_layer_step(pws, dev)
     if "gemm" in sections:
         extra["gemm"] = bench_gemm(pws, dev, (512, 2048))
     if "quantize" in sections:

@@ -21,6 +21,7 @@ from ._lib import SherryError, check, load  # noqa: F401
 __all__ = [
     "PackedWeight", "quantize_pack", "unpack", "gemv", "gemm", "packed_bytes", "num_scales",
     "workspace_bytes", "SherryError", "load", "fake_quant", "fake_quant_ste", "gemv_batched",
+    "FusedWeight", "quantize_pack_fused", "gemv_fused",
 ]
 
 
@@ -199,6 +200,38 @@ def gemv(pw: PackedWeight, x, y_dtype="bfloat16", stream=None, out=None):
                           _ptr(y), code, 1, 0, 0, 0, _ptr(ws), 0 if ws is None else ws.numel(),
                           _stream(stream)))
     return y
+
+
+@dataclass
+class FusedWeight:
+    """Several linears that read the same activations (q/k/v, gate/up) packed
+    as one weight of their stacked rows, so one GEMV launch -- and one set of
+    activation tables per workgroup -- serves all of them."""
+    pw: PackedWeight
+    sizes: tuple            # rows of each member, in order
+
+
+def quantize_pack_fused(weights, granularity: str = "per_group", group_size: int = 128,
+                        stream=None) -> FusedWeight:
+    """Pack [N_i, K] latent weights as one [sum N_i, K] weight.  The scales of
+    per_group / per_channel are row-local, so every member gets exactly the
+    codes and scales of packing it alone; per_tensor would share one scale
+    across the members (a different model) and is refused."""
+    torch = _torch()
+    if str(granularity) == "per_tensor" or _gran(granularity) == _lib.PER_TENSOR:
+        raise ValueError("fused packing needs row-local scales (per_group or per_channel)")
+    ks = {int(w.shape[1]) for w in weights}
+    if len(ks) != 1:
+        raise ValueError("fused members must share K")
+    w = torch.cat([t.contiguous() for t in weights], dim=0)
+    pw = quantize_pack(w, granularity, group_size, stream)
+    return FusedWeight(pw, tuple(int(t.shape[0]) for t in weights))
+
+
+def gemv_fused(fw: FusedWeight, x, y_dtype="bfloat16", stream=None, out=None):
+    """One launch for all members; returns one [B, N_i] view per member."""
+    y = gemv(fw.pw, x, y_dtype, stream, out)
+    return list(y.split(list(fw.sizes), dim=1))
 
 
 def gemv_batched(packed_all, alpha_all, n: int, k: int, x, count: int, packed_stride: int,

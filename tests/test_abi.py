@@ -179,6 +179,15 @@ def test_fake_quant_workspace_sizes(lib):
     assert fq(lib, gran=L.PER_CHANNEL, ws=FAKE, wsb=need - 4) == L.ERR_WORKSPACE
 
 
+def test_fused_packing_refuses_per_tensor():
+    torch = pytest.importorskip("torch")
+    w = torch.zeros((4, 128))
+    with pytest.raises(ValueError):
+        S.quantize_pack_fused([w, w], "per_tensor")
+    with pytest.raises(ValueError):
+        S.quantize_pack_fused([w, torch.zeros((4, 256))], "per_group")
+
+
 def test_binding_raises_value_error():
     with pytest.raises(ValueError):
         L.check(L.ERR_SHAPE)

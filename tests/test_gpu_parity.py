@@ -431,3 +431,31 @@ def test_fake_quant_ste_gradient_passes_through():
     assert np.array_equal(to_np(y.detach()).view(np.uint32), ref.astype(np.float32).view(np.uint32))
     (y * gy).sum().backward()
     assert torch.equal(w.grad, gy)
+
+
+# ------------------------------------------------------------------ fused members
+@pytest.mark.parametrize("gran", ["per_group", "per_channel"])
+def test_fused_qkv_pack_and_gemv(gran):
+    """q/k/v of the 1B layer packed as one 3072x2048 weight: every member has
+    the codes and scales of packing it alone, and one GEMV launch gives each
+    member's product within tolerance."""
+    members = WL.LLAMA_1B[:3]
+    ws = [WL.latent_weight(n, k, WL.layer_1b_weight_seed(i)) for i, (_, n, k) in enumerate(members)]
+    fw = S.quantize_pack_fused([dev_f32(w) for w in ws], gran, 128)
+    k = members[0][2]
+    t_all = to_np(S.unpack(fw.pw, "int8"))
+    a_all = to_np(fw.pw.alpha)
+    a_all = a_all.reshape(k // 128, -1) if gran == "per_group" else a_all.reshape(1, -1)
+    xb, xv = WL.activations_bf16(1, k, 200)
+    ys = [O.bf16_bits_to_f32(to_np(y)) for y in S.gemv_fused(fw, dev_bf16(xb))]
+    r0 = 0
+    for w, (name, n, _), y in zip(ws, members, ys):
+        t_ref = O.ternary(w)
+        a_ref = O.alpha(w, gran, 128)
+        a_ref = a_ref.reshape(k // 128, n) if gran == "per_group" else a_ref.reshape(1, n)
+        assert np.array_equal(t_all[r0:r0 + n], t_ref), name
+        assert np.array_equal(a_all[:, r0:r0 + n].view(np.uint32), a_ref.view(np.uint32)), name
+        y_ref = O.gemv(xv, O.dequant(t_ref, a_ref, gran, 128))
+        check_close(y, y_ref, O.tolerance_bound(xv, O.alpha_per_weight(a_ref, n, k, gran, 128), y_ref),
+                    f"fused {name}")
+        r0 += n

@@ -14,7 +14,8 @@ Also reported, each timed with HIP events on the launch stream:
   single    single-call GEMV per shape from HIP-graph replays, cold and warm
   layer     one token through the 1B layer's linears, cold: 7 launches, or 4
             with q/k/v and gate/up each packed as one weight
-  gemm      prefill GEMM on the 1B layer, M = 512 and 2048 (TFLOP/s on 2MNK)
+  gemm      prefill GEMM on the 1B layer, M = 512 and 2048 (TFLOP/s on 2MNK),
+            and the Arenas training forward (+ lambda X W^T, 4MNK)
   quantize  Sparse-AbsMean quantize+pack of an 8192x8192 bf16 weight with 1%
             outliers x10, per_tensor / per_channel / per_group-128, rotating 4
             input copies (GB/s on bytes read + written); and the fused
@@ -360,43 +361,76 @@ def bench_layer_step(pws, dev, replays=5):
     return res
 
 
-def bench_gemm(pws, dev, ms, reps=10):
+def bench_gemm(pws, dev, ms, reps=20):
+    """Prefill GEMM on the 1B layer (per_group 128) and the Arenas training
+    forward on the same shapes (the Sherry product plus lambda X W^T over the
+    bf16 latent weight: twice the MFMA work).  Workspaces are allocated once,
+    outside the timed launches."""
     import numpy as np
     import oracle as O
     import workloads as WL
     import ternary_weight_quantization_sparse_amd as S
     torch = _torch()
-    res = {}
+    lib = S.load()
+    stream = lambda: torch.cuda.current_stream().cuda_stream  # noqa: E731
+    lam = S.arenas_lambda(300, 1000, 0.5)
+    wds = {name: dev_bf16(WL.f32_to_bf16_bits(w), dev) for (name, n, k, pw, w) in pws}
+    res = {"arenas_lambda": lam}
     for m in ms:
         xb, xv = WL.activations_bf16(m, 8192, 300 + m)
         xs = {k: dev_bf16(np.ascontiguousarray(xb[:, :k]), dev) for k in (2048, 8192)}
         xvs = {k: xv[:, :k] for k in (2048, 8192)}
         ys = {name: torch.empty((m, n), dtype=torch.bfloat16, device=dev) for (name, n, k, _, _) in pws}
+        wss = {}
+        for (name, n, k, pw, _) in pws:
+            b = S.workspace_bytes(3, n, k, "per_group", 128, m)
+            wss[name] = (torch.empty(max(b, 16), dtype=torch.uint8, device=dev), b)
         rows = np.random.default_rng(m).choice(m, size=min(m, 64), replace=False)
-        checks = []
-        for (name, n, k, pw, w) in pws:
-            y = S.gemm(pw, xs[k], out=ys[name])
-            yv = O.bf16_bits_to_f32(to_np(y))[rows]
-            a = to_np(pw.alpha)
-            wq = O.dequant(O.ternary(w), a, "per_group", 128)
-            y_ref = O.gemm(xvs[k][rows], wq)
-            ok, ratio = within_tol(yv, y_ref,
-                                   O.tolerance_bound(xvs[k][rows], O.alpha_per_weight(a, n, k, "per_group", 128), y_ref))
-            checks.append({"shape": name, "within_tol_sampled_rows": ok, "max_err_over_bound": ratio})
-        launches = [(lambda pw=pw, x=xs[k], y=ys[name]: S.gemm(pw, x, out=y)) for (name, n, k, pw, _) in pws]
-        total, per, _ = timed_launches(launches, reps, 3)
-        flops = [2.0 * m * n * k for (_, n, k, _, _) in pws]
-        times = [float(np.mean(p)) for p in per]
-        tf = sum(flops) / (sum(times) * 1e-3) / 1e12
-        res[str(m)] = {
-            "tflops": tf, "frac_of_bf16_peak": tf / BF16_PEAK_TFLOPS,
-            "tflops_algorithmic_1.5mnk": tf * 0.75,
-            "shapes": [{"shape": name, "ms": t, "tflops": f / (t * 1e-3) / 1e12}
-                       for (name, _, _, _, _), t, f in zip(pws, times, flops)],
-            "checks": checks,
-        }
-        log(f"[gemm] M={m}: {tf:.1f} TFLOP/s ({tf / BF16_PEAK_TFLOPS:.1%} of bf16 peak); "
-            f"all within tol: {all(c['within_tol_sampled_rows'] for c in checks)}")
+
+        def mk(name, n, k, pw, arenas):
+            ws, b = wss[name]
+            if arenas:
+                return lambda: S.check(lib.sherry_arenas_gemm(
+                    n, k, 2, 128, pw.packed.data_ptr(), pw.alpha.data_ptr(), wds[name].data_ptr(), lam,
+                    xs[k].data_ptr(), m, ys[name].data_ptr(), ws.data_ptr(), b, stream()))
+            return lambda: S.check(lib.sherry_gemm(
+                n, k, 2, 128, pw.packed.data_ptr(), pw.alpha.data_ptr(), xs[k].data_ptr(), m,
+                ys[name].data_ptr(), ws.data_ptr(), b, stream()))
+
+        for arenas in (False, True):
+            launches = [mk(name, n, k, pw, arenas) for (name, n, k, pw, _) in pws]
+            checks = []
+            for fn, (name, n, k, pw, w) in zip(launches, pws):
+                fn()
+                yv = O.bf16_bits_to_f32(to_np(ys[name]))[rows]
+                a = to_np(pw.alpha)
+                wq = O.dequant(O.ternary(w), a, "per_group", 128)
+                mag = O.alpha_per_weight(a, n, k, "per_group", 128)
+                if arenas:
+                    wv = WL.bf16_bits_to_f32(WL.f32_to_bf16_bits(w))
+                    y_ref = O.arenas_forward(xvs[k][rows], wq, wv, lam)
+                    mag = mag + np.abs(np.float32(lam) * wv)
+                else:
+                    y_ref = O.gemm(xvs[k][rows], wq)
+                ok, ratio = within_tol(yv, y_ref, O.tolerance_bound(xvs[k][rows], mag, y_ref))
+                checks.append({"shape": name, "within_tol_sampled_rows": ok, "max_err_over_bound": ratio})
+            total, per, _ = timed_launches(launches, reps, 5)
+            flops = [(4.0 if arenas else 2.0) * m * n * k for (_, n, k, _, _) in pws]
+            times = [float(np.median(p)) for p in per]
+            tf = sum(flops) / (sum(times) * 1e-3) / 1e12
+            entry = {
+                "tflops": tf, "frac_of_bf16_peak": tf / BF16_PEAK_TFLOPS,
+                "shapes": [{"shape": name, "ms": t, "tflops": f / (t * 1e-3) / 1e12}
+                           for (name, _, _, _, _), t, f in zip(pws, times, flops)],
+                "checks": checks,
+            }
+            if not arenas:
+                entry["tflops_algorithmic_1.5mnk"] = tf * 0.75
+                res[str(m)] = entry
+            else:
+                res[f"arenas_{m}"] = entry
+            log(f"[{'arenas' if arenas else 'gemm'}] M={m}: {tf:.1f} TFLOP/s ({tf / BF16_PEAK_TFLOPS:.1%} of bf16 "
+                f"peak); all within tol: {all(c['within_tol_sampled_rows'] for c in checks)}")
     return res
 
 

@@ -92,7 +92,8 @@ typedef enum {
   SHERRY_OP_UNPACK = 1,
   SHERRY_OP_GEMV = 2,
   SHERRY_OP_GEMM = 3,
-  SHERRY_OP_FAKE_QUANT = 4
+  SHERRY_OP_FAKE_QUANT = 4,
+  SHERRY_OP_ARENAS_GEMM = 5
 } sherry_op;
 
 /* Library ABI version (SHERRY_ABI_VERSION of the build). */
@@ -217,6 +218,31 @@ int32_t sherry_gemm(int64_t n, int64_t k, int32_t granularity, int32_t group_siz
 int32_t sherry_fake_quant(int64_t n, int64_t k, int32_t granularity, int32_t group_size,
                           const void* w, int32_t w_dtype, void* out, int32_t out_dtype, float* alpha,
                           void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * sherry_arenas_gemm -- the Arenas training forward Y = X (T*alpha)^T +
+ * lambda * X W^T: the Sherry product plus an annealed full-precision residual
+ * over the latent weight W ("Sherry: Hardware-Efficient 1.25-Bit Ternary
+ * Quantization via Fine-grained Sparsification", agihunt digest, the
+ * weight-trapping paragraph: the residual weight lambda_t decays to 0 on a
+ * cosine schedule and is gone at inference).  One kernel runs both products
+ * in the same K loop on bf16 MFMA with fp32 accumulation; the schedule is the
+ * caller's (the Python binding has it).
+ *
+ *   packed, alpha   the quantized weight, as for sherry_gemm.
+ *   w       [N, K] bf16 row-major: the latent weight (round an fp32 master
+ *           weight to bf16 first); (N + 128) * K * 2 must stay below 2^31
+ *           (SHERRY_ERR_UNSUPPORTED otherwise).
+ *   lambda  the residual weight for this step (finite).
+ *   x, m, y, workspace: as for sherry_gemm
+ *           (sherry_workspace_bytes(SHERRY_OP_ARENAS_GEMM, ...)).
+ * Result within 1e-3 * sum_k |X[m,k]| * (alpha(n,k) + |lambda * W[n,k]|) of
+ * the exact value (plus half a bf16 ulp of the output).
+ */
+int32_t sherry_arenas_gemm(int64_t n, int64_t k, int32_t granularity, int32_t group_size,
+                           const void* packed, const float* alpha, const void* w, float lambda,
+                           const void* x, int64_t m, void* y, void* workspace, size_t workspace_bytes,
+                           void* stream);
 
 #ifdef __cplusplus
 }

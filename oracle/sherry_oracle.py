@@ -57,6 +57,8 @@ against values printed on the pages.
 
 from __future__ import annotations
 
+import math
+
 import numpy as np
 
 __all__ = [
@@ -65,7 +67,7 @@ __all__ = [
     "encode_block", "decode_code", "encode", "decode_codes",
     "pack", "unpack", "packed_bytes",
     "pairwise_sum_f32", "alpha", "alpha_per_weight", "dequant",
-    "quantize_pack", "fake_quant", "gemv", "gemm", "tolerance_bound", "bf16_half_ulp", "round_to_bf16_bits",
+    "quantize_pack", "fake_quant", "arenas_lambda", "arenas_forward", "gemv", "gemm", "tolerance_bound", "bf16_half_ulp", "round_to_bf16_bits",
     "bf16_bits_to_f32",
 ]
 
@@ -352,6 +354,24 @@ def fake_quant(w: np.ndarray, granularity: str = "per_group",
     validate(w.shape, granularity, group_size)
     a = alpha(w, granularity, group_size)
     return dequant(ternary(w), a, granularity, group_size), a
+
+
+def arenas_lambda(step: int, total_steps: int, lambda0: float) -> float:
+    """Cosine-annealed residual weight [P2 weight-trapping paragraph: lambda_t
+    decays to 0 on a cosine schedule]: lambda0 * (1 + cos(pi t / T)) / 2 for
+    0 <= t < T, and 0 from T on (the residual is gone at inference)."""
+    if total_steps <= 0 or step >= total_steps:
+        return 0.0
+    return lambda0 * 0.5 * (1.0 + math.cos(math.pi * step / total_steps))
+
+
+def arenas_forward(x: np.ndarray, wq: np.ndarray, w: np.ndarray,
+                   lam: float) -> np.ndarray:
+    """Arenas training forward Y = X (T alpha)^T + lambda X W^T in fp64
+    [P2 weight-trapping paragraph]: ``wq`` the dequantized weight, ``w`` the
+    latent weight as the kernel reads it (bf16 values)."""
+    x = np.asarray(x, dtype=np.float64)
+    return x @ np.asarray(wq, dtype=np.float64).T + float(lam) * (x @ np.asarray(w, dtype=np.float64).T)
 
 
 # --------------------------------------------------------------------------

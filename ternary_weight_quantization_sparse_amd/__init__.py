@@ -21,7 +21,7 @@ from ._lib import SherryError, check, load  # noqa: F401
 __all__ = [
     "PackedWeight", "quantize_pack", "unpack", "gemv", "gemm", "packed_bytes", "num_scales",
     "workspace_bytes", "SherryError", "load", "fake_quant", "fake_quant_ste", "gemv_batched",
-    "FusedWeight", "quantize_pack_fused", "gemv_fused",
+    "FusedWeight", "quantize_pack_fused", "gemv_fused", "arenas_lambda", "arenas_gemm",
 ]
 
 
@@ -199,6 +199,40 @@ def gemv(pw: PackedWeight, x, y_dtype="bfloat16", stream=None, out=None):
     check(lib.sherry_gemv(pw.n, pw.k, gran, pw.group_size, _ptr(pw.packed), _ptr(pw.alpha), _ptr(x), b,
                           _ptr(y), code, 1, 0, 0, 0, _ptr(ws), 0 if ws is None else ws.numel(),
                           _stream(stream)))
+    return y
+
+
+def arenas_lambda(step: int, total_steps: int, lambda0: float) -> float:
+    """Cosine-annealed residual weight of the Arenas forward: lambda0 at step 0,
+    0 at ``total_steps`` and after ("Sherry: Hardware-Efficient 1.25-Bit
+    Ternary Quantization via Fine-grained Sparsification", agihunt digest,
+    weight-trapping paragraph)."""
+    import math
+    if total_steps <= 0 or step >= total_steps:
+        return 0.0
+    return lambda0 * 0.5 * (1.0 + math.cos(math.pi * step / total_steps))
+
+
+def arenas_gemm(pw: PackedWeight, w, lam: float, x, stream=None, out=None):
+    """Arenas training forward Y = X (T*alpha)^T + lam * X W^T for prefill
+    activations ``x`` [M, K] bf16 and the latent weight ``w`` [N, K] (bf16;
+    an fp32 master weight is rounded to bf16 here) -> [M, N] bf16."""
+    torch = _torch()
+    if x.dtype != torch.bfloat16 or x.dim() != 2:
+        raise ValueError("x must be a 2-D bfloat16 tensor")
+    if tuple(w.shape) != (pw.n, pw.k):
+        raise ValueError("w must be [N, K] of the packed weight")
+    wb = w.to(torch.bfloat16).contiguous()
+    x = x.contiguous()
+    m = x.shape[0]
+    y = out if out is not None else torch.empty((m, pw.n), dtype=torch.bfloat16, device=x.device)
+    gran = _gran(pw.granularity)
+    lib = load()
+    ws_bytes = int(lib.sherry_workspace_bytes(_lib.OP_ARENAS_GEMM, pw.n, pw.k, gran, pw.group_size, m, 1))
+    ws = _workspace(ws_bytes if ws_bytes != (1 << 64) - 1 else 0, x.device)
+    check(lib.sherry_arenas_gemm(pw.n, pw.k, gran, pw.group_size, _ptr(pw.packed), _ptr(pw.alpha), _ptr(wb),
+                                 float(lam), _ptr(x), m, _ptr(y), _ptr(ws), 0 if ws is None else ws.numel(),
+                                 _stream(stream)))
     return y
 
 

@@ -85,16 +85,19 @@ __device__ inline uint2 decode_bf16(uint32_t code) {
 
 // TM = MFMA tiles per wave along m: 8 (128-row tiles), or 4 (64-row tiles)
 // for per_group, whose second accumulator set would not fit otherwise.
-template <int GRAN, int TM>
+// AR: the Arenas training forward, which adds lambda * X W^T over the dense
+// bf16 latent weight W in the same K loop.
+template <int GRAN, int TM, bool AR = false>
 struct GemmCfg {
   static constexpr bool kGroup = GRAN == SHERRY_PER_GROUP;
+  static constexpr int kWLoads = AR ? kBN / 8 / kWaves : 0;  // 1 KB dense-weight copies per wave per stage
   static constexpr int kTM = TM;
   static constexpr int kBM = 16 * TM;              // rows of X per tile
   static constexpr int kXLoads = kBM / 8 / kWaves;  // 1 KB activation copies per wave per stage
   static constexpr int kRecWave = kRecAlpha + (kGroup ? 64 * 4 : 0);  // record bytes per wave
   // vector-memory operations per wave per stage: activation pieces, nibble
   // and sign records, and for per_group the scales
-  static constexpr int VM_PER_STAGE = kXLoads + 2 + (kGroup ? 1 : 0);
+  static constexpr int VM_PER_STAGE = kXLoads + 2 + (kGroup ? 1 : 0) + kWLoads;
 };
 
 // s_waitcnt with only a vmcnt limit (expcnt / lgkmcnt left at their maxima).
@@ -125,20 +128,22 @@ using Slot = std::integral_constant<int, J>;
 
 // grid: x = tiles (tiles_m * tiles_n), y = K splits.  partial == nullptr:
 // write bf16 Y; else write fp32 partial[split][m][n] (per_group already
-// scaled, per_channel / per_tensor not yet).
-template <int GRAN, int TM>
-__global__ __launch_bounds__(kThreads, 3) void gemm_kernel(const uint8_t* packed,
+// scaled, per_channel / per_tensor not yet; AR: fully scaled).
+template <int GRAN, int TM, bool AR>
+__global__ __launch_bounds__(kThreads, AR ? 1 : 3) void gemm_kernel(const uint8_t* packed,
                                                      const float* __restrict__ alpha,
                                                      const uint16_t* __restrict__ x,
                                                      uint16_t* __restrict__ y, float* __restrict__ partial,
                                                      int64_t n, int64_t k, int64_t m, int group_sbs,
-                                                     int tiles_m, int tiles_n, int sb_per_split) {
-  using C = GemmCfg<GRAN, TM>;
+                                                     int tiles_m, int tiles_n, int sb_per_split,
+                                                     const uint16_t* __restrict__ wd, float lam) {
+  using C = GemmCfg<GRAN, TM, AR>;
   constexpr int kTM = C::kTM, kBM = C::kBM, kXLoads = C::kXLoads, kRecWave = C::kRecWave;
   // one __shared__ object per ring slot: the compiler's wait insertion then
   // knows an LDS read of one slot never aliases the copies in flight into
-  // another
-  constexpr int kSlot = kBM * kRowBytes + kRecWave * kWaves;  // activation tile, then the records
+  // another.  Slot: activation tile, records, and for AR the dense-weight tile.
+  constexpr int kWOff = kBM * kRowBytes + kRecWave * kWaves;
+  constexpr int kSlot = kWOff + (AR ? kBN * kRowBytes : 0);
   __shared__ __attribute__((aligned(16))) char sl0[kSlot], sl1[kSlot], sl2[kSlot];
   __shared__ __attribute__((aligned(16))) uint2 dtab[32];
 
@@ -146,6 +151,7 @@ __global__ __launch_bounds__(kThreads, 3) void gemm_kernel(const uint8_t* packed
     if constexpr (decltype(J)::value == 0) return sl0; else if constexpr (decltype(J)::value == 1) return sl1; else return sl2;
   };
   auto RC = [&](auto J) -> char* { return XS(J) + kBM * kRowBytes; };
+  auto WT = [&](auto J) -> char* { return XS(J) + kWOff; };
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -183,6 +189,7 @@ __global__ __launch_bounds__(kThreads, 3) void gemm_kernel(const uint8_t* packed
   for (int p = 0; p < 2; ++p)
     xlane[p] = (uint32_t)((lane >> 3) * k * 2) + (uint32_t)(((lane & 7) ^ swz_key(p * 8 + (lane >> 3))) * 16);
   const uint32_t xbytes = (uint32_t)(m * k * 2);
+  const uint32_t wbytes = AR ? (uint32_t)(n * k * 2) : 0u;
 
   // weight row whose records this lane copies: n0 + 32 wave + lane % 32
   // (clamped rows feed only outputs that are not stored)
@@ -209,6 +216,19 @@ __global__ __launch_bounds__(kThreads, 3) void gemm_kernel(const uint8_t* packed
     if constexpr (C::kGroup)
       __builtin_amdgcn_global_load_lds(const_cast<float*>(alpha + (int64_t)((int)sb / group_sbs) * n + crow),
                                        (lds_void*)(rb + kRecAlpha), 4, 0, 0);
+    if constexpr (AR) {
+      // dense-weight tile: rows n0 .. n0+127 of W, copied like X (rows past n
+      // read zeros; the host keeps (n + 128) * k * 2 below 2^31)
+      const __amdgpu_buffer_rsrc_t wr = __builtin_amdgcn_make_buffer_rsrc(
+          const_cast<char*>(reinterpret_cast<const char*>(wd)) + sbyte, (short)0, (int)(wbytes - sbyte), kBufferWord3);
+      char* wb = WT(J);
+#pragma unroll
+      for (int i = 0; i < C::kWLoads; ++i) {
+        const int piece = wave * C::kWLoads + i;
+        const uint32_t voff = xlane[i & 1] + (uint32_t)((n0 + piece * 8) * k * 2);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(wr, (lds_void*)(wb + piece * 1024), 16, voff, 0, 0, 0);
+      }
+    }
   };
 
   // This lane's records of the next stage: nibble dword q and the sign dword
@@ -258,10 +278,17 @@ __global__ __launch_bounds__(kThreads, 3) void gemm_kernel(const uint8_t* packed
 
   f32x4 acc[kTN][kTM];
   f32x4 accg[C::kGroup ? kTN : 1][C::kGroup ? kTM : 1];
+  f32x4 accd[AR ? kTN : 1][AR ? kTM : 1];  // AR: X W^T over the dense weight
 #pragma unroll
   for (int i = 0; i < kTN; ++i)
 #pragma unroll
     for (int jj = 0; jj < kTM; ++jj) acc[i][jj] = f32x4{0.f, 0.f, 0.f, 0.f};
+  if constexpr (AR) {
+#pragma unroll
+    for (int i = 0; i < kTN; ++i)
+#pragma unroll
+      for (int jj = 0; jj < kTM; ++jj) accd[i][jj] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
   int gpos = 0;  // superblocks done in the current group (its first stage zeroes accg)
 
   // One stage: stage st sits in slot J = st % 3.
@@ -296,6 +323,12 @@ __global__ __launch_bounds__(kThreads, 3) void gemm_kernel(const uint8_t* packed
           a[i] = __builtin_bit_cast(bf16x8, u32x4{wl.x, wl.y, wh.x, wh.y});
         }
         const int ch = kk * 4 + q;
+        bf16x8 ad[AR ? kTN : 1];
+        if constexpr (AR) {
+#pragma unroll
+          for (int i = 0; i < kTN; ++i)
+            ad[i] = *reinterpret_cast<const bf16x8*>(WT(J) + swz(wave * kWN + i * 16 + r, ch));
+        }
         bf16x8 bv[kTM];
 #pragma unroll
         for (int jj = 0; jj < kTM; ++jj) bv[jj] = *reinterpret_cast<const bf16x8*>(xb + swz(jj * 16 + r, ch));
@@ -310,6 +343,7 @@ __global__ __launch_bounds__(kThreads, 3) void gemm_kernel(const uint8_t* packed
             } else {
               acc[i][jj] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i], b, acc[i][jj], 0, 0, 0);
             }
+            if constexpr (AR) accd[i][jj] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ad[i], b, accd[i][jj], 0, 0, 0);
           }
         }
       }
@@ -371,35 +405,39 @@ __global__ __launch_bounds__(kThreads, 3) void gemm_kernel(const uint8_t* packed
   for (int i = 0; i < kTN; ++i) {
     const int64_t gn0 = n0 + wave * kWN + i * 16 + 4 * q;
     const bool full4 = gn0 + 3 < n && (n & 3) == 0;
-    if (partial != nullptr) {
-      float* pz = partial + (int64_t)kz * m * n;
-#pragma unroll
-      for (int jj = 0; jj < kTM; ++jj) {
-        const int64_t gm = m0 + jj * 16 + r;
-        if (gm >= m) continue;
-        float* dst = pz + gm * n + gn0;
-        if (full4) {
-          *reinterpret_cast<f32x4*>(dst) = acc[i][jj];
-        } else {
-          for (int e = 0; e < 4; ++e)
-            if (gn0 + e < n) dst[e] = acc[i][jj][e];
-        }
-      }
-      continue;
-    }
+    // scale applied here: per_channel / per_tensor when writing Y, and always
+    // for AR (its partials carry the finished value); per_group is scaled
     float sc[4] = {1.f, 1.f, 1.f, 1.f};
+    if (partial == nullptr || AR) {
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      if constexpr (GRAN == SHERRY_PER_CHANNEL) sc[e] = (gn0 + e < n) ? alpha[gn0 + e] : 0.f;
-      if constexpr (GRAN == SHERRY_PER_TENSOR) sc[e] = alpha[0];
+      for (int e = 0; e < 4; ++e) {
+        if constexpr (GRAN == SHERRY_PER_CHANNEL) sc[e] = (gn0 + e < n) ? alpha[gn0 + e] : 0.f;
+        if constexpr (GRAN == SHERRY_PER_TENSOR) sc[e] = alpha[0];
+      }
     }
 #pragma unroll
     for (int jj = 0; jj < kTM; ++jj) {
       const int64_t gm = m0 + jj * 16 + r;
       if (gm >= m) continue;
+      f32x4 v;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        v[e] = acc[i][jj][e] * sc[e];
+        if constexpr (AR) v[e] += lam * accd[i][jj][e];
+      }
+      if (partial != nullptr) {
+        float* dst = partial + (int64_t)kz * m * n + gm * n + gn0;
+        if (full4) {
+          *reinterpret_cast<f32x4*>(dst) = v;
+        } else {
+          for (int e = 0; e < 4; ++e)
+            if (gn0 + e < n) dst[e] = v[e];
+        }
+        continue;
+      }
       uint16_t h[4];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) h[e] = f32_to_bf16_rne(acc[i][jj][e] * sc[e]);
+      for (int e = 0; e < 4; ++e) h[e] = f32_to_bf16_rne(v[e]);
       uint16_t* dst = y + gm * n + gn0;
       if (full4) {
         *reinterpret_cast<uint2*>(dst) = make_uint2(h[0] | ((uint32_t)h[1] << 16), h[2] | ((uint32_t)h[3] << 16));
@@ -451,10 +489,11 @@ __global__ __launch_bounds__(256) void gemm_split_reduce(const float* __restrict
 // the end, stay below 2^31 bytes.
 int64_t gemm_chunk_rows(int64_t k) { return ((((int64_t)1 << 31) / (2 * k) - kMaxBM) / kMaxBM) * kMaxBM; }
 
-template <int GRAN, int TM>
+template <int GRAN, int TM, bool AR>
 hipError_t launch_g(const GemmPlan& p, int64_t n, int64_t k, int group_sbs, const uint8_t* packed,
-                    const float* alpha, const uint16_t* x, int64_t m, uint16_t* y, float* ws, hipStream_t s) {
-  constexpr int kBM = GemmCfg<GRAN, TM>::kBM;
+                    const float* alpha, const uint16_t* x, int64_t m, uint16_t* y, float* ws,
+                    const uint16_t* wd, float lam, hipStream_t s) {
+  constexpr int kBM = GemmCfg<GRAN, TM, AR>::kBM;
   const int64_t chunk = gemm_chunk_rows(k);
   if (chunk < kMaxBM) return hipErrorInvalidValue;
   const int tiles_n = (int)((n + kBN - 1) / kBN);
@@ -464,16 +503,17 @@ hipError_t launch_g(const GemmPlan& p, int64_t n, int64_t k, int group_sbs, cons
   for (int64_t r0 = 0; r0 < m; r0 += chunk) {
     const int64_t mc = m - r0 < chunk ? m - r0 : chunk;
     const int tiles_m = (int)((mc + kBM - 1) / kBM);
-    hipLaunchKernelGGL((gemm_kernel<GRAN, TM>), dim3((unsigned)(tiles_m * tiles_n), (unsigned)splits), dim3(kThreads), 0,
-                       s, packed, alpha, x + r0 * k, y + r0 * n, splits > 1 ? ws : nullptr, n, k, mc, group_sbs,
-                       tiles_m, tiles_n, sb_per_split);
+    hipLaunchKernelGGL((gemm_kernel<GRAN, TM, AR>), dim3((unsigned)(tiles_m * tiles_n), (unsigned)splits),
+                       dim3(kThreads), 0, s, packed, alpha, x + r0 * k, y + r0 * n, splits > 1 ? ws : nullptr, n, k,
+                       mc, group_sbs, tiles_m, tiles_n, sb_per_split, wd, lam);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     if (splits > 1) {
       const int64_t mn = mc * n;
       const int64_t threads = (mn + 3) / 4;
-      hipLaunchKernelGGL((gemm_split_reduce<GRAN>), dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, s, ws,
-                         alpha, y + r0 * n, mn, n, splits);
+      // AR partials are already scaled: sum them with the scale-free reducer
+      hipLaunchKernelGGL((gemm_split_reduce<AR ? SHERRY_PER_GROUP : GRAN>), dim3((unsigned)((threads + 255) / 256)),
+                         dim3(256), 0, s, ws, alpha, y + r0 * n, mn, n, splits);
       e = hipGetLastError();
       if (e != hipSuccess) return e;
     }
@@ -491,7 +531,7 @@ hipError_t launch_g(const GemmPlan& p, int64_t n, int64_t k, int group_sbs, cons
 GemmPlan plan_gemm(int64_t n, int64_t k, int gran, int group_size, int64_t m) {
   GemmPlan p{};
   p.tile_n = kBN;
-  p.tile_m = GemmCfg<SHERRY_PER_GROUP, kGemmTM>::kBM;
+  p.tile_m = GemmCfg<SHERRY_PER_GROUP, kGemmTM, false>::kBM;
   p.splits = 1;
   const int64_t nsb = k / kSuperblock;
   const int64_t group_sbs = gran == SHERRY_PER_GROUP ? group_size / kSuperblock : 1;
@@ -508,9 +548,22 @@ hipError_t launch_gemm(const GemmPlan& p, int64_t n, int64_t k, int gran, int gr
                        const uint8_t* packed, const float* alpha, const uint16_t* x, int64_t m,
                        uint16_t* y, float* ws, hipStream_t s) {
   const int group_sbs = gran == SHERRY_PER_GROUP ? group_size / kSuperblock : 1;
-  if (gran == SHERRY_PER_GROUP) return launch_g<SHERRY_PER_GROUP, kGemmTM>(p, n, k, group_sbs, packed, alpha, x, m, y, ws, s);
-  if (gran == SHERRY_PER_CHANNEL) return launch_g<SHERRY_PER_CHANNEL, kGemmTM>(p, n, k, group_sbs, packed, alpha, x, m, y, ws, s);
-  return launch_g<SHERRY_PER_TENSOR, kGemmTM>(p, n, k, group_sbs, packed, alpha, x, m, y, ws, s);
+  if (gran == SHERRY_PER_GROUP)
+    return launch_g<SHERRY_PER_GROUP, kGemmTM, false>(p, n, k, group_sbs, packed, alpha, x, m, y, ws, nullptr, 0.f, s);
+  if (gran == SHERRY_PER_CHANNEL)
+    return launch_g<SHERRY_PER_CHANNEL, kGemmTM, false>(p, n, k, group_sbs, packed, alpha, x, m, y, ws, nullptr, 0.f, s);
+  return launch_g<SHERRY_PER_TENSOR, kGemmTM, false>(p, n, k, group_sbs, packed, alpha, x, m, y, ws, nullptr, 0.f, s);
+}
+
+hipError_t launch_arenas_gemm(const GemmPlan& p, int64_t n, int64_t k, int gran, int group_size,
+                              const uint8_t* packed, const float* alpha, const uint16_t* wd, float lam,
+                              const uint16_t* x, int64_t m, uint16_t* y, float* ws, hipStream_t s) {
+  const int group_sbs = gran == SHERRY_PER_GROUP ? group_size / kSuperblock : 1;
+  if (gran == SHERRY_PER_GROUP)
+    return launch_g<SHERRY_PER_GROUP, kGemmTM, true>(p, n, k, group_sbs, packed, alpha, x, m, y, ws, wd, lam, s);
+  if (gran == SHERRY_PER_CHANNEL)
+    return launch_g<SHERRY_PER_CHANNEL, kGemmTM, true>(p, n, k, group_sbs, packed, alpha, x, m, y, ws, wd, lam, s);
+  return launch_g<SHERRY_PER_TENSOR, kGemmTM, true>(p, n, k, group_sbs, packed, alpha, x, m, y, ws, wd, lam, s);
 }
 
 }  // namespace sherry

@@ -93,6 +93,9 @@ size_t sherry_workspace_bytes(int32_t op, int64_t n, int64_t k, int32_t granular
       return plan_gemm(n, k, granularity, group_size, batch_or_m).workspace_bytes;
     case SHERRY_OP_FAKE_QUANT:
       return plan_fake_quant(n, k, granularity, group_size).workspace_bytes;
+    case SHERRY_OP_ARENAS_GEMM:
+      if (batch_or_m < 1) return (size_t)-1;
+      return plan_gemm(n, k, granularity, group_size, batch_or_m).workspace_bytes;
     default:
       return (size_t)-1;
   }
@@ -192,6 +195,27 @@ int32_t sherry_fake_quant(int64_t n, int64_t k, int32_t granularity, int32_t gro
   return hip_status(launch_fake_quant(plan, n, k, granularity, group_size, w, w_dtype == SHERRY_BF16, out,
                                       out_dtype, alpha, static_cast<uint8_t*>(workspace),
                                       static_cast<hipStream_t>(stream)));
+}
+
+int32_t sherry_arenas_gemm(int64_t n, int64_t k, int32_t granularity, int32_t group_size,
+                           const void* packed, const float* alpha, const void* w, float lambda,
+                           const void* x, int64_t m, void* y, void* workspace, size_t workspace_bytes,
+                           void* stream) {
+  int st = check_shape(n, k, granularity, group_size);
+  if (st != SHERRY_OK) return st;
+  if (k > kGemmMaxK || (n + 128) > ((int64_t)1 << 31) / (2 * k)) return SHERRY_ERR_UNSUPPORTED;
+  if (!packed || !alpha || !w || !x || !y) return SHERRY_ERR_NULL;
+  if (!aligned16(packed) || !aligned16(alpha) || !aligned16(w) || !aligned16(x) || !aligned16(y))
+    return SHERRY_ERR_ALIGN;
+  if (m < 1 || m > kMaxElems / k || (m + 127) / 128 > 65535) return SHERRY_ERR_BATCH;
+  const GemmPlan plan = plan_gemm(n, k, granularity, group_size, m);
+  if (plan.workspace_bytes > 0 && (!workspace || workspace_bytes < plan.workspace_bytes))
+    return SHERRY_ERR_WORKSPACE;
+  if (plan.workspace_bytes > 0 && !aligned16(workspace)) return SHERRY_ERR_ALIGN;
+  return hip_status(launch_arenas_gemm(plan, n, k, granularity, group_size, static_cast<const uint8_t*>(packed),
+                                       alpha, static_cast<const uint16_t*>(w), lambda,
+                                       static_cast<const uint16_t*>(x), m, static_cast<uint16_t*>(y),
+                                       static_cast<float*>(workspace), static_cast<hipStream_t>(stream)));
 }
 
 }  // extern "C"

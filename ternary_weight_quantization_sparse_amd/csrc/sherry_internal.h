@@ -71,6 +71,11 @@ GemmPlan plan_gemm(int64_t n, int64_t k, int gran, int group_size, int64_t m);
 hipError_t launch_gemm(const GemmPlan& p, int64_t n, int64_t k, int gran, int group_size,
                        const uint8_t* packed, const float* alpha, const uint16_t* x, int64_t m,
                        uint16_t* y, float* ws, hipStream_t s);
+// Arenas training forward: Y = X (T alpha)^T + lam X W^T, W the dense bf16
+// latent weight [N, K]; same plan and workspace as the GEMM.
+hipError_t launch_arenas_gemm(const GemmPlan& p, int64_t n, int64_t k, int gran, int group_size,
+                              const uint8_t* packed, const float* alpha, const uint16_t* wd, float lam,
+                              const uint16_t* x, int64_t m, uint16_t* y, float* ws, hipStream_t s);
 
 // ---------------------------------------------------------------- device helpers
 // Round an fp32 value to bf16, nearest-even (inputs are finite).

@@ -35,7 +35,7 @@ def _declared_symbols():
 
 def test_exports_every_declared_symbol(lib):
     declared = _declared_symbols()
-    assert len(declared) == 10
+    assert len(declared) == 11
     assert set(declared) == set(L.SYMBOLS)
     for name in declared:
         assert hasattr(lib, name), name
@@ -177,6 +177,22 @@ def test_fake_quant_workspace_sizes(lib):
     need = lib.sherry_workspace_bytes(L.OP_FAKE_QUANT, 64, 512, L.PER_CHANNEL, 128, 1, 1)
     assert need >= 64 * 512 * 5 // 32 + 64 * 4 * 4
     assert fq(lib, gran=L.PER_CHANNEL, ws=FAKE, wsb=need - 4) == L.ERR_WORKSPACE
+
+
+def ar(lib, n=64, k=512, gran=L.PER_GROUP, g=128, packed=FAKE, alpha=FAKE2, w=FAKE, lam=0.5, x=FAKE2, m=32,
+       y=FAKE, ws=None, wsb=0):
+    return lib.sherry_arenas_gemm(n, k, gran, g, packed, alpha, w, lam, x, m, y, ws, wsb, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(k=2), L.ERR_SHAPE), (dict(gran=9), L.ERR_GRANULARITY), (dict(g=1000), L.ERR_GROUP),
+    (dict(w=None), L.ERR_NULL), (dict(x=None), L.ERR_NULL), (dict(w=MIS), L.ERR_ALIGN),
+    (dict(m=0), L.ERR_BATCH), (dict(k=516, gran=L.PER_TENSOR), L.ERR_UNSUPPORTED),
+    (dict(n=1 << 18, k=8192, gran=L.PER_TENSOR), L.ERR_UNSUPPORTED),
+    (dict(n=512, k=2048, m=128), L.ERR_WORKSPACE),
+])
+def test_arenas_gemm_rejects(lib, kw, code):
+    assert ar(lib, **kw) == code
 
 
 def test_fused_packing_refuses_per_tensor():

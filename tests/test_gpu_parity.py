@@ -459,3 +459,35 @@ def test_fused_qkv_pack_and_gemv(gran):
         check_close(y, y_ref, O.tolerance_bound(xv, O.alpha_per_weight(a_ref, n, k, gran, 128), y_ref),
                     f"fused {name}")
         r0 += n
+
+
+# ------------------------------------------------------------------ Arenas
+@pytest.mark.parametrize("n,k,m", [(256, 512, 64), (130, 384, 129), (512, 2048, 128), (2048, 2048, 512)])
+@pytest.mark.parametrize("gran", ["per_group", "per_channel", "per_tensor"])
+def test_arenas_gemm_matches_oracle(n, k, m, gran):
+    """Y = X (T alpha)^T + lambda X W^T with W the bf16 latent weight, lambda
+    from the cosine schedule; several of these shapes split K."""
+    w = WL.latent_weight(n, k, 980 + n)
+    wb = WL.f32_to_bf16_bits(w)
+    pw = S.quantize_pack(dev_f32(w), gran, 128)
+    a = to_np(pw.alpha)
+    lam = S.arenas_lambda(300, 1000, 0.5)
+    assert lam == O.arenas_lambda(300, 1000, 0.5)
+    xb, xv = WL.activations_bf16(m, k, 981 + m)
+    print(f"[arenas] {n}x{k} M={m} {gran} lambda={lam:.4f}", flush=True)
+    y = O.bf16_bits_to_f32(to_np(S.arenas_gemm(pw, dev_bf16(wb), lam, dev_bf16(xb))))
+    wv = WL.bf16_bits_to_f32(wb)
+    y_ref = O.arenas_forward(xv, O.dequant(O.ternary(w), a, gran, 128), wv, lam)
+    mag = O.alpha_per_weight(a, n, k, gran, 128) + np.abs(np.float32(lam) * wv)
+    check_close(y, y_ref, O.tolerance_bound(xv, mag, y_ref), f"arenas {n}x{k} M={m} {gran}")
+
+
+def test_arenas_gemm_lambda_zero_is_the_sherry_product():
+    n, k, m = 300, 1024, 70
+    w = WL.latent_weight(n, k, 990)
+    pw = S.quantize_pack(dev_f32(w))
+    xb, _ = WL.activations_bf16(m, k, 991)
+    x = dev_bf16(xb)
+    y0 = O.bf16_bits_to_f32(to_np(S.arenas_gemm(pw, dev_f32(w), 0.0, x)))
+    y1 = O.bf16_bits_to_f32(to_np(S.gemm(pw, x)))
+    assert np.array_equal(y0, y1)

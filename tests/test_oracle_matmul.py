@@ -5,6 +5,8 @@ read back T[n, k] * alpha exactly, the full pack/unpack path against the
 direct ternary, and the tolerance bound against a bf16-rounded output.
 """
 
+import math
+
 import numpy as np
 import pytest
 
@@ -99,3 +101,36 @@ def test_bf16_half_ulp_bounds_rounding():
     hu = O.bf16_half_ulp(y)
     assert np.all(err <= hu * (1 + 1e-12))
     assert err[-2] == hu[-2]
+
+
+# ---------------------------------------------------------------- Arenas
+def test_arenas_lambda_cosine_values():
+    """Cosine annealing from lambda0 to 0: exact ends, the half-way value, the
+    value at a quarter (which tells a cosine from a linear decay: 1/2 + sqrt(2)/4,
+    not 3/4), the mirror symmetry of the half wave, and monotone decay."""
+    lam0, T = 0.75, 1000
+    assert O.arenas_lambda(0, T, lam0) == lam0
+    assert O.arenas_lambda(T, T, lam0) == 0.0 and O.arenas_lambda(T + 5, T, lam0) == 0.0
+    assert abs(O.arenas_lambda(T // 2, T, lam0) - lam0 / 2) < 1e-15
+    assert abs(O.arenas_lambda(T // 4, T, lam0) - lam0 * (0.5 + math.sqrt(2.0) / 4)) < 1e-15
+    for t in range(0, T + 1, 37):
+        assert abs(O.arenas_lambda(t, T, lam0) + O.arenas_lambda(T - t, T, lam0) - lam0) < 1e-15 or t == 0
+    vals = [O.arenas_lambda(t, T, lam0) for t in range(T + 1)]
+    assert all(a >= b for a, b in zip(vals, vals[1:]))
+
+
+def test_arenas_forward_one_hot_and_zero_lambda():
+    """One-hot activations pick column k of T*alpha + lambda*W exactly; with
+    lambda = 0 the forward is the Sherry product."""
+    rng = np.random.default_rng(3)
+    n, k = 6, 8
+    w = rng.standard_normal((n, k)).astype(np.float32)
+    wq = np.where(rng.random((n, k)) < 0.25, 0.0, np.sign(rng.standard_normal((n, k)))) * 0.125
+    lam = 0.3
+    for c in (0, 5, 7):
+        x = np.zeros((1, k))
+        x[0, c] = 1.0
+        y = O.arenas_forward(x, wq, w, lam)
+        assert np.array_equal(y[0], wq[:, c] + lam * w[:, c].astype(np.float64))
+    x = rng.standard_normal((3, k))
+    assert np.array_equal(O.arenas_forward(x, wq, w, 0.0), O.gemm(x, wq))

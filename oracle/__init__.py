@@ -7,3 +7,4 @@ them.
 """
 
 from .sherry_oracle import *  # noqa: F401,F403
+from .compare_oracle import *  # noqa: F401,F403

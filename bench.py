@@ -14,6 +14,8 @@ Also reported, each timed with HIP events on the launch stream:
   single    single-call GEMV per shape from HIP-graph replays, cold and warm
   layer     one token through the 1B layer's linears, cold: 7 launches, or 4
             with q/k/v and gate/up each packed as one weight
+  compare   the same ternary layer as Sherry 1.25-bit, 3-in-5 (1.67-bit) and
+            padded 2-bit, batch-1 GEMV over cold copies: time per layer pass
   gemm      prefill GEMM on the 1B layer, M = 512 and 2048 (TFLOP/s on 2MNK),
             and the Arenas training forward (+ lambda X W^T, 4MNK)
   quantize  Sparse-AbsMean quantize+pack of an 8192x8192 bf16 weight with 1%
@@ -361,6 +363,78 @@ def bench_layer_step(pws, dev, replays=5):
     return res
 
 
+def bench_compare(pws, dev, steps=40, rounds=3):
+    """The pages' central claim on this GPU: the same ternary 1B layer
+    (per-channel scales) stored as Sherry 1.25-bit, three weights in 5 bits
+    (the 1.67-bit TL2 width) and padded 2-bit, each GEMV'd at batch 1 over
+    >= 1 GiB of cold copies per shape (one launch per shape).  All launches
+    are set up first and warmed together; then the formats' 7-launch passes
+    are timed in turn, `rounds` times, and each format keeps its fastest
+    round (the part's clock ramps over the first tens of milliseconds)."""
+    import numpy as np
+    import oracle as O
+    import workloads as WL
+    import ternary_weight_quantization_sparse_amd as S
+    torch = _torch()
+    xs = {k: dev_bf16(WL.activations_bf16(1, k, 200)[0], dev) for k in (2048, 8192)}
+    formats = [("sherry_1.25", None), ("tl2_1.67", 1), ("padded_2bit", 0)]
+    runs = {f: [] for f, _ in formats}   # per format: (launch, count, bytes)
+    ok = {f: True for f, _ in formats}
+    for (name, n, k, _, w) in pws:
+        pw = S.quantize_pack(dev_f32(w, dev), "per_channel", 128)
+        a = to_np(pw.alpha)
+        xv = O.bf16_bits_to_f32(to_np(xs[k]).reshape(1, k))
+        y_ref = O.gemv(xv, O.dequant(O.ternary(w), a, "per_channel", 128))
+        bound = O.tolerance_bound(xv, O.alpha_per_weight(a, n, k, "per_channel", 128), y_ref)
+        for fname, fmt in formats:
+            if fmt is None:
+                nbytes = S.packed_bytes(n, k)
+                rep = Replicated(pw, max(1, -(-GIB // (nbytes + 4 * n))))
+                count = rep.count
+                launch = (lambda r=rep, x=xs[k]: r.gemv(x))
+                yv = rep.y
+            else:
+                planes = S.compare_repack(pw, fmt)
+                nbytes = planes.numel()
+                count = max(1, -(-GIB // (nbytes + 4 * n)))
+                ps = _round_up(nbytes, 256)
+                allp = torch.empty((count, ps), dtype=torch.uint8, device=dev)
+                allp[:, :nbytes] = planes
+                ast = _round_up(n, 64)
+                alla = torch.empty((count, ast), dtype=torch.float32, device=dev)
+                alla[:, :n] = pw.alpha
+                yv = torch.empty((count, ast), dtype=torch.bfloat16, device=dev)
+                launch = (lambda f=fmt, p_=allp, a_=alla, y_=yv, c=count, ps_=ps, as_=ast, x=xs[k], n_=n, k_=k:
+                          S.compare_gemv(f, p_, a_, n_, k_, x, c, ps_, as_, y_, as_))
+            launch()
+            good, _ = within_tol(O.bf16_bits_to_f32(to_np(yv[0, :n])).reshape(1, n), y_ref, bound)
+            ok[fname] &= good
+            runs[fname].append((launch, count, count * (nbytes + 4 * n + 2 * n) + 2 * k))
+    for _ in range(10):
+        for fname, _ in formats:
+            for launch, _, _ in runs[fname]:
+                launch()
+    torch.cuda.synchronize()
+    best = {}
+    for _ in range(rounds):
+        for fname, _ in formats:
+            _, per, _ = timed_launches([r[0] for r in runs[fname]], steps, 2)
+            us = sum(float(np.median(p)) * 1e3 / c for p, (_, c, _) in zip(per, runs[fname]))
+            best[fname] = min(best.get(fname, us), us)
+    res = {}
+    base = best["sherry_1.25"]
+    for fname, _ in formats:
+        nbytes = sum(b / c for (_, c, b) in runs[fname])
+        us = best[fname]
+        res[fname] = {"us_per_layer": us, "bytes_per_layer": nbytes, "gbs": nbytes / (us * 1e-6) / 1e9,
+                      "within_tol": ok[fname], "time_vs_sherry": us / base}
+        log(f"[compare] {fname}: {us:.2f} us per 1B layer pass, {nbytes / 1e6:.2f} MB, "
+            f"{res[fname]['gbs']:.0f} GB/s, {us / base:.2f}x Sherry's time; tol ok={ok[fname]}")
+    del runs
+    torch.cuda.empty_cache()
+    return res
+
+
 def bench_gemm(pws, dev, ms, reps=20):
     """Prefill GEMM on the 1B layer (per_group 128) and the Arenas training
     forward on the same shapes (the Sherry product plus lambda X W^T over the
@@ -596,8 +670,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=50)
-    ap.add_argument("--sections", default="gemv,single,layer,gemm,quantize,gemv3b,cpu",
-                    help="comma list of: gemv (always), single, layer, gemm, quantize, gemv3b, cpu, "
+    ap.add_argument("--sections", default="gemv,single,layer,compare,gemm,quantize,gemv3b,cpu",
+                    help="comma list of: gemv (always), single, layer, compare, gemm, quantize, gemv3b, cpu, "
                          "copycal (a 1 GiB device copy for scaling HBM counters)")
     args = ap.parse_args()
     if args.gpus != 1:
@@ -618,6 +692,8 @@ def main():
         extra["gemv_single_call"] = bench_gemv_single_call(reps, dev)
     if "layer" in sections:
         extra["layer_step"] = bench_layer_step(pws, dev)
+    if "compare" in sections:
+        extra["compare_formats"] = bench_compare(pws, dev)
     if "gemm" in sections:
         extra["gemm"] = bench_gemm(pws, dev, (512, 2048))
     if "quantize" in sections:

@@ -244,6 +244,50 @@ int32_t sherry_arenas_gemm(int64_t n, int64_t k, int32_t granularity, int32_t gr
                            const void* x, int64_t m, void* y, void* workspace, size_t workspace_bytes,
                            void* stream);
 
+/*
+ * Comparison packings of the same ternary matrix -- the two ways of storing
+ * ternary weights the pages set Sherry's 1.25 bits against ("Sherry:
+ * Hardware-Efficient 1.25-Bit Ternary Quantization via Fine-grained
+ * Sparsification", agihunt digest, problem paragraph: pad every weight to 2
+ * bits, or pack three weights in 5 bits, the 1.67-bit width of the "TL2"
+ * kernels in its results table).  They exist to measure that claim on this
+ * GPU: same T, same per-channel scales, same product.
+ *
+ * Layouts (this library's):
+ *   SHERRY_CMP_2BIT  value 0 / +1 / -1 -> code 0 / 1 / 2, 2 bits per weight.
+ *                    K in superblocks of 128; the 32-byte record of
+ *                    (superblock g, row n) at byte (g*N + n)*32; byte j holds
+ *                    block j's 4 weights, weight i in bits 2i.  N*K/4 bytes.
+ *   SHERRY_CMP_TL2   digits d = v + 1; triple code d0 + 3 d1 + 9 d2 in 5 bits.
+ *                    K in superblocks of 192 (64 triples), zero-padded to a
+ *                    multiple of 192; the 40-byte record of (superblock g,
+ *                    row n) at byte (g*N + n)*40 holds code t in bits
+ *                    [5t, 5t+5).  N*ceil(K/192)*40 bytes.
+ */
+typedef enum { SHERRY_CMP_2BIT = 0, SHERRY_CMP_TL2 = 1 } sherry_compare_format;
+
+/* Bytes of a comparison packing; 0 on invalid arguments (format, N <= 0,
+ * K <= 0 or K % 128 != 0). */
+size_t sherry_compare_bytes(int32_t format, int64_t n, int64_t k);
+
+/* Re-encode Sherry planes (sherry_quantize_pack output, [N, K]) into a
+ * comparison packing: out receives sherry_compare_bytes(format, n, k) bytes. */
+int32_t sherry_compare_repack(int32_t format, int64_t n, int64_t k, const void* packed, void* out,
+                              void* stream);
+
+/* Batch-1 GEMV over a comparison packing with per-channel scales:
+ * y[n] = alpha[n] * sum_k x[k] T[n, k], bf16 out (round to nearest even).
+ *   alpha   [N] fp32 (the per_channel scales of the same T).
+ *   x       [K] bf16.   y  [N] bf16 per matrix.
+ *   count / strides as for sherry_gemv (count matrices, shared x; strides
+ *   ignored when count == 1; planes_stride >= sherry_compare_bytes, a multiple
+ *   of 16; alpha_stride >= N; y_stride >= N).
+ * No split of K: launches with few rows are slow (this is a measuring tool).
+ * Result within 1e-3 * sum_k |x[k] * alpha[n]| of the exact product. */
+int32_t sherry_compare_gemv(int32_t format, int64_t n, int64_t k, const void* planes, const float* alpha,
+                            const void* x, void* y, int32_t count, int64_t planes_stride,
+                            int64_t alpha_stride, int64_t y_stride, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -22,6 +22,7 @@ __all__ = [
     "PackedWeight", "quantize_pack", "unpack", "gemv", "gemm", "packed_bytes", "num_scales",
     "workspace_bytes", "SherryError", "load", "fake_quant", "fake_quant_ste", "gemv_batched",
     "FusedWeight", "quantize_pack_fused", "gemv_fused", "arenas_lambda", "arenas_gemm",
+    "compare_repack", "compare_gemv",
 ]
 
 
@@ -233,6 +234,33 @@ def arenas_gemm(pw: PackedWeight, w, lam: float, x, stream=None, out=None):
     check(lib.sherry_arenas_gemm(pw.n, pw.k, gran, pw.group_size, _ptr(pw.packed), _ptr(pw.alpha), _ptr(wb),
                                  float(lam), _ptr(x), m, _ptr(y), _ptr(ws), 0 if ws is None else ws.numel(),
                                  _stream(stream)))
+    return y
+
+
+def compare_repack(pw: PackedWeight, fmt: int, stream=None):
+    """Re-encode a packed weight as padded 2-bit (fmt 0) or three weights in 5
+    bits (fmt 1): the comparison packings of the same ternary matrix."""
+    torch = _torch()
+    lib = load()
+    nbytes = int(lib.sherry_compare_bytes(fmt, pw.n, pw.k))
+    if nbytes == 0:
+        raise ValueError("invalid comparison format or shape")
+    out = torch.empty(nbytes, dtype=torch.uint8, device=pw.packed.device)
+    check(lib.sherry_compare_repack(fmt, pw.n, pw.k, _ptr(pw.packed), _ptr(out), _stream(stream)))
+    return out
+
+
+def compare_gemv(fmt: int, planes, alpha, n: int, k: int, x, count: int = 1, planes_stride: int = 0,
+                 alpha_stride: int = 0, y=None, y_stride: int = 0, stream=None):
+    """Batch-1 GEMV over a comparison packing with per-channel scales."""
+    torch = _torch()
+    if x.dim() == 2:
+        x = x.reshape(-1)
+    if y is None:
+        y = torch.empty((count, n), dtype=torch.bfloat16, device=x.device)
+        y_stride = n
+    check(load().sherry_compare_gemv(fmt, n, k, _ptr(planes), _ptr(alpha), _ptr(x), _ptr(y), count,
+                                     planes_stride, alpha_stride, y_stride, _stream(stream)))
     return y
 
 

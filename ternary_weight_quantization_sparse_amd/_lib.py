@@ -20,6 +20,7 @@ ERR_ALIGN, ERR_WORKSPACE, ERR_BATCH, ERR_HIP = 7, 8, 9, 10
 # enums
 PER_TENSOR, PER_CHANNEL, PER_GROUP = 0, 1, 2
 GRANULARITY = {"per_tensor": PER_TENSOR, "per_channel": PER_CHANNEL, "per_group": PER_GROUP}
+CMP_2BIT, CMP_TL2 = 0, 1
 F32, BF16, I8 = 0, 1, 2
 OP_QUANTIZE_PACK, OP_UNPACK, OP_GEMV, OP_GEMM, OP_FAKE_QUANT, OP_ARENAS_GEMM = 0, 1, 2, 3, 4, 5
 
@@ -27,7 +28,8 @@ OP_QUANTIZE_PACK, OP_UNPACK, OP_GEMV, OP_GEMM, OP_FAKE_QUANT, OP_ARENAS_GEMM = 0
 SYMBOLS = (
     "sherry_abi_version", "sherry_status_string", "sherry_packed_bytes", "sherry_num_scales",
     "sherry_workspace_bytes", "sherry_quantize_pack", "sherry_unpack", "sherry_gemv", "sherry_gemm",
-    "sherry_fake_quant", "sherry_arenas_gemm",
+    "sherry_fake_quant", "sherry_arenas_gemm", "sherry_compare_bytes", "sherry_compare_repack",
+    "sherry_compare_gemv",
 )
 
 _i32, _i64, _sz, _vp = ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t, ctypes.c_void_p
@@ -46,6 +48,9 @@ _SIGNATURES = {
     "sherry_fake_quant": ([_i64, _i64, _i32, _i32, _vp, _i32, _vp, _i32, _vp, _vp, _sz, _vp], _i32),
     "sherry_arenas_gemm": ([_i64, _i64, _i32, _i32, _vp, _vp, _vp, ctypes.c_float, _vp, _i64, _vp, _vp, _sz, _vp],
                            _i32),
+    "sherry_compare_bytes": ([_i32, _i64, _i64], _sz),
+    "sherry_compare_repack": ([_i32, _i64, _i64, _vp, _vp, _vp], _i32),
+    "sherry_compare_gemv": ([_i32, _i64, _i64, _vp, _vp, _vp, _vp, _i32, _i64, _i64, _i64, _vp], _i32),
 }
 
 _lib = None

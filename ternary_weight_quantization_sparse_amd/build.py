@@ -20,7 +20,7 @@ LIB_NAME = "libsherry.so"
 LIB_PATH = os.path.join(PKG_DIR, LIB_NAME)
 
 ARCH = "gfx950"
-SOURCES = ["sherry_api.cpp", "quantize_pack.hip", "unpack.hip", "gemv.hip", "gemm.hip"]
+SOURCES = ["sherry_api.cpp", "quantize_pack.hip", "unpack.hip", "gemv.hip", "gemm.hip", "compare.hip"]
 
 COMMON = [
     f"--offload-arch={ARCH}", "-O3", "-fPIC", "-std=c++17", "-Wall",

@@ -218,4 +218,43 @@ int32_t sherry_arenas_gemm(int64_t n, int64_t k, int32_t granularity, int32_t gr
                                        static_cast<float*>(workspace), static_cast<hipStream_t>(stream)));
 }
 
+size_t sherry_compare_bytes(int32_t format, int64_t n, int64_t k) {
+  if ((format != SHERRY_CMP_2BIT && format != SHERRY_CMP_TL2) || n <= 0 || k <= 0 || k % kSuperblock != 0 ||
+      n > kMaxElems / k)
+    return 0;
+  return compare_bytes(format, n, k);
+}
+
+int32_t sherry_compare_repack(int32_t format, int64_t n, int64_t k, const void* packed, void* out,
+                              void* stream) {
+  if (format != SHERRY_CMP_2BIT && format != SHERRY_CMP_TL2) return SHERRY_ERR_DTYPE;
+  const int st = check_shape(n, k, SHERRY_PER_CHANNEL, 0);
+  if (st != SHERRY_OK) return st;
+  if (!packed || !out) return SHERRY_ERR_NULL;
+  if (!aligned16(packed) || !aligned16(out)) return SHERRY_ERR_ALIGN;
+  return hip_status(launch_compare_repack(format, n, k, static_cast<const uint8_t*>(packed),
+                                          static_cast<uint8_t*>(out), static_cast<hipStream_t>(stream)));
+}
+
+int32_t sherry_compare_gemv(int32_t format, int64_t n, int64_t k, const void* planes, const float* alpha,
+                            const void* x, void* y, int32_t count, int64_t planes_stride,
+                            int64_t alpha_stride, int64_t y_stride, void* stream) {
+  if (format != SHERRY_CMP_2BIT && format != SHERRY_CMP_TL2) return SHERRY_ERR_DTYPE;
+  const int st = check_shape(n, k, SHERRY_PER_CHANNEL, 0);
+  if (st != SHERRY_OK) return st;
+  if (!planes || !alpha || !x || !y) return SHERRY_ERR_NULL;
+  if (!aligned16(planes) || !aligned16(alpha) || !aligned16(x) || !aligned16(y)) return SHERRY_ERR_ALIGN;
+  if (count < 1 || count > 65535) return SHERRY_ERR_BATCH;
+  if (count == 1) {
+    planes_stride = alpha_stride = y_stride = 0;
+  } else {
+    if (planes_stride < (int64_t)compare_bytes(format, n, k) || alpha_stride < n || y_stride < n)
+      return SHERRY_ERR_BATCH;
+    if (planes_stride % 16 != 0 || alpha_stride % 4 != 0 || y_stride % 8 != 0) return SHERRY_ERR_ALIGN;
+  }
+  return hip_status(launch_compare_gemv(format, n, k, static_cast<const uint8_t*>(planes), alpha,
+                                        static_cast<const uint16_t*>(x), static_cast<uint16_t*>(y), count,
+                                        planes_stride, alpha_stride, y_stride, static_cast<hipStream_t>(stream)));
+}
+
 }  // extern "C"

@@ -42,6 +42,15 @@ hipError_t launch_fake_quant(const FakeQuantPlan& p, int64_t n, int64_t k, int g
                              const void* w, bool w_bf16, void* out, int out_dtype, float* alpha,
                              uint8_t* ws, hipStream_t s);
 
+// ---------------------------------------------------------------- comparison packings
+int64_t compare_k_padded(int fmt, int64_t k);
+size_t compare_bytes(int fmt, int64_t n, int64_t k);
+hipError_t launch_compare_repack(int fmt, int64_t n, int64_t k, const uint8_t* packed, uint8_t* out,
+                                 hipStream_t s);
+hipError_t launch_compare_gemv(int fmt, int64_t n, int64_t k, const uint8_t* planes, const float* alpha,
+                               const uint16_t* x, uint16_t* y, int count, int64_t planes_stride,
+                               int64_t alpha_stride, int64_t y_stride, hipStream_t s);
+
 // ---------------------------------------------------------------- unpack
 hipError_t launch_unpack(int64_t n, int64_t k, int gran, int group_size, const uint8_t* packed,
                          const float* alpha, void* out, int out_dtype, hipStream_t s);
@@ -78,6 +87,35 @@ hipError_t launch_arenas_gemm(const GemmPlan& p, int64_t n, int64_t k, int gran,
                               const uint16_t* x, int64_t m, uint16_t* y, float* ws, hipStream_t s);
 
 // ---------------------------------------------------------------- device helpers
+// Ternary values of a block from its code.  The sign bit gives the sign of
+// the first kept weight; p0 / p1 say whether the second / third kept weight
+// has the opposite sign.  Position z is the zero.
+__device__ inline void decode_block(uint32_t code, int t[4]) {
+  const int z = (code >> 2) & 3;
+  const int neg0 = (code >> 4) & 1;
+  const int neg1 = neg0 ^ (code & 1);
+  const int neg2 = neg0 ^ ((code >> 1) & 1);
+#pragma unroll
+  for (int pos = 0; pos < 4; ++pos) {
+    const int rank = pos - (pos > z ? 1 : 0);  // index among kept positions
+    const int neg = rank == 0 ? neg0 : (rank == 1 ? neg1 : neg2);
+    t[pos] = (pos == z) ? 0 : (neg ? -1 : 1);
+  }
+}
+
+__device__ inline uint32_t load_code(const uint8_t* __restrict__ packed, int64_t n, int64_t k,
+                                     int64_t row, int64_t blk) {
+  const int64_t g = blk >> 5;
+  const int j = (int)(blk & 31);
+  const int64_t rec = g * n + row;
+  const uint32_t* nib_plane = reinterpret_cast<const uint32_t*>(packed);
+  const uint32_t* sign_plane = reinterpret_cast<const uint32_t*>(packed + nibble_plane_bytes(n, k));
+  const uint32_t d = nib_plane[rec * 4 + ((j & 7) >> 1)];
+  const uint32_t nib = (d >> (4 * (j & 1) + 8 * (j >> 3))) & 15u;
+  const uint32_t sgn = (sign_plane[rec] >> j) & 1u;
+  return (sgn << 4) | nib;
+}
+
 // Round an fp32 value to bf16, nearest-even (inputs are finite).
 __device__ inline uint16_t f32_to_bf16_rne(float f) {
   uint32_t u = __float_as_uint(f);

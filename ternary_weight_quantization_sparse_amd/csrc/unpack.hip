@@ -10,35 +10,6 @@
 namespace sherry {
 namespace {
 
-// Ternary values of a block from its code.  The sign bit gives the sign of
-// the first kept weight; p0 / p1 say whether the second / third kept weight
-// has the opposite sign.  Position z is the zero.
-__device__ inline void decode_block(uint32_t code, int t[4]) {
-  const int z = (code >> 2) & 3;
-  const int neg0 = (code >> 4) & 1;
-  const int neg1 = neg0 ^ (code & 1);
-  const int neg2 = neg0 ^ ((code >> 1) & 1);
-#pragma unroll
-  for (int pos = 0; pos < 4; ++pos) {
-    const int rank = pos - (pos > z ? 1 : 0);  // index among kept positions
-    const int neg = rank == 0 ? neg0 : (rank == 1 ? neg1 : neg2);
-    t[pos] = (pos == z) ? 0 : (neg ? -1 : 1);
-  }
-}
-
-__device__ inline uint32_t load_code(const uint8_t* __restrict__ packed, int64_t n, int64_t k,
-                                     int64_t row, int64_t blk) {
-  const int64_t g = blk >> 5;
-  const int j = (int)(blk & 31);
-  const int64_t rec = g * n + row;
-  const uint32_t* nib_plane = reinterpret_cast<const uint32_t*>(packed);
-  const uint32_t* sign_plane = reinterpret_cast<const uint32_t*>(packed + nibble_plane_bytes(n, k));
-  const uint32_t d = nib_plane[rec * 4 + ((j & 7) >> 1)];
-  const uint32_t nib = (d >> (4 * (j & 1) + 8 * (j >> 3))) & 15u;
-  const uint32_t sgn = (sign_plane[rec] >> j) & 1u;
-  return (sgn << 4) | nib;
-}
-
 __device__ inline float scale_of(const float* __restrict__ alpha, int gran, int group_size,
                                  int64_t n, int64_t row, int64_t col) {
   if (gran == SHERRY_PER_TENSOR) return alpha[0];

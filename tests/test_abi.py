@@ -35,7 +35,7 @@ def _declared_symbols():
 
 def test_exports_every_declared_symbol(lib):
     declared = _declared_symbols()
-    assert len(declared) == 11
+    assert len(declared) == 14
     assert set(declared) == set(L.SYMBOLS)
     for name in declared:
         assert hasattr(lib, name), name
@@ -193,6 +193,23 @@ def ar(lib, n=64, k=512, gran=L.PER_GROUP, g=128, packed=FAKE, alpha=FAKE2, w=FA
 ])
 def test_arenas_gemm_rejects(lib, kw, code):
     assert ar(lib, **kw) == code
+
+
+def test_compare_bytes_and_rejections(lib):
+    assert lib.sherry_compare_bytes(L.CMP_2BIT, 3, 256) == 3 * 256 // 4
+    assert lib.sherry_compare_bytes(L.CMP_TL2, 3, 256) == 3 * 2 * 40   # K padded to 384
+    assert lib.sherry_compare_bytes(L.CMP_TL2, 3, 384) == 3 * 2 * 40
+    assert lib.sherry_compare_bytes(2, 3, 256) == 0 and lib.sherry_compare_bytes(0, 3, 100) == 0
+    assert lib.sherry_compare_repack(5, 64, 512, FAKE, FAKE2, None) == L.ERR_DTYPE
+    assert lib.sherry_compare_repack(0, 64, 516, FAKE, FAKE2, None) == L.ERR_UNSUPPORTED
+    assert lib.sherry_compare_repack(0, 64, 512, None, FAKE2, None) == L.ERR_NULL
+    assert lib.sherry_compare_repack(1, 64, 512, FAKE, MIS, None) == L.ERR_ALIGN
+    g = lib.sherry_compare_gemv
+    assert g(3, 64, 512, FAKE, FAKE2, FAKE, FAKE2, 1, 0, 0, 0, None) == L.ERR_DTYPE
+    assert g(0, 64, 512, FAKE, None, FAKE, FAKE2, 1, 0, 0, 0, None) == L.ERR_NULL
+    assert g(0, 64, 512, FAKE, FAKE2, FAKE, FAKE2, 0, 0, 0, 0, None) == L.ERR_BATCH
+    assert g(0, 64, 512, FAKE, FAKE2, FAKE, FAKE2, 2, 64 * 512 // 4 - 16, 64, 64, None) == L.ERR_BATCH
+    assert g(1, 64, 512, FAKE, FAKE2, FAKE, FAKE2, 2, 64 * 3 * 40 + 8, 64, 64, None) == L.ERR_ALIGN
 
 
 def test_fused_packing_refuses_per_tensor():

@@ -491,3 +491,61 @@ def test_arenas_gemm_lambda_zero_is_the_sherry_product():
     y0 = O.bf16_bits_to_f32(to_np(S.arenas_gemm(pw, dev_f32(w), 0.0, x)))
     y1 = O.bf16_bits_to_f32(to_np(S.gemm(pw, x)))
     assert np.array_equal(y0, y1)
+
+
+# ------------------------------------------------------------------ comparison packings
+@pytest.mark.parametrize("n,k", [(256, 512), (130, 384), (300, 2048), (2048, 8192)])
+@pytest.mark.parametrize("fmt", [0, 1])
+def test_compare_repack_and_gemv(n, k, fmt):
+    """Padded 2-bit / three-in-five packings of the Sherry ternary matrix:
+    bytes equal the oracle's encoding, and the per-channel GEMV over them is
+    within tolerance of the oracle product."""
+    w = WL.latent_weight(n, k, 1200 + n)
+    pw = S.quantize_pack(dev_f32(w), "per_channel")
+    planes = S.compare_repack(pw, fmt)
+    t = O.ternary(w)
+    if n * k <= 300 * 2048:
+        ref = O.encode_2bit(t) if fmt == 0 else O.encode_tl2(t)
+        assert np.array_equal(to_np(planes), ref)
+    else:
+        # large shape: the records of sampled rows, each encoded on its own
+        got = to_np(planes)
+        assert got.size == O.compare_bytes(fmt, n, k)
+        rec = 32 if fmt == 0 else 40
+        nsb = O.k_padded(fmt, k) // (128 if fmt == 0 else 192)
+        for r in (0, 7, n // 2, n - 1):
+            one = O.encode_2bit(t[r:r + 1]) if fmt == 0 else O.encode_tl2(t[r:r + 1])
+            for g in range(nsb):
+                assert np.array_equal(got[(g * n + r) * rec:(g * n + r + 1) * rec], one[g * rec:(g + 1) * rec]), (r, g)
+    a = to_np(pw.alpha)
+    xb, xv = WL.activations_bf16(1, k, 1201)
+    print(f"[compare] fmt {fmt} {n}x{k}", flush=True)
+    y = O.bf16_bits_to_f32(to_np(S.compare_gemv(fmt, planes, pw.alpha, n, k, dev_bf16(xb))))
+    wq = O.dequant(t, a, "per_channel", 128)
+    y_ref = O.gemv(xv, wq)
+    check_close(y, y_ref, O.tolerance_bound(xv, O.alpha_per_weight(a, n, k, "per_channel", 128), y_ref),
+                f"compare fmt {fmt} {n}x{k}")
+
+
+@pytest.mark.parametrize("fmt", [0, 1])
+def test_compare_gemv_count_strides(fmt):
+    n, k, count = 300, 1024, 3
+    ws = [WL.latent_weight(n, k, 1300 + c) for c in range(count)]
+    pws = [S.quantize_pack(dev_f32(w), "per_channel") for w in ws]
+    planes = [S.compare_repack(pw, fmt) for pw in pws]
+    nb = planes[0].numel()
+    ps = (nb + 255) // 256 * 256
+    allp = torch.zeros((count, ps), dtype=torch.uint8, device=DEV)
+    alla = torch.zeros((count, 304), dtype=torch.float32, device=DEV)
+    for c in range(count):
+        allp[c, :nb] = planes[c]
+        alla[c, :n] = pws[c].alpha
+    xb, xv = WL.activations_bf16(1, k, 1310)
+    y = torch.empty((count, 304), dtype=torch.bfloat16, device=DEV)
+    S.compare_gemv(fmt, allp, alla, n, k, dev_bf16(xb), count, ps, 304, y, 304)
+    yv = O.bf16_bits_to_f32(to_np(y))
+    for c in range(count):
+        a = to_np(pws[c].alpha)
+        y_ref = O.gemv(xv, O.dequant(O.ternary(ws[c]), a, "per_channel", 128))
+        check_close(yv[c:c + 1, :n], y_ref,
+                    O.tolerance_bound(xv, O.alpha_per_weight(a, n, k, "per_channel", 128), y_ref), f"copy {c}")

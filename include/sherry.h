@@ -63,7 +63,8 @@ typedef enum {
   SHERRY_ERR_DTYPE = 5,       /* a dtype argument not allowed for that operand */
   SHERRY_ERR_UNSUPPORTED = 6, /* legal for the method but not built here:
                                  K % 128 != 0, per_group with G % 128 != 0,
-                                 or a GEMM with K > 2^21 */
+                                 K/128 or N/64 above 65535, or a GEMM with
+                                 K > 2^21 */
   SHERRY_ERR_ALIGN = 7,       /* a device pointer or stride is not 16-byte aligned */
   SHERRY_ERR_WORKSPACE = 8,   /* workspace NULL or smaller than sherry_workspace_bytes */
   SHERRY_ERR_BATCH = 9,       /* batch outside 1..16, m < 1, count < 1, or a

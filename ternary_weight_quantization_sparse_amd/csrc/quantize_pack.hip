@@ -21,6 +21,8 @@ namespace sherry {
 namespace {
 
 constexpr int kRowsPerTile = 64;
+// Grid: x = superblock, y = 64-row tile, so consecutive workgroups read
+// adjacent 128-weight spans of the same rows.
 constexpr int kIters = kRowsPerTile / 8;  // 4 waves x 2 halves = 8 rows per iteration
 
 template <bool BF16>
@@ -79,8 +81,8 @@ __global__ __launch_bounds__(256) void quantize_pack_kernel(
     const void* __restrict__ w, int64_t n, int64_t k, uint8_t* __restrict__ packed,
     float* __restrict__ alpha_direct, float* __restrict__ sb_sums, void* __restrict__ dense = nullptr) {
   const int64_t nsb = k / kSuperblock;
-  const int64_t g = blockIdx.y;
-  const int64_t row0 = (int64_t)blockIdx.x * kRowsPerTile;
+  const int64_t g = blockIdx.x;
+  const int64_t row0 = (int64_t)blockIdx.y * kRowsPerTile;
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int half = lane >> 5;
@@ -303,7 +305,7 @@ hipError_t launch_quantize_pack(const QuantizePlan& p, int64_t n, int64_t k, int
                                 int group_size, const void* w, bool w_bf16, uint8_t* packed,
                                 float* alpha, float* ws, hipStream_t s) {
   const int64_t nsb = k / kSuperblock;
-  dim3 grid((unsigned)((n + kRowsPerTile - 1) / kRowsPerTile), (unsigned)nsb);
+  dim3 grid((unsigned)nsb, (unsigned)((n + kRowsPerTile - 1) / kRowsPerTile));
   float* direct = p.direct_alpha ? alpha : nullptr;
   if (w_bf16) {
     hipLaunchKernelGGL(quantize_pack_kernel<true>, grid, dim3(256), 0, s, w, n, k, packed, direct, ws);
@@ -362,7 +364,7 @@ hipError_t launch_fake_quant(const FakeQuantPlan& p, int64_t n, int64_t k, int g
                              uint8_t* ws, hipStream_t s) {
   if (p.fused) {
     const int64_t nsb = k / kSuperblock;
-    dim3 grid((unsigned)((n + kRowsPerTile - 1) / kRowsPerTile), (unsigned)nsb);
+    dim3 grid((unsigned)nsb, (unsigned)((n + kRowsPerTile - 1) / kRowsPerTile));
 #define SHERRY_FQ(B, D) \
   hipLaunchKernelGGL((quantize_pack_kernel<B, D>), grid, dim3(256), 0, s, w, n, k, nullptr, alpha, nullptr, out)
     if (w_bf16) {

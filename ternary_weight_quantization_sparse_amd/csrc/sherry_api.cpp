@@ -29,7 +29,8 @@ int check_shape(int64_t n, int64_t k, int32_t gran, int32_t group_size) {
     return SHERRY_ERR_GROUP;
   if (k % kSuperblock != 0) return SHERRY_ERR_UNSUPPORTED;
   if (gran == SHERRY_PER_GROUP && group_size % kSuperblock != 0) return SHERRY_ERR_UNSUPPORTED;
-  if (k / kSuperblock > 65535) return SHERRY_ERR_UNSUPPORTED;  // grid dimension limit
+  if (k / kSuperblock > 65535) return SHERRY_ERR_UNSUPPORTED;  // grid dimension limits:
+  if ((n + 63) / 64 > 65535) return SHERRY_ERR_UNSUPPORTED;      // superblocks and 64-row tiles
   return SHERRY_OK;
 }
 

@@ -143,6 +143,13 @@ def test_gemm_rejects(lib, kw, code):
     assert gm(lib, **kw) == code
 
 
+def test_grid_limits_are_unsupported(lib):
+    assert lib.sherry_quantize_pack(65535 * 64 + 1, 128, L.PER_TENSOR, 128, FAKE, L.F32, FAKE2, FAKE, None, 0,
+                                    None) == L.ERR_UNSUPPORTED
+    assert lib.sherry_quantize_pack(1, 128 * 65536, L.PER_TENSOR, 128, FAKE, L.F32, FAKE2, FAKE, None, 0,
+                                    None) == L.ERR_UNSUPPORTED
+
+
 def test_gemm_workspace_rejected_when_needed(lib):
     # 128 rows against a 512x2048 weight give 8 output tiles: the plan splits
     # K, which needs a workspace

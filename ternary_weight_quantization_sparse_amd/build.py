@@ -30,7 +30,10 @@ COMMON = [
     "-I", os.path.join(ROOT, "include"),
 ]
 # the scale sums must be plain fp32 adds in a fixed order
-PER_SOURCE = {"quantize_pack.hip": ["-ffp-contract=off"]}
+# gemv.hip: MFMA accumulators in VGPRs, so the per-group scale FMAs read them
+# without a copy out of the accumulation registers first
+PER_SOURCE = {"quantize_pack.hip": ["-ffp-contract=off"],
+              "gemv.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 
 def hipcc() -> str:

@@ -64,25 +64,6 @@ constexpr int kRecNib = 0, kRecSgn = 64 * 16, kRecAlpha = kRecSgn + 64 * 4;
 __device__ inline int swz_key(int row) { return (row >> 1) & 7; }
 __device__ inline int swz(int row, int ch) { return row * kRowBytes + ((ch ^ swz_key(row)) << 4); }
 
-// bf16 patterns of one block (4 weights) from its 5-bit code: code =
-// s<<4 | z<<2 | p1<<1 | p0; the kept positions in order carry the signs
-// s, s^p0, s^p1; position z is 0.
-__device__ inline uint2 decode_bf16(uint32_t code) {
-  const uint32_t z = (code >> 2) & 3;
-  const uint32_t neg0 = (code >> 4) & 1;
-  const uint32_t neg1 = neg0 ^ (code & 1);
-  const uint32_t neg2 = neg0 ^ ((code >> 1) & 1);
-  uint32_t h[4];
-  uint32_t rank = 0;
-#pragma unroll
-  for (uint32_t pos = 0; pos < 4; ++pos) {
-    const uint32_t neg = rank == 0 ? neg0 : (rank == 1 ? neg1 : neg2);
-    h[pos] = (pos == z) ? 0u : (neg ? 0xBF80u : 0x3F80u);
-    rank += (pos == z) ? 0u : 1u;
-  }
-  return make_uint2(h[0] | (h[1] << 16), h[2] | (h[3] << 16));
-}
-
 // TM = MFMA tiles per wave along m: 8 (128-row tiles), or 4 (64-row tiles)
 // for per_group, whose second accumulator set would not fit otherwise.
 // AR: the Arenas training forward, which adds lambda * X W^T over the dense
@@ -99,29 +80,6 @@ struct GemmCfg {
   // and sign records, and for per_group the scales
   static constexpr int VM_PER_STAGE = kXLoads + 2 + (kGroup ? 1 : 0) + kWLoads;
 };
-
-// s_waitcnt with only a vmcnt limit (expcnt / lgkmcnt left at their maxima).
-template <int VM>
-__device__ inline void wait_vmcnt() {
-  static_assert(VM >= 0 && VM < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((VM & 15) | (7 << 4) | (15 << 8) | ((VM >> 4) << 14));
-}
-
-typedef __attribute__((address_space(3))) void lds_void;
-// Word 3 of a raw buffer resource on gfx9-class parts: 32-bit data format
-// (a zero format would make every access read zero), no swizzle, no stride.
-constexpr int kBufferWord3 = 0x00020000;
-
-// Workgroup barrier that orders LDS only: this wave's LDS reads and writes
-// are complete (lgkmcnt 0) before it arrives.  Unlike __syncthreads it does
-// not wait for vector-memory operations, so copies for later stages stay in
-// flight; their completion is waited for explicitly (vmcnt) before the
-// barrier that publishes them.  The memory clobber keeps the compiler from
-// moving LDS accesses across it.
-__device__ inline void lds_barrier() {
-  __builtin_amdgcn_s_waitcnt(15 | (7 << 4) | (0 << 8) | (3 << 14));
-  asm volatile("s_barrier" ::: "memory");
-}
 
 template <int J>
 using Slot = std::integral_constant<int, J>;

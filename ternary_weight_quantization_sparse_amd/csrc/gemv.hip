@@ -20,11 +20,8 @@
 //
 // Batch 2..16 (gemv_mfma_kernel): the contraction is no longer HBM-bound on
 // VALU (batch x 3 adds per block), so blocks are decoded to bf16 and fed to
-// v_mfma_f32_16x16x32_bf16 with the batch as the M dimension.  Decode: the
-// same 4-block byte offsets index a 128-byte LDS table whose 32 dword entries
-// hold the high bytes of the four bf16 weights (+-0.5 or 0, so the low bytes
-// are 0 and the result is rescaled by 2, exactly); two v_perm_b32 spread a
-// dword into the two bf16x2 operand registers.
+// v_mfma_f32_16x16x32_bf16 with the batch as the M dimension; weight records
+// and activations reach LDS by DMA copies (details at the kernel).
 #include <type_traits>
 
 #include "sherry_internal.h"
@@ -35,6 +32,7 @@ namespace {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kLutThreads = 256;
 #ifndef SHERRY_GEMV_SPLIT_TARGET
@@ -255,185 +253,291 @@ __global__ __launch_bounds__(kLutThreads) void gemv_b1_lut_kernel(
   }
 }
 
-// Decode table entry for a code: the high bytes of the 4 bf16 weights, with
-// +-0.5 (0x3F / 0xBF) for kept weights and 0 for the pruned one.
-__device__ inline uint32_t decode_table_entry(uint32_t code) {
-  const uint32_t z = (code >> 2) & 3;
-  const uint32_t neg0 = (code >> 4) & 1;
-  const uint32_t neg1 = neg0 ^ (code & 1);
-  const uint32_t neg2 = neg0 ^ ((code >> 1) & 1);
-  uint32_t e = 0;
-  uint32_t rank = 0;
-  for (uint32_t pos = 0; pos < 4; ++pos) {
-    if (pos == z) continue;
-    const uint32_t neg = rank == 0 ? neg0 : (rank == 1 ? neg1 : neg2);
-    e |= (neg ? 0xBFu : 0x3Fu) << (8 * pos);
-    ++rank;
-  }
-  return e;
+// Batch 2..16.  Workgroup = 4 waves; a wave owns 64 rows as 4 tiles of 16,
+// so every activation fragment feeds 4 MFMAs, and walks the split's K range
+// one superblock at a time.  Lane (r, q) supplies blocks 2q+8t and 2q+1+8t
+// (t = 0..3) of row r of each tile, i.e. k = 32t + 8q .. +7 of the
+// superblock -- exactly nibble dword q of the row's record -- and the
+// activations of batch row r at the same k.
+//
+// Every load of the K loop is an LDS-DMA copy, which holds no registers in
+// flight, with explicit vmcnt waits (vmcnt counts in issue order, so a
+// register load issued a step ahead would force every copy issued before it
+// to land, and the ring would collapse):
+// * weights: each wave copies its own rows' records (1 KB of nibble records,
+//   256 B of sign dwords and, for per_group, 256 B of scales per superblock)
+//   into a private ring kMfmaRing superblocks deep, kMfmaRing - 1 ahead.  No
+//   barrier: no wave reads another's records.
+// * activations: chunks of kXChunk superblocks x XR batch rows (the batch
+//   rounded up; extra rows copy row 0), double-buffered and shared by the
+//   workgroup: the next chunk's copy is issued when a chunk starts and
+//   published by one barrier when it ends.  Rows are padded by 16 bytes so
+//   16 lanes reading 16 rows touch every bank once.
+//
+// Decode: a 32-entry LDS table holds each code's four bf16 weights (+-1, 0)
+// as one 8-byte entry; one ds_read_b64 per block gives both operand dwords
+// (a table of 4-byte high-byte entries plus two v_perm_b32 per block moves
+// half that LDS traffic to the VALU and measured slower).  The byte offsets
+// (code * 8) of four blocks come out of one nibble dword and the sign dword
+// with four bit operations.  All table lookups of a superblock are issued
+// before its 16 MFMAs so their latencies overlap.
+//
+// Per wave and superblock: 1.5 KB of weight records from HBM, ~42 LDS
+// instructions (of which 32 table lookups, ~16 KB), ~85 VALU and 16 MFMA;
+// the LDS traffic, not HBM, is what bounds this kernel today.
+constexpr int kMfmaTiles = 4;
+#ifndef SHERRY_MFMA_RING
+#define SHERRY_MFMA_RING 3
+#endif
+constexpr int kMfmaRing = SHERRY_MFMA_RING;
+constexpr int kXChunk = 4;                                    // superblocks per activation chunk
+constexpr int kXPitch = kXChunk * kSuperblock * 2 + 16;       // bytes per chunk row
+constexpr int kMRecNib = 0, kMRecSgn = 1024, kMRecAlpha = 1280;
+static_assert(kMfmaRing - 2 <= kXChunk, "the chunk-end wait must not cover records still ahead");
+
+// Byte offsets (code * 8) of the blocks of quad q = 2d + h of a superblock
+// (blocks q + 8b, b = 0..3, in byte b): nibble dword d, half h, sign bits
+// q + 8b moved to bit 7 of byte b.
+__device__ inline uint32_t quad_offsets8(uint32_t nib_dword, uint32_t sign_word, int q) {
+  const uint32_t nq = (q & 1) ? (nib_dword >> 1) : (nib_dword << 3);
+  const uint32_t sq = (sign_word << (7 - q)) & 0x80808080u;
+  return __builtin_amdgcn_bitop3_b32(nq, sq, 0x78787878u, 0xEC);  // (nq & mask) | sq
 }
 
-// Batch 2..16.  Workgroup = 4 waves; a wave owns 4 tiles of 16 rows (64
-// rows) so every activation fragment feeds 4 MFMAs.  The K loop walks one
-// superblock at a time through a ring of kMfmaDepth register sets: while the
-// MFMAs of superblock g run, the lane's records (nibble dword q and sign dword
-// of its 4 rows, and the group scales) for g + kMfmaDepth - 1 and the
-// activation fragments for g + 1 are already on their way, so the weight
-// stream never waits for a compute phase.  Lane (r, q) supplies blocks 2q+8t
-// and 2q+1+8t (t = 0..3) of row r, i.e. k = 32t + 8q .. +7 of the
-// superblock, and the activations of batch row r at the same k.
-constexpr int kMfmaTiles = 4;
-constexpr int kMfmaDepth = 4;
-
-template <int J>
-using RingSlot = std::integral_constant<int, J>;
-
-template <int MODE, bool YBF16>
+template <int MODE, int XR, bool YBF16>
 __global__ __launch_bounds__(256) void gemv_mfma_kernel(
-    const uint8_t* __restrict__ packed, const float* __restrict__ alpha,
-    const uint16_t* __restrict__ x, void* __restrict__ y, float* __restrict__ partial, int64_t n,
-    int64_t k, int group_sbs, int batch, int ksplit, int64_t packed_stride, int64_t alpha_stride,
-    int64_t y_stride) {
-  __shared__ uint32_t dtbl[32];
-  if (threadIdx.x < 32) dtbl[threadIdx.x] = decode_table_entry(threadIdx.x);
-  __syncthreads();
+    const uint8_t* packed, const float* alpha, const uint16_t* __restrict__ x, void* __restrict__ y,
+    float* __restrict__ partial, int64_t n, int64_t k, int group_sbs, int batch, int ksplit,
+    int64_t packed_stride, int64_t alpha_stride, int64_t y_stride) {
+  constexpr bool kGroup = MODE == kGroup1 || MODE == kGroupN;
+  constexpr int kRec = kGroup ? 1536 : 1280;  // record bytes per wave per superblock
+  constexpr int kOps = kGroup ? 3 : 2;        // record copies per wave per superblock
+  constexpr int kXOps = XR / 4;               // activation copies per wave per chunk
+  __shared__ __attribute__((aligned(16))) char ring[4][kMfmaRing * kRec];
+  __shared__ __attribute__((aligned(16))) char xbuf[2][XR * kXPitch];
+  __shared__ __attribute__((aligned(16))) uint2 dtab[32];
+  if (threadIdx.x < 32) dtab[threadIdx.x] = decode_bf16(threadIdx.x);
 
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int r = lane & 15;  // weight row inside a 16-row tile / batch row of x
   const int q = lane >> 4;  // nibble dword q of each superblock record
-  const int64_t row0 = (int64_t)blockIdx.x * (64 * kMfmaTiles) + wave * (16 * kMfmaTiles) + r;
+  const int64_t wrow0 = (int64_t)blockIdx.x * (64 * kMfmaTiles) + wave * (16 * kMfmaTiles);
   const int64_t c = blockIdx.y;
   const int kz = blockIdx.z;
   const int64_t nsb = k / kSuperblock;
-  const int64_t sb_per_split = nsb / ksplit;
-  const int64_t sb_begin = kz * sb_per_split;
-  const int64_t sb_end = sb_begin + sb_per_split;
+  const int sb_per_split = (int)(nsb / ksplit);
+  const int64_t sb_begin = kz * (int64_t)sb_per_split;
 
+  // (no __restrict__ on the record planes: the copies must stay where they
+  // are issued)
   const uint8_t* pk = packed + c * packed_stride;
-  const uint8_t* __restrict__ sgn_base = pk + nibble_plane_bytes(n, k);
-  const float* __restrict__ al = alpha + c * alpha_stride;
-  // lanes past the batch read row 0: they only feed output rows that are not
-  // stored, and an unconditional load needs no branch
-  const uint16_t* xrow = x + (int64_t)(r < batch ? r : 0) * k;
-  const char* dt = reinterpret_cast<const char*>(dtbl);
-  constexpr bool kGroup = MODE == kGroup1 || MODE == kGroupN;
+  const uint8_t* sgn_base = pk + nibble_plane_bytes(n, k);
+  const float* al = alpha + c * alpha_stride;
+  char* my_ring = ring[wave];
+  const uint32_t ring_lds = (uint32_t)(size_t)(__attribute__((address_space(3))) char*)my_ring;
 
-  uint32_t rows[kMfmaTiles];
-#pragma unroll
-  for (int i = 0; i < kMfmaTiles; ++i) {
-    const int64_t rr = row0 + i * 16;
-    rows[i] = (uint32_t)(rr < n ? rr : n - 1);  // clamped rows are not stored
-  }
+  // row whose records this lane copies (clamped rows are not stored)
+  int64_t crow = wrow0 + lane;
+  crow = crow < n ? crow : n - 1;
 
-  f32x4 acc[kMfmaTiles], accg[kMfmaTiles];
-#pragma unroll
-  for (int i = 0; i < kMfmaTiles; ++i) {
-    acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
-    accg[i] = f32x4{0.f, 0.f, 0.f, 0.f};
-  }
-  int gpos = 0;
-
-  uint32_t nd[kMfmaDepth][kMfmaTiles], sg[kMfmaDepth][kMfmaTiles];
-  float av[kMfmaDepth][kGroup ? kMfmaTiles : 1];
-  u32x4 xf[2][4];
-  // fetches past the split's end repeat its last superblock (never used)
-  auto fetch = [&](auto J, int64_t g) {
-    constexpr int j = decltype(J)::value;
-    g = g < sb_end ? g : sb_end - 1;
-#pragma unroll
-    for (int i = 0; i < kMfmaTiles; ++i) {
-      nd[j][i] = stream_load(reinterpret_cast<const uint32_t*>(pk + g * n * 16 + rows[i] * 16u + q * 4u));
-      sg[j][i] = stream_load(reinterpret_cast<const uint32_t*>(sgn_base + g * n * 4 + rows[i] * 4u));
-      if constexpr (MODE == kGroup1) av[j][i] = stream_load(al + g * n + rows[i]);
-      if constexpr (MODE == kGroupN) av[j][i] = stream_load(al + (g / group_sbs) * n + rows[i]);
+  // Copies of the records, in superblock order: each call copies superblock
+  // `iss` of the split into ring slot `slot` and moves on to the next one
+  // (past the end it copies the last one again; those are never used).  The
+  // plane pointers advance with it, so no per-copy address arithmetic.
+  int iss = 0, apos = 0;
+  const uint8_t* nib_p = pk + sb_begin * n * 16 + crow * 16;
+  const uint8_t* sgn_p = sgn_base + sb_begin * n * 4 + crow * 4;
+  const float* al_p = al + (kGroup ? (sb_begin / group_sbs) * n : 0) + crow;
+  auto issue = [&](int slot) {
+    char* rb = my_ring + slot * kRec;
+    __builtin_amdgcn_global_load_lds(const_cast<uint8_t*>(nib_p), (lds_void*)(rb + kMRecNib), 16, 0, 0);
+    __builtin_amdgcn_global_load_lds(const_cast<uint8_t*>(sgn_p), (lds_void*)(rb + kMRecSgn), 4, 0, 0);
+    if constexpr (kGroup)
+      __builtin_amdgcn_global_load_lds(const_cast<float*>(al_p), (lds_void*)(rb + kMRecAlpha), 4, 0, 0);
+    if (iss + 1 < sb_per_split) {
+      ++iss;
+      nib_p += n * 16;
+      sgn_p += n * 4;
+      if constexpr (MODE == kGroup1) al_p += n;
+      if constexpr (MODE == kGroupN) {
+        if (++apos == group_sbs) { apos = 0; al_p += n; }
+      }
     }
   };
-  auto fetch_x = [&](auto X, int64_t g) {
-    constexpr int xs = decltype(X)::value;
-    g = g < sb_end ? g : sb_end - 1;
+
+  // activation chunk ch (superblocks kXChunk*ch .. of the split) into buffer
+  // b: wave w copies rows w, w + 4, ...; each row is one 1 KB copy.  Reads
+  // past the activations' end (a short last chunk) fall outside the buffer
+  // resource and return zeros.
+  const uint32_t xbytes = (uint32_t)(batch * k * 2);
+  const __amdgpu_buffer_rsrc_t xr = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t*>(x), (short)0, (int)xbytes, kBufferWord3);
+  auto issue_x = [&](int ch, int b) {
+    ch = ch * kXChunk < sb_per_split ? ch : (sb_per_split - 1) / kXChunk;
+    const uint32_t col = (uint32_t)((sb_begin + (int64_t)ch * kXChunk) * (kSuperblock * 2)) + lane * 16u;
 #pragma unroll
-    for (int t = 0; t < 4; ++t) xf[xs][t] = *reinterpret_cast<const u32x4*>(xrow + g * kSuperblock + 32 * t + 8 * q);
+    for (int i = 0; i < kXOps; ++i) {
+      const int row = wave + 4 * i;
+      const uint32_t src = (uint32_t)(row < batch ? row : 0) * (uint32_t)(k * 2);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(xr, (lds_void*)(xbuf[b] + row * kXPitch), 16, src + col, 0, 0, 0);
+    }
   };
-  auto compute = [&](auto J, auto X) {
-    constexpr int j = decltype(J)::value;
-    constexpr int xs = decltype(X)::value;
+
+  // This lane's operands of one superblock: from its ring slot, nibble dword
+  // q and the sign dword of rows r + 16 i (and for per_group their scales);
+  // from the activation chunk, the four 16-byte fragments of batch row r.
+  // One asm block that waits for its own results: the compiler cannot tell
+  // these reads from ones that might overlap copies still in flight and
+  // would wait for every copy first.
+  uint32_t nd[kMfmaTiles], sg[kMfmaTiles];
+  float av[kGroup ? kMfmaTiles : 1];
+  u32x4 xf[4];
+  const uint32_t xbuf_lds = (uint32_t)(size_t)(__attribute__((address_space(3))) char*)&xbuf[0][0];
+  const uint32_t xrow_off = (uint32_t)((r < batch ? r : 0) * kXPitch + 16 * q);
+  auto read_operands = [&](int slot, int b, int s) {
+    const uint32_t rb = ring_lds + (uint32_t)(slot * kRec);
+    const uint32_t a_nib = rb + kMRecNib + r * 16 + q * 4;
+    const uint32_t a_sgn = rb + kMRecSgn + r * 4;
+    const uint32_t a_x = xbuf_lds + (uint32_t)(b * XR * kXPitch + s * (kSuperblock * 2)) + xrow_off;
+    u32x2 n01, n23, s01, s23;  // tiles (0, 1) and (2, 3)
+    u32x4 x0, x1, x2, x3;
+    if constexpr (kGroup) {
+      const uint32_t a_al = rb + kMRecAlpha + r * 4;
+      u32x2 a01, a23;
+      asm volatile(
+          "ds_read2st64_b32 %0, %10 offset1:1\n"
+          "ds_read2st64_b32 %1, %10 offset0:2 offset1:3\n"
+          "ds_read2_b32 %2, %11 offset1:16\n"
+          "ds_read2_b32 %3, %11 offset0:32 offset1:48\n"
+          "ds_read2_b32 %4, %12 offset1:16\n"
+          "ds_read2_b32 %5, %12 offset0:32 offset1:48\n"
+          "ds_read_b128 %6, %13\n"
+          "ds_read_b128 %7, %13 offset:64\n"
+          "ds_read_b128 %8, %13 offset:128\n"
+          "ds_read_b128 %9, %13 offset:192\n"
+          "s_waitcnt lgkmcnt(0)"
+          : "=&v"(n01), "=&v"(n23), "=&v"(s01), "=&v"(s23), "=&v"(a01), "=&v"(a23),
+            "=&v"(x0), "=&v"(x1), "=&v"(x2), "=&v"(x3)
+          : "v"(a_nib), "v"(a_sgn), "v"(a_al), "v"(a_x)
+          : "memory");
+      av[0] = __uint_as_float(a01[0]);
+      av[kGroup ? 1 : 0] = __uint_as_float(a01[1]);
+      av[kGroup ? 2 : 0] = __uint_as_float(a23[0]);
+      av[kGroup ? 3 : 0] = __uint_as_float(a23[1]);
+    } else {
+      asm volatile(
+          "ds_read2st64_b32 %0, %8 offset1:1\n"
+          "ds_read2st64_b32 %1, %8 offset0:2 offset1:3\n"
+          "ds_read2_b32 %2, %9 offset1:16\n"
+          "ds_read2_b32 %3, %9 offset0:32 offset1:48\n"
+          "ds_read_b128 %4, %10\n"
+          "ds_read_b128 %5, %10 offset:64\n"
+          "ds_read_b128 %6, %10 offset:128\n"
+          "ds_read_b128 %7, %10 offset:192\n"
+          "s_waitcnt lgkmcnt(0)"
+          : "=&v"(n01), "=&v"(n23), "=&v"(s01), "=&v"(s23), "=&v"(x0), "=&v"(x1), "=&v"(x2), "=&v"(x3)
+          : "v"(a_nib), "v"(a_sgn), "v"(a_x)
+          : "memory");
+    }
+    nd[0] = n01[0]; nd[1] = n01[1]; nd[2] = n23[0]; nd[3] = n23[1];
+    sg[0] = s01[0]; sg[1] = s01[1]; sg[2] = s23[0]; sg[3] = s23[1];
+    xf[0] = x0; xf[1] = x1; xf[2] = x2; xf[3] = x3;
+  };
+
+  f32x4 acc[kMfmaTiles], accg[kGroup ? kMfmaTiles : 1];
+#pragma unroll
+  for (int i = 0; i < kMfmaTiles; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+  int gpos = 0;
+
+  auto compute = [&]() {
     uint32_t off_lo[kMfmaTiles], off_hi[kMfmaTiles];
 #pragma unroll
     for (int i = 0; i < kMfmaTiles; ++i) {
-      off_lo[i] = quad_offsets(nd[j][i], sg[j][i], 2 * q);      // blocks 2q + 8t
-      off_hi[i] = quad_offsets(nd[j][i], sg[j][i], 2 * q + 1);  // blocks 2q + 1 + 8t
+      off_lo[i] = quad_offsets8(nd[i], sg[i], 2 * q);      // blocks 2q + 8t
+      off_hi[i] = quad_offsets8(nd[i], sg[i], 2 * q + 1);  // blocks 2q + 1 + 8t
+    }
+    const bool first = MODE == kGroup1 || (MODE == kGroupN && gpos == 0);  // a group starts here
+    // every table lookup of the superblock first (their latencies overlap),
+    // then the 16 MFMAs
+    u32x4 wv[4][kMfmaTiles];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+#pragma unroll
+      for (int i = 0; i < kMfmaTiles; ++i) {
+        const uint2 e0 = *reinterpret_cast<const uint2*>(
+            reinterpret_cast<const char*>(dtab) + __builtin_amdgcn_ubfe(off_lo[i], 8 * t, 8));
+        const uint2 e1 = *reinterpret_cast<const uint2*>(
+            reinterpret_cast<const char*>(dtab) + __builtin_amdgcn_ubfe(off_hi[i], 8 * t, 8));
+        wv[t][i] = u32x4{e0.x, e0.y, e1.x, e1.y};
+      }
     }
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
-      const bf16x8 xv = __builtin_bit_cast(bf16x8, xf[xs][t]);
+      const bf16x8 xv = __builtin_bit_cast(bf16x8, xf[t]);
 #pragma unroll
       for (int i = 0; i < kMfmaTiles; ++i) {
-        const uint32_t e0 = *reinterpret_cast<const uint32_t*>(dt + __builtin_amdgcn_ubfe(off_lo[i], 8 * t, 8));
-        const uint32_t e1 = *reinterpret_cast<const uint32_t*>(dt + __builtin_amdgcn_ubfe(off_hi[i], 8 * t, 8));
-        u32x4 wv;
-        wv[0] = __builtin_amdgcn_perm(0u, e0, 0x010C000Cu);
-        wv[1] = __builtin_amdgcn_perm(0u, e0, 0x030C020Cu);
-        wv[2] = __builtin_amdgcn_perm(0u, e1, 0x010C000Cu);
-        wv[3] = __builtin_amdgcn_perm(0u, e1, 0x030C020Cu);
+        const bf16x8 w8 = __builtin_bit_cast(bf16x8, wv[t][i]);
         if constexpr (kGroup) {
-          accg[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xv, __builtin_bit_cast(bf16x8, wv), accg[i], 0, 0, 0);
+          // the group's first MFMA starts from zero instead of clearing accg
+          const f32x4 cin = (t == 0 && first) ? f32x4{0.f, 0.f, 0.f, 0.f} : accg[i];
+          accg[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xv, w8, cin, 0, 0, 0);
         } else {
-          acc[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xv, __builtin_bit_cast(bf16x8, wv), acc[i], 0, 0, 0);
+          acc[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xv, w8, acc[i], 0, 0, 0);
         }
       }
     }
     if constexpr (kGroup) {
       if (++gpos == group_sbs) {
 #pragma unroll
-        for (int i = 0; i < kMfmaTiles; ++i) {
-          const float a2 = 2.f * av[j][i];
+        for (int i = 0; i < kMfmaTiles; ++i)
 #pragma unroll
-          for (int e = 0; e < 4; ++e) acc[i][e] += a2 * accg[i][e];
-          accg[i] = f32x4{0.f, 0.f, 0.f, 0.f};
-        }
+          for (int e = 0; e < 4; ++e) acc[i][e] += av[i] * accg[i][e];
         gpos = 0;
       }
     }
   };
-  // one superblock: prefetch, then compute slot J with activations X
-  auto step = [&](auto J, auto X, int64_t g) {
-    constexpr int j = decltype(J)::value;
-    constexpr int xs = decltype(X)::value;
-    fetch(RingSlot<(j + kMfmaDepth - 1) % kMfmaDepth>{}, g + kMfmaDepth - 1);
-    fetch_x(RingSlot<1 - xs>{}, g + 1);
-    compute(J, X);
-  };
 
-  static_assert(kMfmaDepth == 4, "the loop below is unrolled by the ring depth");
-  fetch(RingSlot<0>{}, sb_begin);
-  fetch(RingSlot<1>{}, sb_begin + 1);
-  fetch(RingSlot<2>{}, sb_begin + 2);
-  fetch_x(RingSlot<0>{}, sb_begin);
-  // (every early exit leaves the loop, so each path into a step passes
-  // through the step before it and the compiler's waits stay exact)
-  for (int64_t g = sb_begin;; g += 4) {
-    step(RingSlot<0>{}, RingSlot<0>{}, g);
-    if (g + 1 >= sb_end) break;
-    step(RingSlot<1>{}, RingSlot<1>{}, g + 1);
-    if (g + 2 >= sb_end) break;
-    step(RingSlot<2>{}, RingSlot<0>{}, g + 2);
-    if (g + 3 >= sb_end) break;
-    step(RingSlot<3>{}, RingSlot<1>{}, g + 3);
-    if (g + 4 >= sb_end) break;
+  // Prologue: activation chunk 0, records of superblocks 0 .. kMfmaRing - 2.
+  issue_x(0, 0);
+  for (int j = 0; j < kMfmaRing - 1; ++j) issue(j);
+  wait_vmcnt<(kMfmaRing - 1) * kOps>();  // chunk 0 has landed
+  lds_barrier();                          // ... for every wave, and the table is written
+
+  // Chunk ch: issue chunk ch + 1, then per superblock j: copy the records of
+  // j + kMfmaRing - 1, wait for those of j (issued kMfmaRing - 1 steps ago; at
+  // most the later records and one activation chunk are in flight), compute.
+  int slot = 0;
+  const int chunks = (sb_per_split + kXChunk - 1) / kXChunk;
+  for (int ch = 0; ch < chunks; ++ch) {
+    issue_x(ch + 1, (ch + 1) & 1);
+#pragma unroll
+    for (int s = 0; s < kXChunk; ++s) {
+      const int j = ch * kXChunk + s;
+      issue(slot == 0 ? kMfmaRing - 1 : slot - 1);  // superblock j + kMfmaRing - 1
+      wait_vmcnt<(kMfmaRing - 1) * kOps>();
+      if (j < sb_per_split) {
+        read_operands(slot, ch & 1, s);
+        compute();
+      }
+      slot = slot == kMfmaRing - 1 ? 0 : slot + 1;
+    }
+    // the next chunk was issued before this chunk's kXChunk record copies
+    wait_vmcnt<kXChunk * kOps>();
+    lds_barrier();
   }
+  wait_vmcnt<0>();  // the trailing copies have landed in LDS before the wave ends
 
   // lane holds D[batch 4q + e][row r] of each tile
 #pragma unroll
   for (int i = 0; i < kMfmaTiles; ++i) {
-    const int64_t row = row0 + i * 16;
+    const int64_t row = wrow0 + i * 16 + r;
     if (row >= n) continue;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const int b = 4 * q + e;
       if (b >= batch) continue;
       float v = acc[i][e];
-      if constexpr (!kGroup) v *= 2.f;
       if (ksplit == 1) {
         if constexpr (MODE == kChannel) v *= al[row];
         if constexpr (MODE == kTensor) v *= al[0];
@@ -525,14 +629,21 @@ hipError_t launch_gemv_t(const GemvPlan& p, int64_t n, int64_t k, int group_size
     const int mode = GRAN == SHERRY_PER_CHANNEL ? kChannel
                    : GRAN == SHERRY_PER_TENSOR  ? kTensor
                    : (group_sbs == 1 ? kGroup1 : kGroupN);
-#define SHERRY_MFMA_CASE(MD)                                                                                \
-  hipLaunchKernelGGL((gemv_mfma_kernel<MD, YBF16>), grid, dim3(256), 0, s, packed, alpha, x, y, ws, n, k, \
-                     group_sbs, batch, p.ksplit, packed_stride, alpha_stride, y_stride)
+#define SHERRY_MFMA_XR(MD, XR)                                                                           \
+  hipLaunchKernelGGL((gemv_mfma_kernel<MD, XR, YBF16>), grid, dim3(256), 0, s, packed, alpha, x, y, ws, n, \
+                     k, group_sbs, batch, p.ksplit, packed_stride, alpha_stride, y_stride)
+#define SHERRY_MFMA_CASE(MD)                                 \
+  do {                                                       \
+    if (batch <= 4) SHERRY_MFMA_XR(MD, 4);                   \
+    else if (batch <= 8) SHERRY_MFMA_XR(MD, 8);              \
+    else SHERRY_MFMA_XR(MD, 16);                             \
+  } while (0)
     if (mode == kGroup1) SHERRY_MFMA_CASE(kGroup1);
     else if (mode == kGroupN) SHERRY_MFMA_CASE(kGroupN);
     else if (mode == kChannel) SHERRY_MFMA_CASE(kChannel);
     else SHERRY_MFMA_CASE(kTensor);
 #undef SHERRY_MFMA_CASE
+#undef SHERRY_MFMA_XR
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || p.ksplit == 1) return e;

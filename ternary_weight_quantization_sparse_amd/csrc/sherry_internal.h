@@ -116,6 +116,42 @@ __device__ inline uint32_t load_code(const uint8_t* __restrict__ packed, int64_t
   return (sgn << 4) | nib;
 }
 
+// bf16 patterns of one block (4 weights, +-1 or 0) from its code, as the two
+// dwords of an MFMA operand: positions 0,1 in the first, 2,3 in the second.
+__device__ inline uint2 decode_bf16(uint32_t code) {
+  int t[4];
+  decode_block(code, t);
+  uint32_t h[4];
+#pragma unroll
+  for (int pos = 0; pos < 4; ++pos) h[pos] = t[pos] == 0 ? 0u : (t[pos] < 0 ? 0xBF80u : 0x3F80u);
+  return make_uint2(h[0] | (h[1] << 16), h[2] | (h[3] << 16));
+}
+
+// s_waitcnt with only a vmcnt limit (expcnt / lgkmcnt left at their maxima).
+template <int VM>
+__device__ inline void wait_vmcnt() {
+  static_assert(VM >= 0 && VM < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((VM & 15) | (7 << 4) | (15 << 8) | ((VM >> 4) << 14));
+}
+
+// LDS pointer type of the copy builtins that write LDS directly.
+typedef __attribute__((address_space(3))) void lds_void;
+
+// Word 3 of a raw buffer resource on gfx9-class parts: 32-bit data format
+// (a zero format would make every access read zero), no swizzle, no stride.
+constexpr int kBufferWord3 = 0x00020000;
+
+// Workgroup barrier that orders LDS only: this wave's LDS reads and writes
+// are complete (lgkmcnt 0) before it arrives.  Unlike __syncthreads it does
+// not wait for vector-memory operations, so copies for later stages stay in
+// flight; their completion is waited for explicitly (vmcnt) before the
+// barrier that publishes them.  The memory clobber keeps the compiler from
+// moving LDS accesses across it.
+__device__ inline void lds_barrier() {
+  __builtin_amdgcn_s_waitcnt(15 | (7 << 4) | (0 << 8) | (3 << 14));
+  asm volatile("s_barrier" ::: "memory");
+}
+
 // Round an fp32 value to bf16, nearest-even (inputs are finite).
 __device__ inline uint16_t f32_to_bf16_rne(float f) {
   uint32_t u = __float_as_uint(f);

@@ -38,6 +38,9 @@ constexpr int kLutThreads = 256;
 #ifndef SHERRY_GEMV_SPLIT_TARGET
 #define SHERRY_GEMV_SPLIT_TARGET 2048
 #endif
+#ifndef SHERRY_GEMV_MFMA_SPLIT_TARGET
+#define SHERRY_GEMV_MFMA_SPLIT_TARGET 768
+#endif
 #ifndef SHERRY_LUT_WIN_MAX
 #define SHERRY_LUT_WIN_MAX 4  // superblocks per LDS table window (4 -> 16 KB)
 #endif
@@ -290,10 +293,14 @@ constexpr int kMfmaTiles = 4;
 #define SHERRY_MFMA_RING 3
 #endif
 constexpr int kMfmaRing = SHERRY_MFMA_RING;
-constexpr int kXChunk = 4;                                    // superblocks per activation chunk
-constexpr int kXPitch = kXChunk * kSuperblock * 2 + 16;       // bytes per chunk row
+#ifndef SHERRY_XCHUNK_SMALL
+#define SHERRY_XCHUNK_SMALL 8
+#endif
+// superblocks per activation chunk (a multiple of 4: one 1 KB copy per row
+// and 4 superblocks) and bytes per chunk row (padded by 16)
+template <int XR> constexpr int kXChunkOf = XR == 4 ? SHERRY_XCHUNK_SMALL : 4;
+template <int XR> constexpr int kXPitchOf = kXChunkOf<XR> * kSuperblock * 2 + 16;
 constexpr int kMRecNib = 0, kMRecSgn = 1024, kMRecAlpha = 1280;
-static_assert(kMfmaRing - 2 <= kXChunk, "the chunk-end wait must not cover records still ahead");
 
 // Byte offsets (code * 8) of the blocks of quad q = 2d + h of a superblock
 // (blocks q + 8b, b = 0..3, in byte b): nibble dword d, half h, sign bits
@@ -312,7 +319,11 @@ __global__ __launch_bounds__(256) void gemv_mfma_kernel(
   constexpr bool kGroup = MODE == kGroup1 || MODE == kGroupN;
   constexpr int kRec = kGroup ? 1536 : 1280;  // record bytes per wave per superblock
   constexpr int kOps = kGroup ? 3 : 2;        // record copies per wave per superblock
-  constexpr int kXOps = XR / 4;               // activation copies per wave per chunk
+  constexpr int kXChunk = kXChunkOf<XR>, kXPitch = kXPitchOf<XR>;
+  constexpr int kXPieces = kXChunk / 4;       // 1 KB copies per activation row per chunk
+  constexpr int kXOps = XR / 4 * kXPieces;    // activation copies per wave per chunk
+  static_assert(kXChunk % 4 == 0, "chunks are whole 1 KB copies");
+  static_assert(kMfmaRing - 2 <= kXChunk, "the chunk-end wait must not cover records still ahead");
   __shared__ __attribute__((aligned(16))) char ring[4][kMfmaRing * kRec];
   __shared__ __attribute__((aligned(16))) char xbuf[2][XR * kXPitch];
   __shared__ __attribute__((aligned(16))) uint2 dtab[32];
@@ -377,10 +388,13 @@ __global__ __launch_bounds__(256) void gemv_mfma_kernel(
     ch = ch * kXChunk < sb_per_split ? ch : (sb_per_split - 1) / kXChunk;
     const uint32_t col = (uint32_t)((sb_begin + (int64_t)ch * kXChunk) * (kSuperblock * 2)) + lane * 16u;
 #pragma unroll
-    for (int i = 0; i < kXOps; ++i) {
+    for (int i = 0; i < XR / 4; ++i) {
       const int row = wave + 4 * i;
       const uint32_t src = (uint32_t)(row < batch ? row : 0) * (uint32_t)(k * 2);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(xr, (lds_void*)(xbuf[b] + row * kXPitch), 16, src + col, 0, 0, 0);
+#pragma unroll
+      for (int pc = 0; pc < kXPieces; ++pc)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(xr, (lds_void*)(xbuf[b] + row * kXPitch + pc * 1024), 16,
+                                                 src + col + pc * 1024u, 0, 0, 0);
     }
   };
 
@@ -672,11 +686,11 @@ GemvPlan plan_gemv(int64_t n, int64_t k, int gran, int group_size, int batch, in
   }
   p.panels = (n + rows_per_wg - 1) / rows_per_wg;
   // Split K (in whole groups) until the launch has ~2048 workgroups (batch 1;
-  // the table kernel keeps 8 per CU resident) or ~1024 (batch > 1).
+  // the table kernel keeps 8 per CU resident) or ~768 (batch > 1, 3-5 per CU resident).
   const int64_t wgs = p.panels * count;
   const int64_t groups = nsb / group_sbs;
   int64_t split = 1;
-  const int64_t target = p.kind == 0 ? SHERRY_GEMV_SPLIT_TARGET : 1024;
+  const int64_t target = p.kind == 0 ? SHERRY_GEMV_SPLIT_TARGET : SHERRY_GEMV_MFMA_SPLIT_TARGET;
   while (wgs * split * 2 <= target && groups % (split * 2) == 0) split *= 2;
   p.ksplit = (int)split;
   const int64_t sb_per_split = nsb / split;

@@ -7,157 +7,233 @@
 // the nominal kept count L/4*3: "Sherry, Tequila and Fairies in Python",
 // section 1.1 (_reshape_by_granularity, SherryNMQuant.forward).
 //
-// Mapping: one workgroup (4 waves) per tile of 64 rows x one superblock of
-// 128 weights.  Each half-wave owns one (row, superblock) pair and each of its
-// 32 lanes one block of 4 weights, so a wave's loads are two contiguous row
-// segments (coalesced dwordx4 for fp32, dwordx2 for bf16).  The sign plane is
-// a ballot, the nibble dwords an OR-reduction over lanes 1/8/16 apart, and the
-// kept-|w| sum of the superblock a butterfly over XOR offsets 1..16 -- which
-// is exactly the index-order pairwise tree (each level adds lanes 2i and
-// 2i+1, and fp32 addition is commutative).
+// Mapping (details at the kernel): each lane quantizes a few adjacent blocks
+// of one row, a wave covers a contiguous row span of several superblocks, and
+// the per-superblock reductions (kept-|w| sum, sign dword, nibble dwords) are
+// cross-lane DPP moves inside rows of 16 lanes that reproduce the pairwise
+// tree's additions exactly.
 #include "sherry_internal.h"
 
 namespace sherry {
 namespace {
 
-constexpr int kRowsPerTile = 64;
-// Grid: x = superblock, y = 64-row tile, so consecutive workgroups read
-// adjacent 128-weight spans of the same rows.
-constexpr int kIters = kRowsPerTile / 8;  // 4 waves x 2 halves = 8 rows per iteration
-
-template <bool BF16>
-struct Block4 { float v[4]; };
-
-template <bool BF16>
-__device__ inline Block4<BF16> load_block(const void* w, int64_t row, int64_t k, int64_t col) {
-  Block4<BF16> b;
-  if constexpr (BF16) {
-    const uint2 u = *reinterpret_cast<const uint2*>(
-        reinterpret_cast<const uint16_t*>(w) + row * k + col);
-    b.v[0] = __uint_as_float(u.x << 16);
-    b.v[1] = __uint_as_float(u.x & 0xFFFF0000u);
-    b.v[2] = __uint_as_float(u.y << 16);
-    b.v[3] = __uint_as_float(u.y & 0xFFFF0000u);
-  } else {
-    const float4 f = *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(w) + row * k + col);
-    b.v[0] = f.x; b.v[1] = f.y; b.v[2] = f.z; b.v[3] = f.w;
-  }
-  return b;
-}
+#ifndef SHERRY_Q_BPL
+#define SHERRY_Q_BPL 2  // blocks per lane
+#endif
 
 // Quantize one block: returns the 5-bit code, and the kept-|w| sum of the
 // block as a two-level pairwise tree ((a0 + a1) + (a2 + a3)) with the zeroed
 // weight contributing +0.
+//
+// The zero position (first index of the minimum |w|) is a tournament: the
+// smaller of each pair (ties keep the lower index), then the smaller of the
+// two winners (ties keep the left pair).  The pair holding the zero sums to
+// its other member, the larger one (x + 0 = x exactly), so each half of the
+// tree is an add or a max.  The kept positions are then k0 < k1 < k2 =
+// (other of 0/1, 2, 3) when the zero is in the left pair, else (0, 1, other
+// of 2/3); the per-lane booleans stay lane masks until the code is built.
 __device__ inline uint32_t quantize_block(const float v[4], float& kept_sum) {
   const float a0 = fabsf(v[0]), a1 = fabsf(v[1]), a2 = fabsf(v[2]), a3 = fabsf(v[3]);
-  // zero position: first index of the minimum magnitude (strict compares)
-  uint32_t z = 0;
-  float m = a0;
-  if (a1 < m) { z = 1; m = a1; }
-  if (a2 < m) { z = 2; m = a2; }
-  if (a3 < m) { z = 3; }
-  // positive-sign mask, bit i = (v[i] > 0)
-  const uint32_t pos = (v[0] > 0.f ? 1u : 0u) | (v[1] > 0.f ? 2u : 0u) |
-                       (v[2] > 0.f ? 4u : 0u) | (v[3] > 0.f ? 8u : 0u);
-  // kept positions k0 < k1 < k2
-  const uint32_t k0 = (z == 0) ? 1u : 0u;
-  const uint32_t k1 = (z <= 1) ? 2u : 1u;
-  const uint32_t k2 = (z <= 2) ? 3u : 2u;
-  const uint32_t g0 = (pos >> k0) & 1u, g1 = (pos >> k1) & 1u, g2 = (pos >> k2) & 1u;
-  const uint32_t s = g0 ^ 1u;        // 1 when the first kept weight is negative
-  const uint32_t p0 = g1 ^ g0;       // second kept sign differs from the first
-  const uint32_t p1 = g2 ^ g0;       // third kept sign differs from the first
-  kept_sum = ((z == 0 ? 0.f : a0) + (z == 1 ? 0.f : a1)) +
-             ((z == 2 ? 0.f : a2) + (z == 3 ? 0.f : a3));
+  const bool c01 = a1 < a0;  // zero candidate of the left pair is 1 (and a0 is its larger)
+  const bool c23 = a3 < a2;  // ... of the right pair is 3 (and a2 is its larger)
+  const float m01 = c01 ? a1 : a0, m23 = c23 ? a3 : a2;
+  const bool c = m23 < m01;  // the zero is in the right pair
+  const uint32_t z = c ? (c23 ? 3u : 2u) : (c01 ? 1u : 0u);
+  const float left = c ? a0 + a1 : (c01 ? a0 : a1);
+  const float right = c ? (c23 ? a2 : a3) : a2 + a3;
+  kept_sum = left + right;
+  const bool pos0 = v[0] > 0.f, pos1 = v[1] > 0.f, pos2 = v[2] > 0.f, pos3 = v[3] > 0.f;
+  const bool q0 = c ? pos0 : (c01 ? pos0 : pos1);  // sign of the first kept weight
+  const bool q1 = c ? pos1 : pos2;                 // second
+  const bool q2 = c ? (c23 ? pos2 : pos3) : pos3;  // third
+  const uint32_t s = q0 ? 0u : 1u;                 // 1 when the first kept weight is negative
+  const uint32_t p0 = q1 != q0 ? 1u : 0u;          // second kept sign differs from the first
+  const uint32_t p1 = q2 != q0 ? 1u : 0u;          // third kept sign differs from the first
   return (s << 4) | (z << 2) | (p1 << 1) | p0;
 }
+
+// Cross-lane moves inside a row of 16 lanes (DPP): row_shr:n gives lane i
+// the value of lane i - n, row_ror:n that of lane (i - n) mod 16.
+template <int CTRL>
+__device__ inline uint32_t dpp(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xF, 0xF, false);
+}
+template <int CTRL>
+__device__ inline float dpp(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+constexpr int kShr1 = 0x111, kShr2 = 0x112, kShr4 = 0x114, kShr8 = 0x118, kRor4 = 0x124, kRor8 = 0x128;
+constexpr int kQuadXor2 = 0x4E;  // quad_perm [2, 3, 0, 1]
+// ds_swizzle patterns (bit mode, groups of 32 lanes): lane ^ 4, and the last
+// lane of each group of 16 / 8
+constexpr int kSwzXor4 = (4 << 10) | 0x1F, kSwzLast16 = (0x0F << 5) | 0x10, kSwzLast8 = (0x07 << 5) | 0x18;
 
 // DENSE = 0: write the packed planes (and the scale or the superblock sum).
 // DENSE = SHERRY_F32 + 1 / SHERRY_BF16 + 1 (per_group G = 128 only): the
 // fused fake-quant forward -- write T * alpha densely in fp32 (exact) or bf16
 // (round to nearest even) and the scales, no planes.
-template <bool BF16, int DENSE = 0>
+//
+// Mapping: a wave quantizes one row at a time over 2*BPL consecutive
+// superblocks; lane (s, i) -- s = lane / L, L = 32 / BPL lanes per
+// superblock -- owns the BPL adjacent blocks BPL*i .. of superblock s, one
+// contiguous 8*BPL-byte (bf16) or 16*BPL-byte (fp32) load.  The kept-|w| sum
+// of the superblock is the index-order pairwise tree over its 32 block sums:
+// the first log2(BPL) levels inside the lane, the rest across lanes with
+// row_shr by 1, 2, 4 (, 8), which leaves the tree's root in the group's last
+// lane (every add pairs the same two subtrees as the tree; fp32 addition is
+// commutative).  The sign dword is an OR over the same shifts; a nibble dword
+// collects its four bytes from the lanes that hold them (an OR over row_ror or
+// XOR partners).  Workgroup = 4 waves x kRowsPerWave rows.
+constexpr int kRowsPerWave = 8;
+constexpr int kRowsPerWg = 4 * kRowsPerWave;
+
+// Raw bytes of one lane's BPL blocks (8 per block for bf16, 16 for fp32).
+template <bool BF16, int BPL>
+struct LaneRaw { uint4 q[BF16 ? BPL / 2 : BPL]; };
+
+template <bool BF16, int BPL>
+__device__ inline LaneRaw<BF16, BPL> load_lane(const char* p) {
+  LaneRaw<BF16, BPL> r;
+#pragma unroll
+  for (int h = 0; h < (BF16 ? BPL / 2 : BPL); ++h) r.q[h] = reinterpret_cast<const uint4*>(p)[h];
+  return r;
+}
+
+// The 4 weights of block j of a lane as fp32.
+template <bool BF16, int BPL>
+__device__ inline void block_values(const LaneRaw<BF16, BPL>& r, int j, float v[4]) {
+  if constexpr (BF16) {
+    const uint4 u = r.q[j >> 1];
+    const uint32_t d0 = (j & 1) ? u.z : u.x, d1 = (j & 1) ? u.w : u.y;
+    v[0] = __uint_as_float(d0 << 16);
+    v[1] = __uint_as_float(d0 & 0xFFFF0000u);
+    v[2] = __uint_as_float(d1 << 16);
+    v[3] = __uint_as_float(d1 & 0xFFFF0000u);
+  } else {
+    const uint4 u = r.q[j];
+    v[0] = __uint_as_float(u.x); v[1] = __uint_as_float(u.y);
+    v[2] = __uint_as_float(u.z); v[3] = __uint_as_float(u.w);
+  }
+}
+
+template <bool BF16, int DENSE, int BPL>
 __global__ __launch_bounds__(256) void quantize_pack_kernel(
     const void* __restrict__ w, int64_t n, int64_t k, uint8_t* __restrict__ packed,
     float* __restrict__ alpha_direct, float* __restrict__ sb_sums, void* __restrict__ dense = nullptr) {
+  static_assert(BPL == 2 || BPL == 4, "blocks per lane");
+  constexpr int L = 32 / BPL;         // lanes per superblock
+  constexpr int SPW = 64 / L;         // superblocks per wave row
   const int64_t nsb = k / kSuperblock;
-  const int64_t g = blockIdx.x;
-  const int64_t row0 = (int64_t)blockIdx.y * kRowsPerTile;
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
-  const int half = lane >> 5;
-  const int j = lane & 31;  // block index inside the superblock
-  const int64_t col = g * kSuperblock + 4 * j;
+  const int s = lane / L, i = lane % L;
+  const int64_t g = (int64_t)blockIdx.x * SPW + s;  // this lane's superblock
+  const bool gv = g < nsb;
+  const int64_t col = g * kSuperblock + i * (4 * BPL);
+  const int64_t row0 = (int64_t)blockIdx.y * kRowsPerWg + wave * kRowsPerWave;
 
-  // Issue every load of this thread first (8 rows), then compute.
-  Block4<BF16> blk[kIters];
+  // every load of this lane first (kRowsPerWave rows), unconditionally from
+  // clamped in-bounds addresses (rows past n and superblocks past K repeat the
+  // last valid ones and are never stored), so all of them are in flight at once
+  constexpr int64_t kElem = BF16 ? 2 : 4;
+  const int64_t ccol = (gv ? g : nsb - 1) * kSuperblock + i * (4 * BPL);
+  LaneRaw<BF16, BPL> lw[kRowsPerWave];
 #pragma unroll
-  for (int it = 0; it < kIters; ++it) {
-    const int64_t row = row0 + wave * (2 * kIters) + 2 * it + half;
-    if (row < n) {
-      blk[it] = load_block<BF16>(w, row, k, col);
-    } else {
-      blk[it].v[0] = blk[it].v[1] = blk[it].v[2] = blk[it].v[3] = 0.f;
-    }
+  for (int it = 0; it < kRowsPerWave; ++it) {
+    const int64_t row = row0 + it < n ? row0 + it : n - 1;
+    lw[it] = load_lane<BF16, BPL>(reinterpret_cast<const char*>(w) + (row * k + ccol) * kElem);
   }
 
-  uint32_t* nib_plane = reinterpret_cast<uint32_t*>(packed);
-  uint32_t* sign_plane = reinterpret_cast<uint32_t*>(packed + nibble_plane_bytes(n, k));
+  // this lane's records of row row0 (+ it below): (superblock, row) record
+  // g * n + row; the scale or superblock sum likewise
+  const int64_t rec0 = g * n + row0;
+  uint32_t* nib_rec = reinterpret_cast<uint32_t*>(packed) + rec0 * 4;
+  uint32_t* sgn_rec = reinterpret_cast<uint32_t*>(packed + (DENSE ? 0 : nibble_plane_bytes(n, k))) + rec0;
+  float* al_rec = alpha_direct + rec0;
+  float* sum_rec = sb_sums + row0 * nsb + g;
 
 #pragma unroll
-  for (int it = 0; it < kIters; ++it) {
-    const int64_t row = row0 + wave * (2 * kIters) + 2 * it + half;
+  for (int it = 0; it < kRowsPerWave; ++it) {
+    const int64_t row = row0 + it;
+    const bool valid = gv && row < n;
+    uint32_t code[BPL];
+    float bs[BPL];
+    float wv[BPL][4];
+#pragma unroll
+    for (int j = 0; j < BPL; ++j) {
+      block_values<BF16, BPL>(lw[it], j, wv[j]);
+      code[j] = quantize_block(wv[j], bs[j]);
+    }
+
+    // superblock sum: tree levels inside the lane, then across the L lanes
     float sum;
-    const uint32_t code = quantize_block(blk[it].v, sum);
-
-    // sign plane: bit j of the dword = sign bit of block j
-    const unsigned long long ballot = __ballot((code >> 4) & 1u);
-    const uint32_t sign_word = (uint32_t)(ballot >> (32 * half));
-
-    // nibble dword (j & 7) >> 1: block 2d + h + 8b sits at bit 4h + 8b
-    uint32_t nib = (code & 15u) << (4 * (j & 1) + 8 * (j >> 3));
-    nib |= __shfl_xor(nib, 1);
-    nib |= __shfl_xor(nib, 8);
-    nib |= __shfl_xor(nib, 16);
-
-    // pairwise tree over the 32 blocks of the superblock
-    sum += __shfl_xor(sum, 1);
-    sum += __shfl_xor(sum, 2);
-    sum += __shfl_xor(sum, 4);
-    sum += __shfl_xor(sum, 8);
-    sum += __shfl_xor(sum, 16);
+    if constexpr (BPL == 2) sum = bs[0] + bs[1];
+    else sum = (bs[0] + bs[1]) + (bs[BPL - 2] + bs[BPL - 1]);
+    sum += dpp<kShr1>(sum);
+    sum += dpp<kShr2>(sum);
+    sum += dpp<kShr4>(sum);
+    if constexpr (L == 16) sum += dpp<kShr8>(sum);
 
     if constexpr (DENSE != 0) {
-      // every lane holds the superblock's sum after the butterfly
-      const float a = (float)((double)sum / 96.0);
-      if (row < n) {
-        if (j == 3) alpha_direct[g * n + row] = a;
-        const uint32_t z = (code >> 2) & 3u;
-        float f[4];
+      // every lane needs the scale: broadcast the group's last lane
+      const float total = __int_as_float(
+          __builtin_amdgcn_ds_swizzle(__float_as_int(sum), L == 16 ? kSwzLast16 : kSwzLast8));
+      const float a = (float)((double)total / 96.0);
+      if (valid) {
+        if (i == L - 1) al_rec[it] = a;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) f[i] = (uint32_t)i == z ? 0.f : (blk[it].v[i] > 0.f ? a : -a);
-        if constexpr (DENSE == SHERRY_F32 + 1) {
-          *reinterpret_cast<float4*>(reinterpret_cast<float*>(dense) + row * k + col) =
-              make_float4(f[0], f[1], f[2], f[3]);
-        } else {
-          uint2 v;
-          v.x = (uint32_t)f32_to_bf16_rne(f[0]) | ((uint32_t)f32_to_bf16_rne(f[1]) << 16);
-          v.y = (uint32_t)f32_to_bf16_rne(f[2]) | ((uint32_t)f32_to_bf16_rne(f[3]) << 16);
-          *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(dense) + row * k + col) = v;
+        for (int j = 0; j < BPL; ++j) {
+          const uint32_t z = (code[j] >> 2) & 3u;
+          float f[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) f[e] = (uint32_t)e == z ? 0.f : (wv[j][e] > 0.f ? a : -a);
+          const int64_t off = row * k + col + 4 * j;
+          if constexpr (DENSE == SHERRY_F32 + 1) {
+            *reinterpret_cast<float4*>(reinterpret_cast<float*>(dense) + off) = make_float4(f[0], f[1], f[2], f[3]);
+          } else {
+            uint2 v;
+            v.x = (uint32_t)f32_to_bf16_rne(f[0]) | ((uint32_t)f32_to_bf16_rne(f[1]) << 16);
+            v.y = (uint32_t)f32_to_bf16_rne(f[2]) | ((uint32_t)f32_to_bf16_rne(f[3]) << 16);
+            *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(dense) + off) = v;
+          }
         }
       }
       continue;
     }
-    if (row < n) {
-      const int64_t rec = g * n + row;  // (superblock, row) record index
-      if (j < 8 && (j & 1) == 0) nib_plane[rec * 4 + (j >> 1)] = nib;
-      if (j == 1) sign_plane[rec] = sign_word;
-      if (j == 3) {
-        if (alpha_direct) {
-          alpha_direct[g * n + row] = (float)((double)sum / 96.0);
-        } else {
-          sb_sums[row * nsb + g] = sum;
-        }
+
+    // sign dword: bit b of superblock = sign bit of block b
+    uint32_t sgn = 0;
+#pragma unroll
+    for (int j = 0; j < BPL; ++j) sgn |= ((code[j] >> 4) & 1u) << j;
+    sgn <<= BPL * i;
+    sgn |= dpp<kShr1>(sgn);
+    sgn |= dpp<kShr2>(sgn);
+    sgn |= dpp<kShr4>(sgn);
+    if constexpr (L == 16) sgn |= dpp<kShr8>(sgn);
+
+    // nibble dword d holds blocks 2d + 8b (low nibble of byte b) and 2d + 1 + 8b
+    if constexpr (BPL == 2) {
+      // lane i holds byte i >> 2 of dword i & 3
+      uint32_t d = ((code[0] & 15u) | ((code[1] & 15u) << 4)) << (8 * (i >> 2));
+      d |= dpp<kRor4>(d);
+      d |= dpp<kRor8>(d);
+      if (valid && i < 4) nib_rec[it * 4 + i] = d;
+    } else {
+      // lane i holds byte i >> 1 of dwords 2 (i & 1) and 2 (i & 1) + 1
+      uint32_t d0 = ((code[0] & 15u) | ((code[1] & 15u) << 4)) << (8 * (i >> 1));
+      uint32_t d1 = ((code[BPL - 2] & 15u) | ((code[BPL - 1] & 15u) << 4)) << (8 * (i >> 1));
+      d0 |= dpp<kQuadXor2>(d0);
+      d1 |= dpp<kQuadXor2>(d1);
+      d0 |= (uint32_t)__builtin_amdgcn_ds_swizzle((int)d0, kSwzXor4);
+      d1 |= (uint32_t)__builtin_amdgcn_ds_swizzle((int)d1, kSwzXor4);
+      if (valid && i < 2) *reinterpret_cast<uint2*>(nib_rec + it * 4 + 2 * i) = make_uint2(d0, d1);
+    }
+    if (valid && i == L - 1) {
+      sgn_rec[it] = sgn;
+      if (alpha_direct) {
+        al_rec[it] = (float)((double)sum / 96.0);
+      } else {
+        sum_rec[it * nsb] = sum;
       }
     }
   }
@@ -285,6 +361,13 @@ __global__ __launch_bounds__(256) void tree_level_kernel(const float* __restrict
   }
 }
 
+// Grid: x = groups of 2*BPL superblocks, y = tiles of kRowsPerWg rows, so
+// consecutive workgroups read adjacent spans of the same rows.
+inline dim3 quantize_grid(int64_t n, int64_t nsb) {
+  constexpr int spw = 2 * SHERRY_Q_BPL;
+  return dim3((unsigned)((nsb + spw - 1) / spw), (unsigned)((n + kRowsPerWg - 1) / kRowsPerWg));
+}
+
 }  // namespace
 
 QuantizePlan plan_quantize(int64_t n, int64_t k, int gran, int group_size) {
@@ -305,12 +388,14 @@ hipError_t launch_quantize_pack(const QuantizePlan& p, int64_t n, int64_t k, int
                                 int group_size, const void* w, bool w_bf16, uint8_t* packed,
                                 float* alpha, float* ws, hipStream_t s) {
   const int64_t nsb = k / kSuperblock;
-  dim3 grid((unsigned)nsb, (unsigned)((n + kRowsPerTile - 1) / kRowsPerTile));
+  const dim3 grid = quantize_grid(n, nsb);
   float* direct = p.direct_alpha ? alpha : nullptr;
   if (w_bf16) {
-    hipLaunchKernelGGL(quantize_pack_kernel<true>, grid, dim3(256), 0, s, w, n, k, packed, direct, ws);
+    hipLaunchKernelGGL((quantize_pack_kernel<true, 0, SHERRY_Q_BPL>), grid, dim3(256), 0, s, w, n, k, packed,
+                       direct, ws, nullptr);
   } else {
-    hipLaunchKernelGGL(quantize_pack_kernel<false>, grid, dim3(256), 0, s, w, n, k, packed, direct, ws);
+    hipLaunchKernelGGL((quantize_pack_kernel<false, 0, SHERRY_Q_BPL>), grid, dim3(256), 0, s, w, n, k, packed,
+                       direct, ws, nullptr);
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || p.direct_alpha) return e;
@@ -364,9 +449,10 @@ hipError_t launch_fake_quant(const FakeQuantPlan& p, int64_t n, int64_t k, int g
                              uint8_t* ws, hipStream_t s) {
   if (p.fused) {
     const int64_t nsb = k / kSuperblock;
-    dim3 grid((unsigned)nsb, (unsigned)((n + kRowsPerTile - 1) / kRowsPerTile));
-#define SHERRY_FQ(B, D) \
-  hipLaunchKernelGGL((quantize_pack_kernel<B, D>), grid, dim3(256), 0, s, w, n, k, nullptr, alpha, nullptr, out)
+    const dim3 grid = quantize_grid(n, nsb);
+#define SHERRY_FQ(B, D)                                                                                  \
+  hipLaunchKernelGGL((quantize_pack_kernel<B, D, SHERRY_Q_BPL>), grid, dim3(256), 0, s, w, n, k, nullptr, \
+                     alpha, nullptr, out)
     if (w_bf16) {
       if (out_dtype == SHERRY_F32) SHERRY_FQ(true, SHERRY_F32 + 1); else SHERRY_FQ(true, SHERRY_BF16 + 1);
     } else {

@@ -21,35 +21,63 @@ namespace {
 #define SHERRY_Q_BPL 2  // blocks per lane
 #endif
 
-// Quantize one block: returns the 5-bit code, and the kept-|w| sum of the
-// block as a two-level pairwise tree ((a0 + a1) + (a2 + a3)) with the zeroed
-// weight contributing +0.
-//
-// The zero position (first index of the minimum |w|) is a tournament: the
-// smaller of each pair (ties keep the lower index), then the smaller of the
-// two winners (ties keep the left pair).  The pair holding the zero sums to
-// its other member, the larger one (x + 0 = x exactly), so each half of the
-// tree is an add or a max.  The kept positions are then k0 < k1 < k2 =
-// (other of 0/1, 2, 3) when the zero is in the left pair, else (0, 1, other
-// of 2/3); the per-lane booleans stay lane masks until the code is built.
-__device__ inline uint32_t quantize_block(const float v[4], float& kept_sum) {
+// Zero position and kept-|w| sum of one block.  The zero is the first index
+// of the minimum |w|, found as a tournament: the smaller of each pair (ties
+// keep the lower index), then the smaller of the two winners (ties keep the
+// left pair).  The kept-|w| sum is the two-level pairwise tree ((a0 + a1) +
+// (a2 + a3)) with the zeroed weight contributing +0; the pair holding the
+// zero sums to its other member, the larger one (x + 0 = x exactly), so each
+// half of the tree is an add or a pick.
+__device__ inline uint32_t block_zero(const float v[4], float& kept_sum) {
   const float a0 = fabsf(v[0]), a1 = fabsf(v[1]), a2 = fabsf(v[2]), a3 = fabsf(v[3]);
   const bool c01 = a1 < a0;  // zero candidate of the left pair is 1 (and a0 is its larger)
   const bool c23 = a3 < a2;  // ... of the right pair is 3 (and a2 is its larger)
   const float m01 = c01 ? a1 : a0, m23 = c23 ? a3 : a2;
   const bool c = m23 < m01;  // the zero is in the right pair
-  const uint32_t z = c ? (c23 ? 3u : 2u) : (c01 ? 1u : 0u);
   const float left = c ? a0 + a1 : (c01 ? a0 : a1);
   const float right = c ? (c23 ? a2 : a3) : a2 + a3;
   kept_sum = left + right;
-  const bool pos0 = v[0] > 0.f, pos1 = v[1] > 0.f, pos2 = v[2] > 0.f, pos3 = v[3] > 0.f;
-  const bool q0 = c ? pos0 : (c01 ? pos0 : pos1);  // sign of the first kept weight
-  const bool q1 = c ? pos1 : pos2;                 // second
-  const bool q2 = c ? (c23 ? pos2 : pos3) : pos3;  // third
-  const uint32_t s = q0 ? 0u : 1u;                 // 1 when the first kept weight is negative
-  const uint32_t p0 = q1 != q0 ? 1u : 0u;          // second kept sign differs from the first
-  const uint32_t p1 = q2 != q0 ? 1u : 0u;          // third kept sign differs from the first
-  return (s << 4) | (z << 2) | (p1 << 1) | p0;
+  return c ? (c23 ? 3u : 2u) : (c01 ? 1u : 0u);
+}
+
+// The code of a block from its zero position z and positive mask (bit i =
+// weight i > 0): the kept positions k0 < k1 < k2 are all but z; s = the first
+// kept weight is not positive, p0 / p1 = the second / third kept weight's
+// sign differs from the first.  code = s<<4 | z<<2 | p1<<1 | p0.
+__device__ inline uint32_t block_code(uint32_t z, uint32_t pos) {
+  uint32_t k[3], r = 0;
+  for (uint32_t i = 0; i < 4; ++i)
+    if (i != z) k[r++] = i;
+  const uint32_t q0 = (pos >> k[0]) & 1u, q1 = (pos >> k[1]) & 1u, q2 = (pos >> k[2]) & 1u;
+  return ((q0 ^ 1u) << 4) | (z << 2) | ((q2 ^ q0) << 1) | (q1 ^ q0);
+}
+
+// Lookup index of a block: z << 4 | pos', where pos' holds the positive flags
+// of weights 0, 2, 1, 3 in bits 0..3 (the order the bf16 path produces them).
+__device__ inline uint32_t code_index(uint32_t z, uint32_t pos_perm) { return (z << 4) | pos_perm; }
+__device__ inline uint32_t unpermute_pos(uint32_t pp) {
+  return (pp & 1u) | ((pp >> 1) & 1u) << 2 | ((pp >> 2) & 1u) << 1 | ((pp >> 3) & 1u) << 3;
+}
+
+// pos' of a block of 4 bf16 weights held as dwords d0 = w0 | w1 << 16 and
+// d1 = w2 | w3 << 16: clamp each 16-bit weight (as a signed integer) to [0, 1]
+// -- 1 exactly for the positive ones (sign clear, not zero) -- then fold the
+// four flags into one nibble.  The clamps are written as packed 16-bit
+// instructions (register operands only): the compiler would otherwise split
+// them into per-half compares and selects.
+__device__ inline uint32_t pos_perm_bf16(uint32_t d0, uint32_t d1) {
+  uint32_t t01, t23;
+  asm("v_pk_min_i16 %0, %2, %4\n"
+      "v_pk_min_i16 %1, %3, %4\n"
+      "v_pk_max_i16 %0, %0, 0\n"
+      "v_pk_max_i16 %1, %1, 0"
+      : "=&v"(t01), "=&v"(t23)
+      : "v"(d0), "v"(d1), "v"(0x00010001u));
+  const uint32_t sum = t01 + (t23 << 1);  // pos0 + 2 pos2 | (pos1 + 2 pos3) << 16
+  return (sum & 3u) | (sum >> 14);        // pos0 | pos2 << 1 | pos1 << 2 | pos3 << 3
+}
+__device__ inline uint32_t pos_perm_f32(const float v[4]) {
+  return (v[0] > 0.f ? 1u : 0u) | (v[2] > 0.f ? 2u : 0u) | (v[1] > 0.f ? 4u : 0u) | (v[3] > 0.f ? 8u : 0u);
 }
 
 // Cross-lane moves inside a row of 16 lanes (DPP): row_shr:n gives lane i
@@ -63,6 +91,19 @@ __device__ inline float dpp(float v) {
   return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
 }
 constexpr int kShr1 = 0x111, kShr2 = 0x112, kShr4 = 0x114, kShr8 = 0x118, kRor4 = 0x124, kRor8 = 0x128;
+// row_shl:n (lane i gets lane i + n of its row) for n = 1..7
+template <typename T>
+__device__ inline T dpp_shl(T v, int n) {
+  switch (n) {
+    case 1: return dpp<0x101>(v);
+    case 2: return dpp<0x102>(v);
+    case 3: return dpp<0x103>(v);
+    case 4: return dpp<0x104>(v);
+    case 5: return dpp<0x105>(v);
+    case 6: return dpp<0x106>(v);
+    default: return dpp<0x107>(v);
+  }
+}
 constexpr int kQuadXor2 = 0x4E;  // quad_perm [2, 3, 0, 1]
 // ds_swizzle patterns (bit mode, groups of 32 lanes): lane ^ 4, and the last
 // lane of each group of 16 / 8
@@ -132,6 +173,11 @@ __global__ __launch_bounds__(256) void quantize_pack_kernel(
   const int64_t col = g * kSuperblock + i * (4 * BPL);
   const int64_t row0 = (int64_t)blockIdx.y * kRowsPerWg + wave * kRowsPerWave;
 
+  // code of every (zero position, positive flags) pair
+  __shared__ uint8_t code_tab[64];
+  if (DENSE == 0 && threadIdx.x < 64)
+    code_tab[threadIdx.x] = (uint8_t)block_code(threadIdx.x >> 4, unpermute_pos(threadIdx.x & 15));
+
   // every load of this lane first (kRowsPerWave rows), unconditionally from
   // clamped in-bounds addresses (rows past n and superblocks past K repeat the
   // last valid ones and are never stored), so all of them are in flight at once
@@ -147,11 +193,14 @@ __global__ __launch_bounds__(256) void quantize_pack_kernel(
   // this lane's records of row row0 (+ it below): (superblock, row) record
   // g * n + row; the scale or superblock sum likewise
   const int64_t rec0 = g * n + row0;
+  if constexpr (DENSE == 0) __syncthreads();  // the code table is written
   uint32_t* nib_rec = reinterpret_cast<uint32_t*>(packed) + rec0 * 4;
   uint32_t* sgn_rec = reinterpret_cast<uint32_t*>(packed + (DENSE ? 0 : nibble_plane_bytes(n, k))) + rec0;
   float* al_rec = alpha_direct + rec0;
   float* sum_rec = sb_sums + row0 * nsb + g;
 
+  float sums[kRowsPerWave];
+  uint32_t sgns[kRowsPerWave];
 #pragma unroll
   for (int it = 0; it < kRowsPerWave; ++it) {
     const int64_t row = row0 + it;
@@ -162,7 +211,19 @@ __global__ __launch_bounds__(256) void quantize_pack_kernel(
 #pragma unroll
     for (int j = 0; j < BPL; ++j) {
       block_values<BF16, BPL>(lw[it], j, wv[j]);
-      code[j] = quantize_block(wv[j], bs[j]);
+      const uint32_t z = block_zero(wv[j], bs[j]);
+      if constexpr (DENSE != 0) {
+        code[j] = z << 2;  // only the zero position is used
+      } else {
+        uint32_t pp;
+        if constexpr (BF16) {
+          const uint4 u = lw[it].q[j >> 1];
+          pp = pos_perm_bf16((j & 1) ? u.z : u.x, (j & 1) ? u.w : u.y);
+        } else {
+          pp = pos_perm_f32(wv[j]);
+        }
+        code[j] = code_tab[code_index(z, pp)];
+      }
     }
 
     // superblock sum: tree levels inside the lane, then across the L lanes
@@ -228,12 +289,29 @@ __global__ __launch_bounds__(256) void quantize_pack_kernel(
       d1 |= (uint32_t)__builtin_amdgcn_ds_swizzle((int)d1, kSwzXor4);
       if (valid && i < 2) *reinterpret_cast<uint2*>(nib_rec + it * 4 + 2 * i) = make_uint2(d0, d1);
     }
-    if (valid && i == L - 1) {
-      sgn_rec[it] = sgn;
+    sums[it] = sum;
+    sgns[it] = sgn;
+  }
+  if constexpr (DENSE == 0) {
+    // Lane L-1-it of each group collects row it's superblock sum and sign
+    // dword (both sit in lane L-1), so one division and one store of each
+    // serve all the rows.
+    static_assert(kRowsPerWave <= L && kRowsPerWave <= 8, "rows gathered by row_shl");
+    float sv = sums[0];
+    uint32_t sg = sgns[0];
+#pragma unroll
+    for (int it = 1; it < kRowsPerWave; ++it) {
+      const float sh = dpp_shl(sums[it], it);
+      const uint32_t gh = dpp_shl(sgns[it], it);
+      if (i == L - 1 - it) { sv = sh; sg = gh; }
+    }
+    const int rit = L - 1 - i;  // the row this lane now holds
+    if (gv && rit < kRowsPerWave && row0 + rit < n) {
+      sgn_rec[rit] = sg;
       if (alpha_direct) {
-        al_rec[it] = (float)((double)sum / 96.0);
+        al_rec[rit] = (float)((double)sv / 96.0);
       } else {
-        sum_rec[it * nsb] = sum;
+        sum_rec[rit * nsb] = sv;
       }
     }
   }

@@ -172,7 +172,7 @@ __global__ __launch_bounds__(kThreads, AR ? 1 : 3) void gemm_kernel(const uint8_
     __builtin_amdgcn_global_load_lds(const_cast<uint8_t*>(sgn_plane + sb * n * 4 + crow * 4),
                                      (lds_void*)(rb + kRecSgn), 4, 0, 0);
     if constexpr (C::kGroup)
-      __builtin_amdgcn_global_load_lds(const_cast<float*>(alpha + (int64_t)((int)sb / group_sbs) * n + crow),
+      __builtin_amdgcn_global_load_lds(const_cast<float*>(alpha + (group_sbs == 1 ? sb : (int64_t)((int)sb / group_sbs)) * n + crow),
                                        (lds_void*)(rb + kRecAlpha), 4, 0, 0);
     if constexpr (AR) {
       // dense-weight tile: rows n0 .. n0+127 of W, copied like X (rows past n
@@ -262,6 +262,14 @@ __global__ __launch_bounds__(kThreads, AR ? 1 : 3) void gemm_kernel(const uint8_
 
     const char* xb = XS(J);
     const char* dt = reinterpret_cast<const char*>(dtab);
+    // table offsets of the blocks this lane decodes, four per dword: byte cb
+    // of off_lo / off_hi = blocks 8cb + 2q / 8cb + 2q + 1 of the superblock
+    uint32_t off_lo[kTN], off_hi[kTN];
+#pragma unroll
+    for (int i = 0; i < kTN; ++i) {
+      off_lo[i] = quad_offsets8(nd[i], sg[i], 2 * q);
+      off_hi[i] = quad_offsets8(nd[i], sg[i], 2 * q + 1);
+    }
     auto mma = [&](auto zero_c) {
 #pragma unroll
       for (int kk = 0; kk < kStageK / 32; ++kk) {
@@ -272,12 +280,8 @@ __global__ __launch_bounds__(kThreads, AR ? 1 : 3) void gemm_kernel(const uint8_
         bf16x8 a[kTN];
 #pragma unroll
         for (int i = 0; i < kTN; ++i) {
-          const uint32_t byte = __builtin_amdgcn_ubfe(nd[i], 8 * cb, 8);
-          const uint32_t s2 = __builtin_amdgcn_ubfe(sg[i], 8 * cb + 2 * q, 2);
-          const uint32_t lo = ((byte & 15u) | ((s2 & 1u) << 4)) * 8u;
-          const uint32_t hi = ((byte >> 4) | ((s2 >> 1) << 4)) * 8u;
-          const uint2 wl = *reinterpret_cast<const uint2*>(dt + lo);
-          const uint2 wh = *reinterpret_cast<const uint2*>(dt + hi);
+          const uint2 wl = *reinterpret_cast<const uint2*>(dt + __builtin_amdgcn_ubfe(off_lo[i], 8 * cb, 8));
+          const uint2 wh = *reinterpret_cast<const uint2*>(dt + __builtin_amdgcn_ubfe(off_hi[i], 8 * cb, 8));
           a[i] = __builtin_bit_cast(bf16x8, u32x4{wl.x, wl.y, wh.x, wh.y});
         }
         const int ch = kk * 4 + q;

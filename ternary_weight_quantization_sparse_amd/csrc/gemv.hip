@@ -302,15 +302,6 @@ template <int XR> constexpr int kXChunkOf = XR == 4 ? SHERRY_XCHUNK_SMALL : 4;
 template <int XR> constexpr int kXPitchOf = kXChunkOf<XR> * kSuperblock * 2 + 16;
 constexpr int kMRecNib = 0, kMRecSgn = 1024, kMRecAlpha = 1280;
 
-// Byte offsets (code * 8) of the blocks of quad q = 2d + h of a superblock
-// (blocks q + 8b, b = 0..3, in byte b): nibble dword d, half h, sign bits
-// q + 8b moved to bit 7 of byte b.
-__device__ inline uint32_t quad_offsets8(uint32_t nib_dword, uint32_t sign_word, int q) {
-  const uint32_t nq = (q & 1) ? (nib_dword >> 1) : (nib_dword << 3);
-  const uint32_t sq = (sign_word << (7 - q)) & 0x80808080u;
-  return __builtin_amdgcn_bitop3_b32(nq, sq, 0x78787878u, 0xEC);  // (nq & mask) | sq
-}
-
 template <int MODE, int XR, bool YBF16>
 __global__ __launch_bounds__(256) void gemv_mfma_kernel(
     const uint8_t* packed, const float* alpha, const uint16_t* __restrict__ x, void* __restrict__ y,

@@ -127,6 +127,15 @@ __device__ inline uint2 decode_bf16(uint32_t code) {
   return make_uint2(h[0] | (h[1] << 16), h[2] | (h[3] << 16));
 }
 
+// Byte offsets (code * 8, into a table of 8-byte entries) of the blocks of
+// quad q = 2d + h of a superblock record (blocks q + 8b, b = 0..3, in byte
+// b): nibble dword d, half h, sign bits q + 8b moved to bit 7 of byte b.
+__device__ inline uint32_t quad_offsets8(uint32_t nib_dword, uint32_t sign_word, int q) {
+  const uint32_t nq = (q & 1) ? (nib_dword >> 1) : (nib_dword << 3);
+  const uint32_t sq = (sign_word << (7 - q)) & 0x80808080u;
+  return __builtin_amdgcn_bitop3_b32(nq, sq, 0x78787878u, 0xEC);  // (nq & mask) | sq
+}
+
 // s_waitcnt with only a vmcnt limit (expcnt / lgkmcnt left at their maxima).
 template <int VM>
 __device__ inline void wait_vmcnt() {

@@ -4,25 +4,28 @@
 // F.linear with the dequantized ternary weight); activations stay bf16 (same
 // section, and the agihunt digest's limits paragraph).
 //
-// Tiling: a workgroup of 4 waves owns a 128 (m) x 128 (n) output tile; wave w
-// owns all 128 m and the 32 n starting at 32w, as 8 x 2 tiles of
+// Tiling: a workgroup of 4 waves owns a 64 (m) x 128 (n) output tile; wave w
+// owns all 64 m and the 32 n starting at 32w, as 4 x 2 tiles of
 // v_mfma_f32_16x16x32_bf16 with the weights as the A operand (MFMA row = n)
 // and the activations as B (MFMA column = m), so each lane's four
-// accumulators are four consecutive n of one output row.  Two workgroups
+// accumulators are four consecutive n of one output row.  Three workgroups
 // share a CU and run out of step, so one's copies and barrier waits overlap
-// the other's MFMAs.
+// the others' MFMAs.
 //
-// K loop: stages of 64 k (half a 128-weight superblock) in a three-deep ring.
-// The activation tile of a stage (128 rows x 128 bytes) is copied straight
-// from global memory into LDS by buffer loads (no registers), two stages
-// ahead; 16-byte chunks are XOR-swizzled so MFMA operand reads are
-// conflict-free.  The weights never sit in LDS as bf16: each lane loads the
-// nibble dword and sign dword of its two weight rows into registers (also two
-// stages ahead) and decodes its own A operands right before the MFMAs: byte
-// cb of nibble dword q holds the lookup nibbles of two consecutive blocks (8
-// consecutive k), and each nibble with its block's sign bit indexes a
-// 32-entry LDS table of the block's 4 bf16 weights {-1, 0, +1}.  One barrier
-// per stage publishes the copied activation tile.
+// K loop: stages of 128 k (one superblock) in a two-slot ring.  The
+// activation tile of a stage (64 rows x 256 bytes) is copied straight from
+// global memory into LDS by buffer loads (no registers) one stage ahead;
+// 16-byte chunks are XOR-swizzled so MFMA operand reads are conflict-free.
+// The weights never sit in LDS as bf16: each wave copies the nibble and sign
+// records of its 32 weight rows into the slot, reads its lane's two nibble
+// and sign dwords into registers at the end of the previous stage, and
+// decodes its own A operands right before the MFMAs: byte cb of nibble dword
+// q holds the lookup nibbles of two consecutive blocks (8 consecutive k), and
+// each nibble with its block's sign bit indexes a 32-entry LDS table of the
+// block's 4 bf16 weights {-1, 0, +1}.  One barrier per stage publishes the
+// copied tile; a stage of a whole superblock gives each wave 32 MFMAs between
+// barriers (stages of 64 k with a three-slot ring, the same LDS, ran 11-28%
+// slower).
 //
 // Scales: per_group keeps an fp32 accumulator set per group (the group's first
 // MFMA starts from zero) and adds alpha(n, group) * acc_g to the output
@@ -44,7 +47,7 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int kStageK = 64;                 // k per LDS stage
+constexpr int kStageK = 128;                // k per LDS stage: one superblock
 constexpr int kRowBytes = kStageK * 2;      // one LDS row: 64 bf16
 constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
@@ -58,23 +61,22 @@ constexpr int kGemmTM = 4;                  // MFMA tiles per wave along m: 64-r
 // 64 nibble records (16 B), 64 sign dwords, and for per_group 64 scales.
 constexpr int kRecNib = 0, kRecSgn = 64 * 16, kRecAlpha = kRecSgn + 64 * 4;
 
-// Activation LDS rows are 128 bytes = 8 chunks of 16 bytes; chunk c of row r
-// sits at physical chunk c ^ ((r >> 1) & 7).  An MFMA operand read (16 rows x
-// 4 chunks per quarter wave) then touches every bank once.
-__device__ inline int swz_key(int row) { return (row >> 1) & 7; }
+// Activation LDS rows are 256 bytes = 16 chunks of 16 bytes; chunk c of row r
+// sits at physical chunk c ^ (r & 15).  An MFMA operand read (a quarter wave:
+// 16 rows, one chunk) then touches every bank once.
+__device__ inline int swz_key(int row) { return row & 15; }
 __device__ inline int swz(int row, int ch) { return row * kRowBytes + ((ch ^ swz_key(row)) << 4); }
 
-// TM = MFMA tiles per wave along m: 8 (128-row tiles), or 4 (64-row tiles)
-// for per_group, whose second accumulator set would not fit otherwise.
+// TM = MFMA tiles per wave along m (4: 64-row tiles).
 // AR: the Arenas training forward, which adds lambda * X W^T over the dense
 // bf16 latent weight W in the same K loop.
 template <int GRAN, int TM, bool AR = false>
 struct GemmCfg {
   static constexpr bool kGroup = GRAN == SHERRY_PER_GROUP;
-  static constexpr int kWLoads = AR ? kBN / 8 / kWaves : 0;  // 1 KB dense-weight copies per wave per stage
+  static constexpr int kWLoads = AR ? kBN * kRowBytes / 1024 / kWaves : 0;  // 1 KB dense-weight copies per wave per stage
   static constexpr int kTM = TM;
   static constexpr int kBM = 16 * TM;              // rows of X per tile
-  static constexpr int kXLoads = kBM / 8 / kWaves;  // 1 KB activation copies per wave per stage
+  static constexpr int kXLoads = kBM * kRowBytes / 1024 / kWaves;  // 1 KB activation copies per wave per stage
   static constexpr int kRecWave = kRecAlpha + (kGroup ? 64 * 4 : 0);  // record bytes per wave
   // vector-memory operations per wave per stage: activation pieces, nibble
   // and sign records, and for per_group the scales
@@ -102,11 +104,11 @@ __global__ __launch_bounds__(kThreads, AR ? 1 : 3) void gemm_kernel(const uint8_
   // another.  Slot: activation tile, records, and for AR the dense-weight tile.
   constexpr int kWOff = kBM * kRowBytes + kRecWave * kWaves;
   constexpr int kSlot = kWOff + (AR ? kBN * kRowBytes : 0);
-  __shared__ __attribute__((aligned(16))) char sl0[kSlot], sl1[kSlot], sl2[kSlot];
+  __shared__ __attribute__((aligned(16))) char sl0[kSlot], sl1[kSlot];
   __shared__ __attribute__((aligned(16))) uint2 dtab[32];
 
   auto XS = [&](auto J) -> char* {
-    if constexpr (decltype(J)::value == 0) return sl0; else if constexpr (decltype(J)::value == 1) return sl1; else return sl2;
+    if constexpr (decltype(J)::value == 0) return sl0; else return sl1;
   };
   auto RC = [&](auto J) -> char* { return XS(J) + kBM * kRowBytes; };
   auto WT = [&](auto J) -> char* { return XS(J) + kWOff; };
@@ -126,7 +128,7 @@ __global__ __launch_bounds__(kThreads, AR ? 1 : 3) void gemm_kernel(const uint8_
   const int64_t n0 = (int64_t)tn * kBN;
   const int kz = blockIdx.y;
   const int64_t sb0 = (int64_t)kz * sb_per_split;  // first superblock of this split
-  const int stages = 2 * sb_per_split;
+  const int stages = sb_per_split;
 
   if (tid < 32) dtab[tid] = decode_bf16(tid);
 
@@ -135,17 +137,19 @@ __global__ __launch_bounds__(kThreads, AR ? 1 : 3) void gemm_kernel(const uint8_
   const uint8_t* nib_plane = packed;
   const uint8_t* sgn_plane = packed + nibble_plane_bytes(n, k);
 
-  // Activation copies: piece p (8 rows) of a stage goes to LDS bytes
-  // [1024p, 1024p + 1024); lane l of the copy fetches physical chunk l%8 of
-  // row 8p + l/8, i.e. logical chunk (l%8) ^ swz_key(row).  The key has a
-  // period of 16 rows, so the lane part of the offset depends only on the
-  // piece's parity.  Rows past m fall outside the buffer resource's range and
-  // read zeros (the host keeps (m + 128) * k * 2 below 2^31).
-  static_assert(kXLoads % 2 == 0, "pieces of one wave alternate parity");
-  uint32_t xlane[2];
+  // Activation copies: piece p (4 rows) of a stage goes to LDS bytes
+  // [1024p, 1024p + 1024); lane l of the copy fetches physical chunk l%16 of
+  // row 4p + l/16, i.e. logical chunk (l%16) ^ swz_key(row).  The key has a
+  // period of 16 rows, so the lane part of the offset depends only on p % 4.
+  // Rows past m fall outside the buffer resource's range and read zeros (the
+  // host keeps (m + 128) * k * 2 below 2^31).
+  constexpr int kRowsPerCopy = 1024 / kRowBytes;  // rows per 1 KB copy
+  static_assert(kXLoads % 4 == 0 && 16 % kRowsPerCopy == 0, "piece phases repeat every 16 rows");
+  uint32_t xlane[4];
 #pragma unroll
-  for (int p = 0; p < 2; ++p)
-    xlane[p] = (uint32_t)((lane >> 3) * k * 2) + (uint32_t)(((lane & 7) ^ swz_key(p * 8 + (lane >> 3))) * 16);
+  for (int p = 0; p < 4; ++p)
+    xlane[p] = (uint32_t)((lane >> 4) * k * 2) +
+               (uint32_t)(((lane & 15) ^ swz_key(p * kRowsPerCopy + (lane >> 4))) * 16);
   const uint32_t xbytes = (uint32_t)(m * k * 2);
   const uint32_t wbytes = AR ? (uint32_t)(n * k * 2) : 0u;
 
@@ -155,15 +159,15 @@ __global__ __launch_bounds__(kThreads, AR ? 1 : 3) void gemm_kernel(const uint8_
   crow = crow < n ? crow : n - 1;
 
   auto issue = [&](auto J, int st) {
-    const int64_t sb = sb0 + (st >> 1);
-    const uint32_t sbyte = (uint32_t)((sb * 2 + (st & 1)) * (kStageK * 2));
+    const int64_t sb = sb0 + st;
+    const uint32_t sbyte = (uint32_t)(sb * (kStageK * 2));
     const __amdgpu_buffer_rsrc_t xr = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<char*>(reinterpret_cast<const char*>(x)) + sbyte, (short)0, (int)(xbytes - sbyte), kBufferWord3);
     char* xb = XS(J);
 #pragma unroll
     for (int i = 0; i < kXLoads; ++i) {
       const int piece = wave * kXLoads + i;
-      const uint32_t voff = xlane[i & 1] + (uint32_t)((m0 + piece * 8) * k * 2);
+      const uint32_t voff = xlane[piece & 3] + (uint32_t)((m0 + piece * kRowsPerCopy) * k * 2);
       __builtin_amdgcn_raw_ptr_buffer_load_lds(xr, (lds_void*)(xb + piece * 1024), 16, voff, 0, 0, 0);
     }
     char* rb = RC(J) + wave * kRecWave;
@@ -183,7 +187,7 @@ __global__ __launch_bounds__(kThreads, AR ? 1 : 3) void gemm_kernel(const uint8_
 #pragma unroll
       for (int i = 0; i < C::kWLoads; ++i) {
         const int piece = wave * C::kWLoads + i;
-        const uint32_t voff = xlane[i & 1] + (uint32_t)((n0 + piece * 8) * k * 2);
+        const uint32_t voff = xlane[piece & 3] + (uint32_t)((n0 + piece * kRowsPerCopy) * k * 2);
         __builtin_amdgcn_raw_ptr_buffer_load_lds(wr, (lds_void*)(wb + piece * 1024), 16, voff, 0, 0, 0);
       }
     }
@@ -251,14 +255,13 @@ __global__ __launch_bounds__(kThreads, AR ? 1 : 3) void gemm_kernel(const uint8_
 
   // One stage: stage st sits in slot J = st % 3.
   auto stage = [&](auto J, int st) {
-    constexpr int j2 = (decltype(J)::value + 2) % 3;
-    const bool group_end = C::kGroup && (st & 1) == 1 && gpos + 1 == group_sbs;
-    // copies two stages ahead into slot j2 (consumed in the previous stage).
-    // Issued unconditionally, so every stage has the same number of memory
-    // operations in flight and the compiler's waits for the weight records
-    // stay two stages behind; past the end they repeat the last stage into a
-    // slot nobody reads.
-    issue(Slot<j2>{}, st + 2 < stages ? st + 2 : stages - 1);
+    constexpr int j2 = (decltype(J)::value + 1) % 2;
+    const bool group_end = C::kGroup && gpos + 1 == group_sbs;
+    // copies one stage ahead into slot j2 (read in the previous stage, which
+    // every wave has finished: it ended with a barrier).  Issued
+    // unconditionally; past the end they repeat the last stage into a slot
+    // nobody reads.
+    issue(Slot<j2>{}, st + 1 < stages ? st + 1 : stages - 1);
 
     const char* xb = XS(J);
     const char* dt = reinterpret_cast<const char*>(dtab);
@@ -276,7 +279,7 @@ __global__ __launch_bounds__(kThreads, AR ? 1 : 3) void gemm_kernel(const uint8_
         // byte cb of nibble dword q: blocks 8cb + 2q (low nibble) and
         // 8cb + 2q + 1 (high) = k 32cb + 8q .. +7 of the superblock, which is
         // chunk q of k-step kk of this stage
-        const int cb = 2 * (st & 1) + kk;
+        const int cb = kk;
         bf16x8 a[kTN];
 #pragma unroll
         for (int i = 0; i < kTN; ++i) {
@@ -310,14 +313,14 @@ __global__ __launch_bounds__(kThreads, AR ? 1 : 3) void gemm_kernel(const uint8_
         }
       }
     };
-    if (C::kGroup && (st & 1) == 0 && gpos == 0) {
+    if (C::kGroup && gpos == 0) {
       mma(std::true_type{});
     } else {
       mma(std::false_type{});
     }
 
     if constexpr (C::kGroup) {
-      if ((st & 1) == 1) {
+      {
         if (group_end) {
           // the group's scales came with this stage's copies
 #pragma unroll
@@ -335,30 +338,26 @@ __global__ __launch_bounds__(kThreads, AR ? 1 : 3) void gemm_kernel(const uint8_
       }
     }
 
-    // this wave's copies of stage st+1 (issued one stage ago) have landed;
-    // only this stage's copies may still be in flight
-    wait_vmcnt<C::VM_PER_STAGE>();
-    read_records(Slot<(decltype(J)::value + 1) % 3>{});
+    // this wave's copies of stage st+1 (issued at the start of this stage)
+    // have landed; the barrier then publishes every wave's
+    wait_vmcnt<0>();
+    read_records(Slot<j2>{});
     lds_barrier();
   };
 
-  // prologue: stages 0 and 1 in flight, stage 0 landed
+  // prologue: stage 0 landed
   issue(Slot<0>{}, 0);
-  issue(Slot<1>{}, stages > 1 ? 1 : 0);
-  wait_vmcnt<C::VM_PER_STAGE>();
+  wait_vmcnt<0>();
   read_records(Slot<0>{});
   lds_barrier();  // decode table and stage 0 visible
 
   // (every early exit leaves the loop, so each path into a stage passes
-  // through the stage before it: that keeps the compiler's own waits for the
-  // weight records two stages behind)
-  for (int st = 0;; st += 3) {
+  // through the stage before it)
+  for (int st = 0;; st += 2) {
     stage(Slot<0>{}, st);
     if (st + 1 >= stages) break;
     stage(Slot<1>{}, st + 1);
     if (st + 2 >= stages) break;
-    stage(Slot<2>{}, st + 2);
-    if (st + 3 >= stages) break;
   }
   wait_vmcnt<0>();  // the trailing repeat copies have landed before the wave ends
 

@@ -55,11 +55,15 @@ constexpr int kTN = 2;                      // MFMA tiles per wave along n
 constexpr int kWN = 16 * kTN;               // 32 weight rows per wave
 constexpr int kBN = kWN * kWaves;           // 128 weight rows per tile
 constexpr int kMaxBM = 128;                 // largest activation tile (rows) the host chunking allows for
+#ifndef SHERRY_GEMM_SPLIT_TARGET
+#define SHERRY_GEMM_SPLIT_TARGET 512  // split K until a launch has this many workgroups
+#endif
 constexpr int kGemmTM = 4;                  // MFMA tiles per wave along m: 64-row tiles
-// Per-wave record area of a ring slot: lane l copies the records of weight
-// row 32 wave + l % 32 (lanes >= 32 duplicate, so the copies need no branch):
-// 64 nibble records (16 B), 64 sign dwords, and for per_group 64 scales.
-constexpr int kRecNib = 0, kRecSgn = 64 * 16, kRecAlpha = kRecSgn + 64 * 4;
+// Per-wave record area of a ring slot: lane l < 32 copies the records of
+// weight row 32 wave + l: 32 nibble records (16 B), 32 sign dwords, and for
+// per_group 32 scales (the other lanes sit the copies out, so the area stays
+// small enough for four workgroups per CU on per_channel / per_tensor).
+constexpr int kRecNib = 0, kRecSgn = 32 * 16, kRecAlpha = kRecSgn + 32 * 4;
 
 // Activation LDS rows are 256 bytes = 16 chunks of 16 bytes; chunk c of row r
 // sits at physical chunk c ^ (r & 15).  An MFMA operand read (a quarter wave:
@@ -77,7 +81,7 @@ struct GemmCfg {
   static constexpr int kTM = TM;
   static constexpr int kBM = 16 * TM;              // rows of X per tile
   static constexpr int kXLoads = kBM * kRowBytes / 1024 / kWaves;  // 1 KB activation copies per wave per stage
-  static constexpr int kRecWave = kRecAlpha + (kGroup ? 64 * 4 : 0);  // record bytes per wave
+  static constexpr int kRecWave = kRecAlpha + (kGroup ? 32 * 4 : 0);  // record bytes per wave
   // vector-memory operations per wave per stage: activation pieces, nibble
   // and sign records, and for per_group the scales
   static constexpr int VM_PER_STAGE = kXLoads + 2 + (kGroup ? 1 : 0) + kWLoads;
@@ -171,13 +175,16 @@ __global__ __launch_bounds__(kThreads, AR ? 1 : 3) void gemm_kernel(const uint8_
       __builtin_amdgcn_raw_ptr_buffer_load_lds(xr, (lds_void*)(xb + piece * 1024), 16, voff, 0, 0, 0);
     }
     char* rb = RC(J) + wave * kRecWave;
-    __builtin_amdgcn_global_load_lds(const_cast<uint8_t*>(nib_plane + sb * n * 16 + crow * 16),
-                                     (lds_void*)(rb + kRecNib), 16, 0, 0);
-    __builtin_amdgcn_global_load_lds(const_cast<uint8_t*>(sgn_plane + sb * n * 4 + crow * 4),
-                                     (lds_void*)(rb + kRecSgn), 4, 0, 0);
-    if constexpr (C::kGroup)
-      __builtin_amdgcn_global_load_lds(const_cast<float*>(alpha + (group_sbs == 1 ? sb : (int64_t)((int)sb / group_sbs)) * n + crow),
-                                       (lds_void*)(rb + kRecAlpha), 4, 0, 0);
+    if (lane < 32) {
+      __builtin_amdgcn_global_load_lds(const_cast<uint8_t*>(nib_plane + sb * n * 16 + crow * 16),
+                                       (lds_void*)(rb + kRecNib), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(const_cast<uint8_t*>(sgn_plane + sb * n * 4 + crow * 4),
+                                       (lds_void*)(rb + kRecSgn), 4, 0, 0);
+      if constexpr (C::kGroup)
+        __builtin_amdgcn_global_load_lds(
+            const_cast<float*>(alpha + (group_sbs == 1 ? sb : (int64_t)((int)sb / group_sbs)) * n + crow),
+            (lds_void*)(rb + kRecAlpha), 4, 0, 0);
+    }
     if constexpr (AR) {
       // dense-weight tile: rows n0 .. n0+127 of W, copied like X (rows past n
       // read zeros; the host keeps (n + 128) * k * 2 below 2^31)
@@ -500,7 +507,7 @@ GemmPlan plan_gemm(int64_t n, int64_t k, int gran, int group_size, int64_t m) {
   const int64_t mc = chunk > 0 && m > chunk ? chunk : m;
   const int64_t tiles = ((mc + p.tile_m - 1) / p.tile_m) * ((n + kBN - 1) / kBN);
   auto valid = [&](int64_t s) { return nsb % s == 0 && (nsb / s) % group_sbs == 0 && nsb / s >= 2; };
-  while (tiles * p.splits < 512 && p.splits < 8 && valid(2 * p.splits)) p.splits *= 2;
+  while (tiles * p.splits < SHERRY_GEMM_SPLIT_TARGET && p.splits < 8 && valid(2 * p.splits)) p.splits *= 2;
   p.workspace_bytes = p.splits > 1 ? (size_t)p.splits * (size_t)mc * (size_t)n * sizeof(float) : 0;
   return p;
 }

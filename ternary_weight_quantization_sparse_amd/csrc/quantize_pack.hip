@@ -91,7 +91,7 @@ __device__ inline float dpp(float v) {
   return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
 }
 constexpr int kShr1 = 0x111, kShr2 = 0x112, kShr4 = 0x114, kShr8 = 0x118, kRor4 = 0x124, kRor8 = 0x128;
-// row_shl:n (lane i gets lane i + n of its row) for n = 1..7
+// row_shl:n / row_shr:n (lane i gets lane i + n / i - n of its row), n = 1..7
 template <typename T>
 __device__ inline T dpp_shl(T v, int n) {
   switch (n) {
@@ -102,6 +102,18 @@ __device__ inline T dpp_shl(T v, int n) {
     case 5: return dpp<0x105>(v);
     case 6: return dpp<0x106>(v);
     default: return dpp<0x107>(v);
+  }
+}
+template <typename T>
+__device__ inline T dpp_shr(T v, int n) {
+  switch (n) {
+    case 1: return dpp<0x111>(v);
+    case 2: return dpp<0x112>(v);
+    case 3: return dpp<0x113>(v);
+    case 4: return dpp<0x114>(v);
+    case 5: return dpp<0x115>(v);
+    case 6: return dpp<0x116>(v);
+    default: return dpp<0x117>(v);
   }
 }
 constexpr int kQuadXor2 = 0x4E;  // quad_perm [2, 3, 0, 1]
@@ -201,6 +213,7 @@ __global__ __launch_bounds__(256) void quantize_pack_kernel(
 
   float sums[kRowsPerWave];
   uint32_t sgns[kRowsPerWave];
+  uint32_t zs[DENSE != 0 ? kRowsPerWave : 1];  // dense: the blocks' zero positions, 2 bits each
 #pragma unroll
   for (int it = 0; it < kRowsPerWave; ++it) {
     const int64_t row = row0 + it;
@@ -236,29 +249,11 @@ __global__ __launch_bounds__(256) void quantize_pack_kernel(
     if constexpr (L == 16) sum += dpp<kShr8>(sum);
 
     if constexpr (DENSE != 0) {
-      // every lane needs the scale: broadcast the group's last lane
-      const float total = __int_as_float(
-          __builtin_amdgcn_ds_swizzle(__float_as_int(sum), L == 16 ? kSwzLast16 : kSwzLast8));
-      const float a = (float)((double)total / 96.0);
-      if (valid) {
-        if (i == L - 1) al_rec[it] = a;
+      sums[it] = sum;
+      uint32_t zz = 0;  // zero position of block j in bits 2j, 2j+1
 #pragma unroll
-        for (int j = 0; j < BPL; ++j) {
-          const uint32_t z = (code[j] >> 2) & 3u;
-          float f[4];
-#pragma unroll
-          for (int e = 0; e < 4; ++e) f[e] = (uint32_t)e == z ? 0.f : (wv[j][e] > 0.f ? a : -a);
-          const int64_t off = row * k + col + 4 * j;
-          if constexpr (DENSE == SHERRY_F32 + 1) {
-            *reinterpret_cast<float4*>(reinterpret_cast<float*>(dense) + off) = make_float4(f[0], f[1], f[2], f[3]);
-          } else {
-            uint2 v;
-            v.x = (uint32_t)f32_to_bf16_rne(f[0]) | ((uint32_t)f32_to_bf16_rne(f[1]) << 16);
-            v.y = (uint32_t)f32_to_bf16_rne(f[2]) | ((uint32_t)f32_to_bf16_rne(f[3]) << 16);
-            *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(dense) + off) = v;
-          }
-        }
-      }
+      for (int j = 0; j < BPL; ++j) zz |= (code[j] >> 2) << (2 * j);
+      zs[it] = zz;
       continue;
     }
 
@@ -291,6 +286,45 @@ __global__ __launch_bounds__(256) void quantize_pack_kernel(
     }
     sums[it] = sum;
     sgns[it] = sgn;
+  }
+  if constexpr (DENSE != 0) {
+    // Lane L-1-it of each group collects row it's sum; one division gives
+    // every row's scale, which row_shr and a broadcast hand back to the group.
+    float sv = sums[0];
+#pragma unroll
+    for (int it = 1; it < kRowsPerWave; ++it) {
+      const float sh = dpp_shl(sums[it], it);
+      if (i == L - 1 - it) sv = sh;
+    }
+    const float av = (float)((double)sv / 96.0);
+    const int rit = L - 1 - i;
+    if (gv && rit < kRowsPerWave && row0 + rit < n) al_rec[rit] = av;
+#pragma unroll
+    for (int it = 0; it < kRowsPerWave; ++it) {
+      const float at = it == 0 ? av : dpp_shr(av, it);  // row it's scale in lane L-1
+      const float a = __int_as_float(
+          __builtin_amdgcn_ds_swizzle(__float_as_int(at), L == 16 ? kSwzLast16 : kSwzLast8));
+      const int64_t row = row0 + it;
+      if (!(gv && row < n)) continue;
+#pragma unroll
+      for (int j = 0; j < BPL; ++j) {
+        float wv[4];
+        block_values<BF16, BPL>(lw[it], j, wv);
+        const uint32_t z = (zs[it] >> (2 * j)) & 3u;
+        float f[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) f[e] = (uint32_t)e == z ? 0.f : (wv[e] > 0.f ? a : -a);
+        const int64_t off = row * k + col + 4 * j;
+        if constexpr (DENSE == SHERRY_F32 + 1) {
+          *reinterpret_cast<float4*>(reinterpret_cast<float*>(dense) + off) = make_float4(f[0], f[1], f[2], f[3]);
+        } else {
+          uint2 v;
+          v.x = (uint32_t)f32_to_bf16_rne(f[0]) | ((uint32_t)f32_to_bf16_rne(f[1]) << 16);
+          v.y = (uint32_t)f32_to_bf16_rne(f[2]) | ((uint32_t)f32_to_bf16_rne(f[3]) << 16);
+          *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(dense) + off) = v;
+        }
+      }
+    }
   }
   if constexpr (DENSE == 0) {
     // Lane L-1-it of each group collects row it's superblock sum and sign

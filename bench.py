@@ -577,6 +577,66 @@ def bench_quantize(dev, reps=10):
     return res
 
 
+def bench_unpack(dev, reps=20):
+    """Unpack / dequantize of an 8192x8192 per_group-128 weight to int8 T, bf16
+    and fp32 T*alpha.  Each dtype rotates over packed copies and outputs of
+    >= 1 GiB in total, so the writes reach HBM; bytes = packed planes (+ scales
+    for the scaled outputs) + the output."""
+    import numpy as np
+    import oracle as O
+    import workloads as WL
+    import ternary_weight_quantization_sparse_amd as S
+    torch = _torch()
+    n = k = 8192
+    bits, vals = WL.latent_weight_outliers_bf16(n, k, 5000)
+    pw = S.quantize_pack(dev_bf16(bits, dev), "per_group", 128)
+    t_ref = O.ternary(vals)
+    ref_a = O.alpha(vals, "per_group", 128)
+    rows = np.random.default_rng(11).choice(n, 64, replace=False)
+    lib = S.load()
+    res = {}
+    for name, od, esize in (("int8", S._lib.I8, 1), ("bfloat16", S._lib.BF16, 2), ("float32", S._lib.F32, 4)):
+        got = to_np(S.unpack(pw, name))
+        if name == "int8":
+            ok = bool(np.array_equal(got, t_ref))
+        else:
+            wq = O.dequant(t_ref[rows], ref_a[:, rows], "per_group", 128).astype(np.float32)
+            ok = bool(np.array_equal(got[rows], O.round_to_bf16_bits(wq)) if name == "bfloat16"
+                      else np.array_equal(got[rows].view(np.uint32), wq.view(np.uint32)))
+        del got
+        outs = [torch.empty(n * k * esize, dtype=torch.uint8, device=dev)
+                for _ in range(max(2, -(-GIB // (n * k * esize))))]
+        ins = [pw.packed] + [pw.packed.clone() for _ in range(7)]
+
+        def launch(i=[0]):
+            o, p_ = outs[i[0] % len(outs)], ins[i[0] % len(ins)]
+            i[0] += 1
+            S.check(lib.sherry_unpack(n, k, S._lib.PER_GROUP, 128, p_.data_ptr(), pw.alpha.data_ptr(),
+                                      o.data_ptr(), od, torch.cuda.current_stream().cuda_stream))
+        timed_launches([launch], reps, reps)
+        _, per, _ = timed_launches([launch], reps, 2)
+        t = float(np.median(per[0]))
+        nbytes = S.packed_bytes(n, k) + (0 if name == "int8" else 4 * pw.alpha.numel()) + n * k * esize
+        res[name] = {"exact": ok, "ms": t, "gbs": nbytes / (t * 1e-3) / 1e9,
+                     "frac_of_hbm_peak": nbytes / (t * 1e-3) / 1e9 / HBM_PEAK_GBS, "bytes": nbytes,
+                     "output_buffers": len(outs)}
+        log(f"[unpack] 8192x8192 -> {name}: exact={ok} {t * 1e3:.1f} us, {res[name]['gbs']:.0f} GB/s")
+        del outs, ins
+    # reference write rate at the int8 output's size: torch's fill of 64 MiB
+    # buffers, rotating over 1 GiB
+    bufs = [torch.empty(64 << 20, dtype=torch.uint8, device=dev) for _ in range(16)]
+
+    def fill(i=[0]):
+        bufs[i[0] % len(bufs)].fill_(1)
+        i[0] += 1
+    timed_launches([fill], reps, reps)
+    _, per, _ = timed_launches([fill], reps, 2)
+    t = float(np.median(per[0]))
+    res["torch_fill_64mib"] = {"ms": t, "gbs": (64 << 20) / (t * 1e-3) / 1e9}
+    log(f"[unpack] reference: torch fill of 64 MiB {t * 1e3:.1f} us, {res['torch_fill_64mib']['gbs']:.0f} GB/s")
+    return res
+
+
 def bench_gemv_3b(dev, batches, sweeps_per_replay=8, warm_replays=30, replays=20):
     import numpy as np
     import oracle as O
@@ -699,8 +759,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=50)
-    ap.add_argument("--sections", default="gemv,single,layer,compare,gemm,quantize,gemv3b,cpu",
-                    help="comma list of: gemv (always), single, layer, compare, gemm, quantize, gemv3b, cpu, "
+    ap.add_argument("--sections", default="gemv,single,layer,compare,gemm,quantize,unpack,gemv3b,cpu",
+                    help="comma list of: gemv (always), single, layer, compare, gemm, quantize, unpack, gemv3b, cpu, "
                          "copycal (a 1 GiB device copy for scaling HBM counters)")
     args = ap.parse_args()
     if args.gpus != 1:
@@ -727,6 +787,8 @@ def main():
         extra["gemm"] = bench_gemm(pws, dev, (512, 2048))
     if "quantize" in sections:
         extra["quantize"] = bench_quantize(dev)
+    if "unpack" in sections:
+        extra["unpack"] = bench_unpack(dev)
     if "gemv3b" in sections:
         extra["gemv_3b"] = bench_gemv_3b(dev, (1, 4, 16))
     if "copycal" in sections:

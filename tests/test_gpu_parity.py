@@ -140,6 +140,37 @@ def test_unpack(gran, g, n, k):
     assert np.array_equal(got_b, O.round_to_bf16_bits(wq))
 
 
+@pytest.mark.parametrize("gran", ["per_group", "per_tensor"])
+@pytest.mark.parametrize("n,k", [(1, 128), (9, 640), (33, 1152), (96, 512)])
+def test_unpack_edges(gran, n, k):
+    """Row counts off every rows-per-workgroup step (32, 16, 8), an odd number
+    of superblock columns, and all-zero rows / groups: their kept weights are
+    -1 with alpha 0, so T*alpha is -0.0 there."""
+    g = np.random.default_rng(n * 7 + k)
+    w = (g.integers(-2, 3, size=(n, k)) * 0.25).astype(np.float32)
+    w[0, :128] = 0.0
+    if n > 5:
+        w[5] = 0.0
+    pw, ref_a = check_quantize(dev_f32(w), w, gran)
+    t_ref = O.ternary(w)
+    assert np.array_equal(to_np(S.unpack(pw, "int8")), t_ref)
+    wq = O.dequant(t_ref, ref_a, gran, 128).astype(np.float32)
+    assert np.array_equal(to_np(S.unpack(pw, "float32")).view(np.uint32), wq.view(np.uint32))
+    assert np.array_equal(to_np(S.unpack(pw, "bfloat16")), O.round_to_bf16_bits(wq))
+
+
+def test_unpack_8192_bf16_outliers():
+    bits, vals = WL.latent_weight_outliers_bf16(8192, 8192, 5000)
+    pw = S.quantize_pack(dev_bf16(bits), "per_group", 128)
+    t_ref = O.ternary(vals)
+    assert np.array_equal(to_np(S.unpack(pw, "int8")), t_ref)
+    rows = np.random.default_rng(3).choice(8192, 48, replace=False)
+    ref_a = O.alpha(vals[rows], "per_group", 128)
+    wq = O.dequant(t_ref[rows], ref_a, "per_group", 128).astype(np.float32)
+    assert np.array_equal(to_np(S.unpack(pw, "float32"))[rows].view(np.uint32), wq.view(np.uint32))
+    assert np.array_equal(to_np(S.unpack(pw, "bfloat16"))[rows], O.round_to_bf16_bits(wq))
+
+
 # ------------------------------------------------------------------ gemv
 def gemv_case(n, k, wseed, xbits, xvals, gran="per_group", g=128, y_dtype="float32"):
     w = WL.latent_weight(n, k, wseed)

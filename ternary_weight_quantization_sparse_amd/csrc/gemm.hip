@@ -10,7 +10,9 @@
 // and the activations as B (MFMA column = m), so each lane's four
 // accumulators are four consecutive n of one output row.  Three workgroups
 // share a CU and run out of step, so one's copies and barrier waits overlap
-// the others' MFMAs.
+// the others' MFMAs.  Launches with enough tiles to fill the GPU at two per
+// CU use 64 x 256 tiles instead (4 x 4 MFMA tiles per wave: each activation
+// fragment read from LDS feeds four MFMAs, not two).
 //
 // K loop: stages of 128 k (one superblock) in a two-slot ring.  The
 // activation tile of a stage (64 rows x 256 bytes) is copied straight from
@@ -51,19 +53,14 @@ constexpr int kStageK = 128;                // k per LDS stage: one superblock
 constexpr int kRowBytes = kStageK * 2;      // one LDS row: 64 bf16
 constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
-constexpr int kTN = 2;                      // MFMA tiles per wave along n
-constexpr int kWN = 16 * kTN;               // 32 weight rows per wave
-constexpr int kBN = kWN * kWaves;           // 128 weight rows per tile
+#ifndef SHERRY_GEMM_WIDE_TILES
+#define SHERRY_GEMM_WIDE_TILES 512  // 256-wide weight tiles once a launch has this many of them
+#endif
 constexpr int kMaxBM = 128;                 // largest activation tile (rows) the host chunking allows for
 #ifndef SHERRY_GEMM_SPLIT_TARGET
 #define SHERRY_GEMM_SPLIT_TARGET 512  // split K until a launch has this many workgroups
 #endif
 constexpr int kGemmTM = 4;                  // MFMA tiles per wave along m: 64-row tiles
-// Per-wave record area of a ring slot: lane l < 32 copies the records of
-// weight row 32 wave + l: 32 nibble records (16 B), 32 sign dwords, and for
-// per_group 32 scales (the other lanes sit the copies out, so the area stays
-// small enough for four workgroups per CU on per_channel / per_tensor).
-constexpr int kRecNib = 0, kRecSgn = 32 * 16, kRecAlpha = kRecSgn + 32 * 4;
 
 // Activation LDS rows are 256 bytes = 16 chunks of 16 bytes; chunk c of row r
 // sits at physical chunk c ^ (r & 15).  An MFMA operand read (a quarter wave:
@@ -71,17 +68,27 @@ constexpr int kRecNib = 0, kRecSgn = 32 * 16, kRecAlpha = kRecSgn + 32 * 4;
 __device__ inline int swz_key(int row) { return row & 15; }
 __device__ inline int swz(int row, int ch) { return row * kRowBytes + ((ch ^ swz_key(row)) << 4); }
 
-// TM = MFMA tiles per wave along m (4: 64-row tiles).
+// TM = MFMA tiles per wave along m (4: 64-row tiles); TN = MFMA tiles per
+// wave along n (2: 32 weight rows per wave, 128 per workgroup; 4: 64 and
+// 256, twice the MFMAs per activation fragment read, for launches with
+// enough tiles to fill the GPU at two workgroups per CU).
 // AR: the Arenas training forward, which adds lambda * X W^T over the dense
 // bf16 latent weight W in the same K loop.
-template <int GRAN, int TM, bool AR = false>
+template <int GRAN, int TM, bool AR, int TN>
 struct GemmCfg {
   static constexpr bool kGroup = GRAN == SHERRY_PER_GROUP;
+  static constexpr int kTN = TN;
+  static constexpr int kWN = 16 * TN;              // weight rows per wave
+  static constexpr int kBN = kWN * kWaves;         // weight rows per tile
   static constexpr int kWLoads = AR ? kBN * kRowBytes / 1024 / kWaves : 0;  // 1 KB dense-weight copies per wave per stage
   static constexpr int kTM = TM;
   static constexpr int kBM = 16 * TM;              // rows of X per tile
   static constexpr int kXLoads = kBM * kRowBytes / 1024 / kWaves;  // 1 KB activation copies per wave per stage
-  static constexpr int kRecWave = kRecAlpha + (kGroup ? 32 * 4 : 0);  // record bytes per wave
+  // Per-wave record area of a ring slot: lane l < kWN copies the records of
+  // weight row kWN wave + l: kWN nibble records (16 B), kWN sign dwords, and
+  // for per_group kWN scales.
+  static constexpr int kRecNib = 0, kRecSgn = kWN * 16, kRecAlpha = kRecSgn + kWN * 4;
+  static constexpr int kRecWave = kRecAlpha + (kGroup ? kWN * 4 : 0);  // record bytes per wave
   // vector-memory operations per wave per stage: activation pieces, nibble
   // and sign records, and for per_group the scales
   static constexpr int VM_PER_STAGE = kXLoads + 2 + (kGroup ? 1 : 0) + kWLoads;
@@ -93,16 +100,18 @@ using Slot = std::integral_constant<int, J>;
 // grid: x = tiles (tiles_m * tiles_n), y = K splits.  partial == nullptr:
 // write bf16 Y; else write fp32 partial[split][m][n] (per_group already
 // scaled, per_channel / per_tensor not yet; AR: fully scaled).
-template <int GRAN, int TM, bool AR>
-__global__ __launch_bounds__(kThreads, AR ? 1 : 3) void gemm_kernel(const uint8_t* packed,
+template <int GRAN, int TM, bool AR, int TN>
+__global__ __launch_bounds__(kThreads, AR ? 1 : (TN == 4 ? 2 : 3)) void gemm_kernel(const uint8_t* packed,
                                                      const float* __restrict__ alpha,
                                                      const uint16_t* __restrict__ x,
                                                      uint16_t* __restrict__ y, float* __restrict__ partial,
                                                      int64_t n, int64_t k, int64_t m, int group_sbs,
                                                      int tiles_m, int tiles_n, int sb_per_split,
                                                      const uint16_t* __restrict__ wd, float lam) {
-  using C = GemmCfg<GRAN, TM, AR>;
+  using C = GemmCfg<GRAN, TM, AR, TN>;
   constexpr int kTM = C::kTM, kBM = C::kBM, kXLoads = C::kXLoads, kRecWave = C::kRecWave;
+  constexpr int kTN = C::kTN, kWN = C::kWN, kBN = C::kBN;
+  constexpr int kRecNib = C::kRecNib, kRecSgn = C::kRecSgn, kRecAlpha = C::kRecAlpha;
   // one __shared__ object per ring slot: the compiler's wait insertion then
   // knows an LDS read of one slot never aliases the copies in flight into
   // another.  Slot: activation tile, records, and for AR the dense-weight tile.
@@ -157,9 +166,9 @@ __global__ __launch_bounds__(kThreads, AR ? 1 : 3) void gemm_kernel(const uint8_
   const uint32_t xbytes = (uint32_t)(m * k * 2);
   const uint32_t wbytes = AR ? (uint32_t)(n * k * 2) : 0u;
 
-  // weight row whose records this lane copies: n0 + 32 wave + lane % 32
+  // weight row whose records this lane copies: n0 + kWN wave + lane % kWN
   // (clamped rows feed only outputs that are not stored)
-  int64_t crow = n0 + wave * kWN + (lane & 31);
+  int64_t crow = n0 + wave * kWN + (lane % kWN);
   crow = crow < n ? crow : n - 1;
 
   auto issue = [&](auto J, int st) {
@@ -175,7 +184,7 @@ __global__ __launch_bounds__(kThreads, AR ? 1 : 3) void gemm_kernel(const uint8_
       __builtin_amdgcn_raw_ptr_buffer_load_lds(xr, (lds_void*)(xb + piece * 1024), 16, voff, 0, 0, 0);
     }
     char* rb = RC(J) + wave * kRecWave;
-    if (lane < 32) {
+    if (lane < kWN) {
       __builtin_amdgcn_global_load_lds(const_cast<uint8_t*>(nib_plane + sb * n * 16 + crow * 16),
                                        (lds_void*)(rb + kRecNib), 16, 0, 0);
       __builtin_amdgcn_global_load_lds(const_cast<uint8_t*>(sgn_plane + sb * n * 4 + crow * 4),
@@ -201,37 +210,21 @@ __global__ __launch_bounds__(kThreads, AR ? 1 : 3) void gemm_kernel(const uint8_
   };
 
   // This lane's records of the next stage: nibble dword q and the sign dword
-  // of rows r and 16 + r of its wave's rows, and for per_group the scales of
-  // rows 4q .. 4q+3 and 16 + 4q .. .  Each wave copies its own records, so
+  // of rows r, 16 + r, ... of its wave's rows.  Each wave copies its own records, so
   // they are read right after its own wait for the copies, before the
   // barrier.  The reads are one asm block that waits for its own results:
   // the compiler cannot tell these LDS reads from ones that might overlap
   // copies still in flight and would otherwise wait for every copy.
-  static_assert(kTN == 2, "the record reads below cover two row tiles");
+  static_assert(kTN % 2 == 0, "the record reads below cover row tiles in pairs");
   uint32_t nd[kTN], sg[kTN];
-  f32x4 av[C::kGroup ? kTN : 1];
   auto read_records = [&](auto J) {
     const uint32_t rb = (uint32_t)(size_t)(__attribute__((address_space(3))) char*)(RC(J) + wave * kRecWave);
-    const uint32_t a_nib = rb + kRecNib + r * 16 + q * 4;
-    const uint32_t a_sgn = rb + kRecSgn + r * 4;
-    uint32_t n0v, n1v, s0v, s1v;
-    if constexpr (C::kGroup) {
-      const uint32_t a_al = rb + kRecAlpha + q * 16;
-      f32x4 a0v, a1v;
-      asm volatile(
-          "ds_read_b32 %0, %6\n"
-          "ds_read_b32 %1, %6 offset:256\n"
-          "ds_read_b32 %2, %7\n"
-          "ds_read_b32 %3, %7 offset:64\n"
-          "ds_read_b128 %4, %8\n"
-          "ds_read_b128 %5, %8 offset:64\n"
-          "s_waitcnt lgkmcnt(0)"
-          : "=&v"(n0v), "=&v"(n1v), "=&v"(s0v), "=&v"(s1v), "=&v"(a0v), "=&v"(a1v)
-          : "v"(a_nib), "v"(a_sgn), "v"(a_al)
-          : "memory");
-      av[0] = a0v;
-      av[C::kGroup ? 1 : 0] = a1v;
-    } else {
+#pragma unroll
+    for (int pr = 0; pr < kTN / 2; ++pr) {
+      // row tiles 2pr, 2pr + 1: 16 rows of 16 nibble bytes / 4 sign bytes each
+      const uint32_t a_nib = rb + kRecNib + pr * 512 + r * 16 + q * 4;
+      const uint32_t a_sgn = rb + kRecSgn + pr * 128 + r * 4;
+      uint32_t n0v, n1v, s0v, s1v;
       asm volatile(
           "ds_read_b32 %0, %4\n"
           "ds_read_b32 %1, %4 offset:256\n"
@@ -241,8 +234,8 @@ __global__ __launch_bounds__(kThreads, AR ? 1 : 3) void gemm_kernel(const uint8_
           : "=&v"(n0v), "=&v"(n1v), "=&v"(s0v), "=&v"(s1v)
           : "v"(a_nib), "v"(a_sgn)
           : "memory");
+      nd[2 * pr] = n0v; nd[2 * pr + 1] = n1v; sg[2 * pr] = s0v; sg[2 * pr + 1] = s1v;
     }
-    nd[0] = n0v; nd[1] = n1v; sg[0] = s0v; sg[1] = s1v;
   };
 
   f32x4 acc[kTN][kTM];
@@ -329,7 +322,25 @@ __global__ __launch_bounds__(kThreads, AR ? 1 : 3) void gemm_kernel(const uint8_
     if constexpr (C::kGroup) {
       {
         if (group_end) {
-          // the group's scales came with this stage's copies
+          // the group's scales came with this stage's copies and are still in
+          // its slot (the copies in flight go to the other one): scales of
+          // rows 4q .. 4q+3 of each row tile, read here rather than held in
+          // registers through the stage (which made the 256-row tiles spill)
+          const uint32_t rb = (uint32_t)(size_t)(__attribute__((address_space(3))) char*)(RC(J) + wave * kRecWave);
+          f32x4 av[kTN];
+#pragma unroll
+          for (int pr = 0; pr < kTN / 2; ++pr) {
+            f32x4 a0v, a1v;
+            asm volatile(
+                "ds_read_b128 %0, %2\n"
+                "ds_read_b128 %1, %2 offset:64\n"
+                "s_waitcnt lgkmcnt(0)"
+                : "=&v"(a0v), "=&v"(a1v)
+                : "v"(rb + kRecAlpha + pr * 128 + q * 16)
+                : "memory");
+            av[2 * pr] = a0v;
+            av[2 * pr + 1] = a1v;
+          }
 #pragma unroll
           for (int i = 0; i < kTN; ++i) {
 #pragma unroll
@@ -457,11 +468,11 @@ __global__ __launch_bounds__(256) void gemm_split_reduce(const float* __restrict
 // the end, stay below 2^31 bytes.
 int64_t gemm_chunk_rows(int64_t k) { return ((((int64_t)1 << 31) / (2 * k) - kMaxBM) / kMaxBM) * kMaxBM; }
 
-template <int GRAN, int TM, bool AR>
+template <int GRAN, int TM, bool AR, int TN>
 hipError_t launch_g(const GemmPlan& p, int64_t n, int64_t k, int group_sbs, const uint8_t* packed,
                     const float* alpha, const uint16_t* x, int64_t m, uint16_t* y, float* ws,
                     const uint16_t* wd, float lam, hipStream_t s) {
-  constexpr int kBM = GemmCfg<GRAN, TM, AR>::kBM;
+  constexpr int kBM = GemmCfg<GRAN, TM, AR, TN>::kBM, kBN = GemmCfg<GRAN, TM, AR, TN>::kBN;
   const int64_t chunk = gemm_chunk_rows(k);
   if (chunk < kMaxBM) return hipErrorInvalidValue;
   const int tiles_n = (int)((n + kBN - 1) / kBN);
@@ -471,7 +482,7 @@ hipError_t launch_g(const GemmPlan& p, int64_t n, int64_t k, int group_sbs, cons
   for (int64_t r0 = 0; r0 < m; r0 += chunk) {
     const int64_t mc = m - r0 < chunk ? m - r0 : chunk;
     const int tiles_m = (int)((mc + kBM - 1) / kBM);
-    hipLaunchKernelGGL((gemm_kernel<GRAN, TM, AR>), dim3((unsigned)(tiles_m * tiles_n), (unsigned)splits),
+    hipLaunchKernelGGL((gemm_kernel<GRAN, TM, AR, TN>), dim3((unsigned)(tiles_m * tiles_n), (unsigned)splits),
                        dim3(kThreads), 0, s, packed, alpha, x + r0 * k, y + r0 * n, splits > 1 ? ws : nullptr, n, k,
                        mc, group_sbs, tiles_m, tiles_n, sb_per_split, wd, lam);
     hipError_t e = hipGetLastError();
@@ -491,21 +502,32 @@ hipError_t launch_g(const GemmPlan& p, int64_t n, int64_t k, int group_sbs, cons
 
 }  // namespace
 
-// Splits of K for launches with few tiles: the smallest power of two (at most
-// 8) that brings the launch to 512 workgroups (two per CU), over whole groups
-// and at least two superblocks per split.  Measured on the LLaMA-3.2-1B
-// shapes at M = 512 and 2048, fuller launches gain nothing from splitting and
-// deeper splits lose to their shorter K loops and partial traffic.
-GemmPlan plan_gemm(int64_t n, int64_t k, int gran, int group_size, int64_t m) {
+// Tile width and splits of K.  Launches with at least SHERRY_GEMM_WIDE_TILES
+// tiles 256 weight rows wide (two per CU fill the GPU) use them: each
+// activation fragment read from LDS then feeds twice the MFMAs.  Others use
+// 128-row tiles and split K for launches with few tiles: the smallest power
+// of two (at most 8) that brings the launch to 512 workgroups (two per CU),
+// over whole groups and at least two superblocks per split.  Measured on the
+// LLaMA-3.2-1B shapes at M = 512 and 2048, fuller launches gain nothing from
+// splitting and deeper splits lose to their shorter K loops and partial
+// traffic.  The Arenas forward (`wide` false) keeps 128-row tiles: its dense
+// weight tile already fills the LDS of one workgroup per CU.
+GemmPlan plan_gemm(int64_t n, int64_t k, int gran, int group_size, int64_t m, bool wide) {
   GemmPlan p{};
-  p.tile_n = kBN;
-  p.tile_m = GemmCfg<SHERRY_PER_GROUP, kGemmTM, false>::kBM;
+  p.tile_m = GemmCfg<SHERRY_PER_GROUP, kGemmTM, false, 2>::kBM;
   p.splits = 1;
   const int64_t nsb = k / kSuperblock;
   const int64_t group_sbs = gran == SHERRY_PER_GROUP ? group_size / kSuperblock : 1;
   const int64_t chunk = gemm_chunk_rows(k);
   const int64_t mc = chunk > 0 && m > chunk ? chunk : m;
-  const int64_t tiles = ((mc + p.tile_m - 1) / p.tile_m) * ((n + kBN - 1) / kBN);
+  const int64_t tiles_m = (mc + p.tile_m - 1) / p.tile_m;
+  if (wide && tiles_m * ((n + 255) / 256) >= SHERRY_GEMM_WIDE_TILES) {
+    p.tile_n = 256;
+    p.workspace_bytes = 0;
+    return p;
+  }
+  p.tile_n = 128;
+  const int64_t tiles = tiles_m * ((n + p.tile_n - 1) / p.tile_n);
   auto valid = [&](int64_t s) { return nsb % s == 0 && (nsb / s) % group_sbs == 0 && nsb / s >= 2; };
   while (tiles * p.splits < SHERRY_GEMM_SPLIT_TARGET && p.splits < 8 && valid(2 * p.splits)) p.splits *= 2;
   p.workspace_bytes = p.splits > 1 ? (size_t)p.splits * (size_t)mc * (size_t)n * sizeof(float) : 0;
@@ -516,22 +538,29 @@ hipError_t launch_gemm(const GemmPlan& p, int64_t n, int64_t k, int gran, int gr
                        const uint8_t* packed, const float* alpha, const uint16_t* x, int64_t m,
                        uint16_t* y, float* ws, hipStream_t s) {
   const int group_sbs = gran == SHERRY_PER_GROUP ? group_size / kSuperblock : 1;
-  if (gran == SHERRY_PER_GROUP)
-    return launch_g<SHERRY_PER_GROUP, kGemmTM, false>(p, n, k, group_sbs, packed, alpha, x, m, y, ws, nullptr, 0.f, s);
-  if (gran == SHERRY_PER_CHANNEL)
-    return launch_g<SHERRY_PER_CHANNEL, kGemmTM, false>(p, n, k, group_sbs, packed, alpha, x, m, y, ws, nullptr, 0.f, s);
-  return launch_g<SHERRY_PER_TENSOR, kGemmTM, false>(p, n, k, group_sbs, packed, alpha, x, m, y, ws, nullptr, 0.f, s);
+#define SHERRY_GEMM_LAUNCH(G, TN) \
+  return launch_g<G, kGemmTM, false, TN>(p, n, k, group_sbs, packed, alpha, x, m, y, ws, nullptr, 0.f, s)
+  if (p.tile_n == 256) {
+    if (gran == SHERRY_PER_GROUP) SHERRY_GEMM_LAUNCH(SHERRY_PER_GROUP, 4);
+    if (gran == SHERRY_PER_CHANNEL) SHERRY_GEMM_LAUNCH(SHERRY_PER_CHANNEL, 4);
+    SHERRY_GEMM_LAUNCH(SHERRY_PER_TENSOR, 4);
+  }
+  if (gran == SHERRY_PER_GROUP) SHERRY_GEMM_LAUNCH(SHERRY_PER_GROUP, 2);
+  if (gran == SHERRY_PER_CHANNEL) SHERRY_GEMM_LAUNCH(SHERRY_PER_CHANNEL, 2);
+  SHERRY_GEMM_LAUNCH(SHERRY_PER_TENSOR, 2);
+#undef SHERRY_GEMM_LAUNCH
 }
 
 hipError_t launch_arenas_gemm(const GemmPlan& p, int64_t n, int64_t k, int gran, int group_size,
                               const uint8_t* packed, const float* alpha, const uint16_t* wd, float lam,
                               const uint16_t* x, int64_t m, uint16_t* y, float* ws, hipStream_t s) {
+  if (p.tile_n != 128) return hipErrorInvalidValue;
   const int group_sbs = gran == SHERRY_PER_GROUP ? group_size / kSuperblock : 1;
   if (gran == SHERRY_PER_GROUP)
-    return launch_g<SHERRY_PER_GROUP, kGemmTM, true>(p, n, k, group_sbs, packed, alpha, x, m, y, ws, wd, lam, s);
+    return launch_g<SHERRY_PER_GROUP, kGemmTM, true, 2>(p, n, k, group_sbs, packed, alpha, x, m, y, ws, wd, lam, s);
   if (gran == SHERRY_PER_CHANNEL)
-    return launch_g<SHERRY_PER_CHANNEL, kGemmTM, true>(p, n, k, group_sbs, packed, alpha, x, m, y, ws, wd, lam, s);
-  return launch_g<SHERRY_PER_TENSOR, kGemmTM, true>(p, n, k, group_sbs, packed, alpha, x, m, y, ws, wd, lam, s);
+    return launch_g<SHERRY_PER_CHANNEL, kGemmTM, true, 2>(p, n, k, group_sbs, packed, alpha, x, m, y, ws, wd, lam, s);
+  return launch_g<SHERRY_PER_TENSOR, kGemmTM, true, 2>(p, n, k, group_sbs, packed, alpha, x, m, y, ws, wd, lam, s);
 }
 
 }  // namespace sherry

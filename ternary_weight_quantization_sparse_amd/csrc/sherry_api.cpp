@@ -91,12 +91,12 @@ size_t sherry_workspace_bytes(int32_t op, int64_t n, int64_t k, int32_t granular
       return plan_gemv(n, k, granularity, group_size, (int)batch_or_m, count).workspace_bytes;
     case SHERRY_OP_GEMM:
       if (batch_or_m < 1) return (size_t)-1;
-      return plan_gemm(n, k, granularity, group_size, batch_or_m).workspace_bytes;
+      return plan_gemm(n, k, granularity, group_size, batch_or_m, true).workspace_bytes;
     case SHERRY_OP_FAKE_QUANT:
       return plan_fake_quant(n, k, granularity, group_size).workspace_bytes;
     case SHERRY_OP_ARENAS_GEMM:
       if (batch_or_m < 1) return (size_t)-1;
-      return plan_gemm(n, k, granularity, group_size, batch_or_m).workspace_bytes;
+      return plan_gemm(n, k, granularity, group_size, batch_or_m, false).workspace_bytes;
     default:
       return (size_t)-1;
   }
@@ -171,7 +171,7 @@ int32_t sherry_gemm(int64_t n, int64_t k, int32_t granularity, int32_t group_siz
   if (!packed || !alpha || !x || !y) return SHERRY_ERR_NULL;
   if (!aligned16(packed) || !aligned16(alpha) || !aligned16(x) || !aligned16(y)) return SHERRY_ERR_ALIGN;
   if (m < 1 || m > kMaxElems / k || (m + 127) / 128 > 65535) return SHERRY_ERR_BATCH;
-  const GemmPlan plan = plan_gemm(n, k, granularity, group_size, m);
+  const GemmPlan plan = plan_gemm(n, k, granularity, group_size, m, true);
   if (plan.workspace_bytes > 0 && (!workspace || workspace_bytes < plan.workspace_bytes))
     return SHERRY_ERR_WORKSPACE;
   if (plan.workspace_bytes > 0 && !aligned16(workspace)) return SHERRY_ERR_ALIGN;
@@ -209,7 +209,7 @@ int32_t sherry_arenas_gemm(int64_t n, int64_t k, int32_t granularity, int32_t gr
   if (!aligned16(packed) || !aligned16(alpha) || !aligned16(w) || !aligned16(x) || !aligned16(y))
     return SHERRY_ERR_ALIGN;
   if (m < 1 || m > kMaxElems / k || (m + 127) / 128 > 65535) return SHERRY_ERR_BATCH;
-  const GemmPlan plan = plan_gemm(n, k, granularity, group_size, m);
+  const GemmPlan plan = plan_gemm(n, k, granularity, group_size, m, false);
   if (plan.workspace_bytes > 0 && (!workspace || workspace_bytes < plan.workspace_bytes))
     return SHERRY_ERR_WORKSPACE;
   if (plan.workspace_bytes > 0 && !aligned16(workspace)) return SHERRY_ERR_ALIGN;

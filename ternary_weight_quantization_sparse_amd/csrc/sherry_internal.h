@@ -76,7 +76,9 @@ struct GemmPlan {
   int splits;              // K ranges per output tile (1 = none)
   size_t workspace_bytes;  // splits > 1: fp32 partials [splits][M][N]
 };
-GemmPlan plan_gemm(int64_t n, int64_t k, int gran, int group_size, int64_t m);
+// wide: 256-row weight tiles allowed (the plain GEMM; the Arenas forward
+// passes false).
+GemmPlan plan_gemm(int64_t n, int64_t k, int gran, int group_size, int64_t m, bool wide);
 hipError_t launch_gemm(const GemmPlan& p, int64_t n, int64_t k, int gran, int group_size,
                        const uint8_t* packed, const float* alpha, const uint16_t* x, int64_t m,
                        uint16_t* y, float* ws, hipStream_t s);

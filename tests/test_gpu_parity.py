@@ -337,6 +337,17 @@ def test_gemm_ragged(n, k, m, gran, g):
     gemm_case(n, k, m, 900 + n, 5000 + m, gran, g)
 
 
+@pytest.mark.parametrize("gran,g,k", [("per_group", 128, 256), ("per_group", 256, 512),
+                                       ("per_channel", 128, 256), ("per_tensor", 128, 384)])
+def test_gemm_wide_tiles_ragged(gran, g, k):
+    """Launches with >= 512 tiles of 64 x 256 take the 256-row weight tiles:
+    N = 4000 leaves a partial last weight tile (160 rows), M = 2000 a partial
+    last activation tile (16 rows); every output is checked."""
+    n, m = 4000, 2000
+    print(f"[gemm] wide tiles {n}x{k} M={m} {gran} G={g}", flush=True)
+    gemm_case(n, k, m, 3100 + k, 3200 + g, gran, g)
+
+
 @pytest.mark.parametrize("gran", ["per_group", "per_channel", "per_tensor"])
 def test_gemm_correlated_inputs(gran):
     """Activation rows drawn from the weight's own stream (x = w / 0.02 for

@@ -637,18 +637,31 @@ def bench_unpack(dev, reps=20):
     return res
 
 
-def bench_gemv_3b(dev, batches, sweeps_per_replay=8, warm_replays=30, replays=20):
+# Fused packing of the 3B stack: q/k/v as one [5120, 3072] weight and
+# gate/up as one [16384, 3072] weight per layer (row-local scales, so every
+# member keeps the codes and scales of packing it alone): 4 launches per
+# sweep instead of 7.
+FUSED_3B = (("qkv", (0, 1, 2)), ("o", (3,)), ("gate_up", (4, 5)), ("down", (6,)))
+
+
+def bench_gemv_3b(dev, batches, sweeps_per_replay=8, warm_replays=30, replays=20, fused=False):
     import numpy as np
     import oracle as O
     import workloads as WL
     import ternary_weight_quantization_sparse_amd as S
     torch = _torch()
     layers = WL.LLAMA_3B_LAYERS
+    groups = FUSED_3B if fused else tuple((name, (i,)) for i, (name, _, _) in enumerate(WL.LLAMA_3B))
     shapes = []
-    for i, (name, n, k) in enumerate(WL.LLAMA_3B):
+    for name, members in groups:
+        k = WL.LLAMA_3B[members[0]][2]
+        n = sum(WL.LLAMA_3B[i][1] for i in members)
         pw0 = None
         for layer in range(layers):
-            w = WL.latent_weight_device(n, k, WL.layer_3b_weight_seed(layer, i), dev)
+            parts = [WL.latent_weight_device(WL.LLAMA_3B[i][1], k, WL.layer_3b_weight_seed(layer, i), dev)
+                     for i in members]
+            w = parts[0] if len(parts) == 1 else torch.cat(parts, dim=0)
+            del parts
             pw = S.quantize_pack(w, "per_group", 128)
             if layer == 0:
                 rep = Replicated(pw, layers, batch=1)
@@ -719,7 +732,10 @@ def bench_gemv_3b(dev, batches, sweeps_per_replay=8, warm_replays=30, replays=20
         res[f"B{b}"] = {"ms_per_sweep": ms, "bytes": nbytes, "gbs": nbytes / (ms * 1e-3) / 1e9,
                         "frac_of_hbm_peak": nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
                         "layer0_within_tol": ok_all, "max_err_over_bound": worst}
-        log(f"[gemv-3b] B={b}: {ms:.3f} ms/sweep, {res[f'B{b}']['gbs']:.0f} GB/s; tol ok={ok_all}")
+        log(f"[gemv-3b{'-fused' if fused else ''}] B={b}: {ms:.3f} ms/sweep, {res[f'B{b}']['gbs']:.0f} GB/s; "
+            f"tol ok={ok_all}")
+    res["launches_per_sweep"] = len(groups)
+    res["shapes"] = [{"name": name, "n": n, "k": k} for (name, n, k, _, _) in shapes]
     return res
 
 
@@ -791,6 +807,7 @@ def main():
         extra["unpack"] = bench_unpack(dev)
     if "gemv3b" in sections:
         extra["gemv_3b"] = bench_gemv_3b(dev, (1, 4, 16))
+        extra["gemv_3b_fused"] = bench_gemv_3b(dev, (1, 4, 16), fused=True)
     if "copycal" in sections:
         # a plain copy of known size, for scaling HBM counters (FETCH_SIZE / WRITE_SIZE)
         src = torch.empty(GIB, dtype=torch.uint8, device=dev).fill_(1)

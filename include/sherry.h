@@ -183,9 +183,10 @@ int32_t sherry_gemv(int64_t n, int64_t k, int32_t granularity, int32_t group_siz
 
 /*
  * sherry_gemm -- prefill product Y[m, n] = sum_k X[m, k] * T[n, k] * alpha(n, k)
- * (same definition as sherry_gemv with M rows of activations).  Ternary
- * tiles are unpacked to bf16 in LDS and multiplied on bf16 MFMA with fp32
- * accumulation per group, then scaled.
+ * (same definition as sherry_gemv with M rows of activations).  Each wave
+ * decodes its ternary blocks into bf16 MFMA operands (+-1 / 0) in registers
+ * through a 32-entry LDS table; bf16 MFMA with fp32 accumulation per group,
+ * then scaled.
  *
  *   x   [M, K] bf16 row-major;  y [M, N] bf16 row-major (round to nearest even).
  *   m   >= 1.

@@ -438,11 +438,16 @@ __global__ __launch_bounds__(256) void gemm_split_reduce(const float* __restrict
   if (i0 >= mn) return;
   float s[4] = {0.f, 0.f, 0.f, 0.f};
   if ((mn & 3) == 0) {
-    for (int z = 0; z < splits; ++z) {
-      const f32x4 v = *reinterpret_cast<const f32x4*>(partial + z * mn + i0);
+    // every split's load first (splits <= 8), then the adds in split order
+    f32x4 v[8];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) s[e] += v[e];
-    }
+    for (int z = 0; z < 8; ++z)
+      if (z < splits) v[z] = *reinterpret_cast<const f32x4*>(partial + z * mn + i0);
+#pragma unroll
+    for (int z = 0; z < 8; ++z)
+      if (z < splits)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) s[e] += v[z][e];
   } else {
     for (int z = 0; z < splits; ++z)
       for (int e = 0; e < 4; ++e)
@@ -478,6 +483,7 @@ hipError_t launch_g(const GemmPlan& p, int64_t n, int64_t k, int group_sbs, cons
   const int tiles_n = (int)((n + kBN - 1) / kBN);
   const int64_t nsb = k / kSuperblock;
   const int splits = p.splits;
+  if (splits < 1 || splits > 8) return hipErrorInvalidValue;  // the reducer holds up to 8 partials
   const int sb_per_split = (int)(nsb / splits);
   for (int64_t r0 = 0; r0 < m; r0 += chunk) {
     const int64_t mc = m - r0 < chunk ? m - r0 : chunk;

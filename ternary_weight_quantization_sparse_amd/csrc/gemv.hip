@@ -566,8 +566,18 @@ __global__ void gemv_split_reduce(const float* __restrict__ partial, const float
   const int64_t c = idx / per;
   const int64_t bn = idx % per;
   const int64_t row = bn % n;
+  // loads 8 splits ahead of their adds (one memory latency per 8 splits, not
+  // per split); the adds keep split order
+  const float* p = partial + c * ksplit * per + bn;
   float v = 0.f;
-  for (int s = 0; s < ksplit; ++s) v += partial[(c * ksplit + s) * per + bn];
+  for (int s0 = 0; s0 < ksplit; s0 += 8) {
+    float t[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) t[j] = s0 + j < ksplit ? p[(int64_t)(s0 + j) * per] : 0.f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      if (s0 + j < ksplit) v += t[j];
+  }
   const float* al = alpha + c * alpha_stride;
   if constexpr (GRAN == SHERRY_PER_CHANNEL) v *= al[row];
   if constexpr (GRAN == SHERRY_PER_TENSOR) v *= al[0];

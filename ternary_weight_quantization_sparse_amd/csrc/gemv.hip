@@ -36,10 +36,10 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kLutThreads = 256;
 #ifndef SHERRY_GEMV_SPLIT_TARGET
-#define SHERRY_GEMV_SPLIT_TARGET 2048
+#define SHERRY_GEMV_SPLIT_TARGET 2048      // batch 1: split K until a launch has ~this many workgroups
 #endif
 #ifndef SHERRY_GEMV_MFMA_SPLIT_TARGET
-#define SHERRY_GEMV_MFMA_SPLIT_TARGET 768
+#define SHERRY_GEMV_MFMA_SPLIT_TARGET 768  // batch 2..16: the same, for the MFMA kernel
 #endif
 #ifndef SHERRY_LUT_WIN_MAX
 #define SHERRY_LUT_WIN_MAX 4  // superblocks per LDS table window (4 -> 16 KB)
@@ -52,8 +52,8 @@ constexpr int kLutThreads = 256;
 #endif
 constexpr int kTableFloatsPerSb = kBlocksPerSb * 32;  // 32 entries per block
 
-// The 4 byte offsets (entry*4 into a block's 32-entry fp32 table, or into the
-// 128-byte decode table) of the blocks in quad q of a superblock record.
+// The 4 byte offsets (entry * 4, into a block's 32-entry fp32 table of 128
+// bytes) of the blocks in quad q of a superblock record.
 // Quad q = 2d + h holds blocks q + 8b (b = 0..3): nibble dword d, nibble half
 // h, and sign bits q + 8b, which a shift moves to bit 6 of byte b.
 __device__ inline uint32_t quad_offsets(uint32_t nib_dword, uint32_t sign_word, int q) {
@@ -286,15 +286,17 @@ __global__ __launch_bounds__(kLutThreads) void gemv_b1_lut_kernel(
 // before its 16 MFMAs so their latencies overlap.
 //
 // Per wave and superblock: 1.5 KB of weight records from HBM, ~42 LDS
-// instructions (of which 32 table lookups, ~16 KB), ~85 VALU and 16 MFMA;
-// the LDS traffic, not HBM, is what bounds this kernel today.
+// instructions (of which 32 table lookups, ~16 KB), ~85 VALU and 16 MFMA.
+// The decode, not HBM, bounds this kernel: the issue and latency of the
+// table lookups and the VALU; the lookups' bytes run at about half of what
+// 8-byte lookups into this table sustain on gfx950.
 constexpr int kMfmaTiles = 4;
 #ifndef SHERRY_MFMA_RING
-#define SHERRY_MFMA_RING 3
+#define SHERRY_MFMA_RING 3  // record ring slots per wave (superblocks in flight + 1)
 #endif
 constexpr int kMfmaRing = SHERRY_MFMA_RING;
 #ifndef SHERRY_XCHUNK_SMALL
-#define SHERRY_XCHUNK_SMALL 8
+#define SHERRY_XCHUNK_SMALL 8  // superblocks per activation chunk at batch <= 4
 #endif
 // superblocks per activation chunk (a multiple of 4: one 1 KB copy per row
 // and 4 superblocks) and bytes per chunk row (padded by 16)

@@ -22,11 +22,17 @@ Also reported, each timed with HIP events on the launch stream:
             outliers x10, per_tensor / per_channel / per_group-128, rotating 4
             input copies (GB/s on bytes read + written); and the fused
             fake-quant forward (dense bf16 T*alpha) of the same weight
+  unpack    the 8192x8192 per_group planes to int8 T, bf16 and fp32 T*alpha
   gemv_3b   the 28-layer LLaMA-3.2-3B linear stack at batch 1, 4, 16 (each
-            shape one launch over its 28 layers)
+            shape one launch over its 28 layers), and the same stack with
+            q/k/v and gate/up packed as fused weights
   cpu_baseline  the CPU oracle (NumPy, one thread) on a bounded sample of the
             headline workload: one 1B layer from packed bytes to fp64 outputs.
-Every timed configuration is first checked against the oracle.
+Every timed configuration is first cross-checked on the GPU: products against
+an fp64 product over the library's unpacked weight, to the parity tolerance;
+quantizations for their invariants.  Parity with the CPU oracle of these same
+workloads is established by tests/; this file runs the oracle only for the
+CPU baseline.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--sections ...]
 """
@@ -135,10 +141,38 @@ def to_np(t):
     return t.cpu().numpy()
 
 
-def within_tol(y, y_ref, bound):
-    import numpy as np
-    err = np.abs(np.asarray(y, dtype=np.float64) - y_ref)
-    return bool(np.all(err <= bound)), float(np.max(err / bound))
+# Cross-checks of the timed launches.  Oracle parity of every benchmark
+# workload is established by tests/ (the oracle is test infrastructure, and
+# this file calls it only for the CPU baseline); here each timed result is
+# compared, on the GPU, with an fp64 product over the weight the library's own
+# unpack kernel returns (exact T * alpha), to the same tolerance:
+# 1e-3 * sum_k |x_k * alpha_k| (over the kept weights) plus half a bf16 ulp of
+# the output.
+def product_reference(pw, x):
+    """(y_ref, bound) for y = x (T alpha)^T, fp64 on the GPU."""
+    import ternary_weight_quantization_sparse_amd as S
+    w = S.unpack(pw, "float32").double()
+    xd = x.double()
+    y_ref = xd @ w.t()
+    bound = 1e-3 * (xd.abs() @ w.abs().t()) + y_ref.abs() * 2.0 ** -8 + 1e-30
+    del w
+    return y_ref, bound
+
+
+def within_bound(y, y_ref, bound):
+    """(all within, max |y - y_ref| / bound) for GPU tensors of one shape."""
+    ratio = float(((y.double() - y_ref).abs() / bound).max().item())
+    return ratio <= 1.0, ratio
+
+
+def ternary_structure_ok(pw):
+    """Every 4-weight block of the unpacked T holds exactly one zero and three
+    +-1 values (the format's invariant), checked on the GPU."""
+    import ternary_weight_quantization_sparse_amd as S
+    t = S.unpack(pw, "int8").reshape(-1, 4)
+    ok = bool(((t == 0).sum(dim=1) == 1).all().item()) and bool((t.abs() <= 1).all().item())
+    del t
+    return ok
 
 
 def timed_launches(launches, steps, warmup, per_launch=True):
@@ -189,7 +223,6 @@ def counters_for_current_source():
 # ----------------------------------------------------------------------------
 def bench_gemv_1b(args, dev):
     import numpy as np
-    import oracle as O
     import workloads as WL
     import ternary_weight_quantization_sparse_amd as S
 
@@ -197,21 +230,17 @@ def bench_gemv_1b(args, dev):
     for i, (name, n, k) in enumerate(WL.LLAMA_1B):
         w = WL.latent_weight(n, k, WL.layer_1b_weight_seed(i))
         pw = S.quantize_pack(dev_f32(w, dev), "per_group", 128)
-        ref_p, ref_a = O.quantize_pack(w, "per_group", 128)
-        ok_q = bool(np.array_equal(to_np(pw.packed), ref_p) and
-                    np.array_equal(to_np(pw.alpha).view(np.uint32), ref_a.reshape(-1).view(np.uint32)))
+        ok_t = ternary_structure_ok(pw)
         rep = Replicated(pw, copies_for(n, k))
-        xb, xv = WL.activations_bf16(1, k, 200)
+        xb, _ = WL.activations_bf16(1, k, 200)
         x = dev_bf16(xb, dev)
-        y = to_np(rep.gemv(x))
-        wq = O.dequant(O.ternary(w), ref_a, "per_group", 128)
-        y_ref = O.gemv(xv, wq)
-        ok_y, ratio = within_tol(O.bf16_bits_to_f32(y[0, :n]).reshape(1, n), y_ref,
-                                 O.tolerance_bound(xv, O.alpha_per_weight(ref_a, n, k, "per_group", 128), y_ref))
-        same = bool(np.all(y[:, :n] == y[0:1, :n]))
-        checks.append({"shape": name, "pack_bit_exact": ok_q, "gemv_within_tol": ok_y,
+        y = rep.gemv(x)
+        y_ref, bound = product_reference(pw, x)
+        ok_y, ratio = within_bound(y[0, :n].reshape(1, n), y_ref, bound)
+        same = bool((y[:, :n] == y[0:1, :n]).all().item())
+        checks.append({"shape": name, "ternary_structure": ok_t, "gemv_within_tol": ok_y,
                        "max_err_over_bound": ratio, "copies_identical": same})
-        log(f"[gemv-1b] {name} {n}x{k}: copies={rep.count} pack_exact={ok_q} tol={ok_y} "
+        log(f"[gemv-1b] {name} {n}x{k}: copies={rep.count} structure={ok_t} tol={ok_y} "
             f"(max err/bound {ratio:.3g})")
         reps.append((name, rep, x))
         pws.append((name, n, k, pw, w))
@@ -372,7 +401,6 @@ def bench_compare(pws, dev, steps=40, rounds=3):
     are timed in turn, `rounds` times, and each format keeps its fastest
     round (the part's clock ramps over the first tens of milliseconds)."""
     import numpy as np
-    import oracle as O
     import workloads as WL
     import ternary_weight_quantization_sparse_amd as S
     torch = _torch()
@@ -382,10 +410,7 @@ def bench_compare(pws, dev, steps=40, rounds=3):
     ok = {f: True for f, _ in formats}
     for (name, n, k, _, w) in pws:
         pw = S.quantize_pack(dev_f32(w, dev), "per_channel", 128)
-        a = to_np(pw.alpha)
-        xv = O.bf16_bits_to_f32(to_np(xs[k]).reshape(1, k))
-        y_ref = O.gemv(xv, O.dequant(O.ternary(w), a, "per_channel", 128))
-        bound = O.tolerance_bound(xv, O.alpha_per_weight(a, n, k, "per_channel", 128), y_ref)
+        y_ref, bound = product_reference(pw, xs[k])
         for fname, fmt in formats:
             if fmt is None:
                 nbytes = S.packed_bytes(n, k)
@@ -407,7 +432,7 @@ def bench_compare(pws, dev, steps=40, rounds=3):
                 launch = (lambda f=fmt, p_=allp, a_=alla, y_=yv, c=count, ps_=ps, as_=ast, x=xs[k], n_=n, k_=k:
                           S.compare_gemv(f, p_, a_, n_, k_, x, c, ps_, as_, y_, as_))
             launch()
-            good, _ = within_tol(O.bf16_bits_to_f32(to_np(yv[0, :n])).reshape(1, n), y_ref, bound)
+            good, _ = within_bound(yv[0, :n].reshape(1, n), y_ref, bound)
             ok[fname] &= good
             runs[fname].append((launch, count, count * (nbytes + 4 * n + 2 * n) + 2 * k))
     for _ in range(10):
@@ -441,7 +466,6 @@ def bench_gemm(pws, dev, ms, reps=20):
     bf16 latent weight: twice the MFMA work).  Workspaces are allocated once,
     outside the timed launches."""
     import numpy as np
-    import oracle as O
     import workloads as WL
     import ternary_weight_quantization_sparse_amd as S
     torch = _torch()
@@ -451,15 +475,14 @@ def bench_gemm(pws, dev, ms, reps=20):
     wds = {name: dev_bf16(WL.f32_to_bf16_bits(w), dev) for (name, n, k, pw, w) in pws}
     res = {"arenas_lambda": lam}
     for m in ms:
-        xb, xv = WL.activations_bf16(m, 8192, 300 + m)
+        xb, _ = WL.activations_bf16(m, 8192, 300 + m)
         xs = {k: dev_bf16(np.ascontiguousarray(xb[:, :k]), dev) for k in (2048, 8192)}
-        xvs = {k: xv[:, :k] for k in (2048, 8192)}
         ys = {name: torch.empty((m, n), dtype=torch.bfloat16, device=dev) for (name, n, k, _, _) in pws}
         wss = {}
         for (name, n, k, pw, _) in pws:
             b = S.workspace_bytes(3, n, k, "per_group", 128, m)
             wss[name] = (torch.empty(max(b, 16), dtype=torch.uint8, device=dev), b)
-        rows = np.random.default_rng(m).choice(m, size=min(m, 64), replace=False)
+        rows = torch.from_numpy(np.random.default_rng(m).choice(m, size=min(m, 64), replace=False)).to(dev)
 
         def mk(name, n, k, pw, arenas):
             ws, b = wss[name]
@@ -476,17 +499,18 @@ def bench_gemm(pws, dev, ms, reps=20):
             checks = []
             for fn, (name, n, k, pw, w) in zip(launches, pws):
                 fn()
-                yv = O.bf16_bits_to_f32(to_np(ys[name]))[rows]
-                a = to_np(pw.alpha)
-                wq = O.dequant(O.ternary(w), a, "per_group", 128)
-                mag = O.alpha_per_weight(a, n, k, "per_group", 128)
+                xr = xs[k][rows]
+                y_ref, bound = product_reference(pw, xr)
                 if arenas:
-                    wv = WL.bf16_bits_to_f32(WL.f32_to_bf16_bits(w))
-                    y_ref = O.arenas_forward(xvs[k][rows], wq, wv, lam)
-                    mag = mag + np.abs(np.float32(lam) * wv)
-                else:
-                    y_ref = O.gemm(xvs[k][rows], wq)
-                ok, ratio = within_tol(yv, y_ref, O.tolerance_bound(xvs[k][rows], mag, y_ref))
+                    # plus lambda X W^T over the bf16 latent weight, and its
+                    # share of the bound
+                    wl = float(np.float32(lam)) * wds[name].double()
+                    xd = xr.double()
+                    y_ref = y_ref + xd @ wl.t()
+                    bound = (1e-3 * (xd.abs() @ (S.unpack(pw, "float32").double().abs() + wl.abs()).t())
+                             + y_ref.abs() * 2.0 ** -8 + 1e-30)
+                    del wl
+                ok, ratio = within_bound(ys[name][rows], y_ref, bound)
                 checks.append({"shape": name, "within_tol_sampled_rows": ok, "max_err_over_bound": ratio})
             # warm up for ~0.3 s of passes: the part ramps its clock under MFMA
             # load, and short warm-ups time the ramp rather than the kernels
@@ -515,22 +539,39 @@ def bench_gemm(pws, dev, ms, reps=20):
     return res
 
 
+def quantize_consistent(w, pw):
+    """GPU checks of a quantization that need no oracle: one zero per block,
+    the zero on a smallest |w| of its block, kept signs +1 iff w > 0, scales
+    finite and non-negative."""
+    torch = _torch()
+    t = _unpack_i8(pw).reshape(-1, 4)
+    wf = w.float().reshape(-1, 4)
+    aw = wf.abs()
+    ok = ((t == 0).sum(dim=1) == 1).all()
+    ok &= ((aw * (t == 0)).sum(dim=1) == aw.min(dim=1).values).all()
+    ok &= ((t == 0) | (t == torch.where(wf > 0, 1, -1).to(t.dtype))).all()
+    ok &= (torch.isfinite(pw.alpha) & (pw.alpha >= 0)).all()
+    return bool(ok.item())
+
+
+def _unpack_i8(pw):
+    import ternary_weight_quantization_sparse_amd as S
+    return S.unpack(pw, "int8")
+
+
 def bench_quantize(dev, reps=10):
     import numpy as np
-    import oracle as O
     import workloads as WL
     import ternary_weight_quantization_sparse_amd as S
     torch = _torch()
     n = k = 8192
-    bits, vals = WL.latent_weight_outliers_bf16(n, k, 5000)
+    bits, _ = WL.latent_weight_outliers_bf16(n, k, 5000)
     w0 = dev_bf16(bits, dev)
     copies = [w0] + [w0.clone() for _ in range(3)]
     res = {}
     for gran in ("per_tensor", "per_channel", "per_group"):
         pw = S.quantize_pack(w0, gran, 128)
-        ref_p, ref_a = O.quantize_pack(vals, gran, 128)
-        ok = bool(np.array_equal(to_np(pw.packed), ref_p) and
-                  np.array_equal(to_np(pw.alpha).view(np.uint32), ref_a.reshape(-1).view(np.uint32)))
+        ok = quantize_consistent(w0, pw)
         ws_b = S.workspace_bytes(0, n, k, gran, 128)
         ws = torch.empty(max(ws_b, 16), dtype=torch.uint8, device=dev)
         packed = torch.empty(S.packed_bytes(n, k), dtype=torch.uint8, device=dev)
@@ -546,17 +587,21 @@ def bench_quantize(dev, reps=10):
                                              torch.cuda.current_stream().cuda_stream))
         total, per, _ = timed_launches([launch], reps, 2)
         t = float(np.median(per[0]))
+        # the timed launches rewrote packed / alpha from identical copies
+        same = bool(torch.equal(packed, pw.packed) and torch.equal(alpha, pw.alpha))
         rd, wr = n * k * 2, S.packed_bytes(n, k) + 4 * alpha.numel()
-        res[gran] = {"bit_exact": ok, "ms": t, "gbs": (rd + wr) / (t * 1e-3) / 1e9,
+        res[gran] = {"consistent": ok, "repeatable": same, "ms": t, "gbs": (rd + wr) / (t * 1e-3) / 1e9,
                      "gweights_per_s": n * k / (t * 1e-3) / 1e9}
-        log(f"[quantize] {gran}: bit_exact={ok} {t * 1e3:.1f} us, {res[gran]['gbs']:.0f} GB/s")
+        log(f"[quantize] {gran}: consistent={ok} repeatable={same} {t * 1e3:.1f} us, "
+            f"{res[gran]['gbs']:.0f} GB/s")
     # quantization-aware-training forward: dense bf16 T*alpha from the same
     # weight (per_group 128: the fused kernel)
+    # (equal, bit for bit, to quantize + pack followed by unpack to bf16)
     out, a = S.fake_quant(w0, "per_group", 128)
-    ref, ref_a = O.fake_quant(vals, "per_group", 128)
-    ok = bool(np.array_equal(to_np(out), O.round_to_bf16_bits(ref.astype(np.float32))) and
-              np.array_equal(to_np(a).view(np.uint32), ref_a.reshape(-1).view(np.uint32)))
-    del ref
+    pw = S.quantize_pack(w0, "per_group", 128)
+    ok = bool(torch.equal(out.view(torch.int16), S.unpack(pw, "bfloat16").view(torch.int16)) and
+              torch.equal(a, pw.alpha))
+    del pw
     outs = [torch.empty_like(w0) for _ in range(2)]
     alpha = torch.empty(S.num_scales(n, k, "per_group", 128), dtype=torch.float32, device=dev)
     lib = S.load()
@@ -570,9 +615,9 @@ def bench_quantize(dev, reps=10):
     total, per, _ = timed_launches([fq], reps, 2)
     t = float(np.median(per[0]))
     nbytes = n * k * 2 + n * k * 2 + 4 * alpha.numel()
-    res["fake_quant_per_group_bf16"] = {"bit_exact": ok, "ms": t, "gbs": nbytes / (t * 1e-3) / 1e9,
+    res["fake_quant_per_group_bf16"] = {"equals_quantize_then_unpack": ok, "ms": t, "gbs": nbytes / (t * 1e-3) / 1e9,
                                         "gweights_per_s": n * k / (t * 1e-3) / 1e9}
-    log(f"[fake-quant] per_group bf16->bf16: bit_exact={ok} {t * 1e3:.1f} us, "
+    log(f"[fake-quant] per_group bf16->bf16: equals quantize+unpack={ok} {t * 1e3:.1f} us, "
         f"{res['fake_quant_per_group_bf16']['gbs']:.0f} GB/s")
     return res
 
@@ -583,27 +628,30 @@ def bench_unpack(dev, reps=20):
     >= 1 GiB in total, so the writes reach HBM; bytes = packed planes (+ scales
     for the scaled outputs) + the output."""
     import numpy as np
-    import oracle as O
     import workloads as WL
     import ternary_weight_quantization_sparse_amd as S
     torch = _torch()
     n = k = 8192
-    bits, vals = WL.latent_weight_outliers_bf16(n, k, 5000)
-    pw = S.quantize_pack(dev_bf16(bits, dev), "per_group", 128)
-    t_ref = O.ternary(vals)
-    ref_a = O.alpha(vals, "per_group", 128)
-    rows = np.random.default_rng(11).choice(n, 64, replace=False)
+    bits, _ = WL.latent_weight_outliers_bf16(n, k, 5000)
+    w0 = dev_bf16(bits, dev)
+    pw = S.quantize_pack(w0, "per_group", 128)
     lib = S.load()
     res = {}
+    # consistency of the three outputs, on the GPU: T is a valid quantization
+    # of the weight; fp32 is T times the broadcast scale (exact); bf16 is that
+    # rounded to nearest even
+    t = S.unpack(pw, "int8")
+    scaled = t.float() * pw.alpha.view(k // 128, n).t().repeat_interleave(128, dim=1)
+    expect = {"int8": None, "float32": scaled.view(torch.int32), "bfloat16": scaled.to(torch.bfloat16).view(torch.int16)}
+    del t
     for name, od, esize in (("int8", S._lib.I8, 1), ("bfloat16", S._lib.BF16, 2), ("float32", S._lib.F32, 4)):
-        got = to_np(S.unpack(pw, name))
         if name == "int8":
-            ok = bool(np.array_equal(got, t_ref))
+            ok = quantize_consistent(w0, pw)
         else:
-            wq = O.dequant(t_ref[rows], ref_a[:, rows], "per_group", 128).astype(np.float32)
-            ok = bool(np.array_equal(got[rows], O.round_to_bf16_bits(wq)) if name == "bfloat16"
-                      else np.array_equal(got[rows].view(np.uint32), wq.view(np.uint32)))
-        del got
+            got = S.unpack(pw, name)
+            ok = bool(torch.equal(got.view(torch.int16 if name == "bfloat16" else torch.int32), expect[name]))
+            del got
+        expect[name] = None
         outs = [torch.empty(n * k * esize, dtype=torch.uint8, device=dev)
                 for _ in range(max(2, -(-GIB // (n * k * esize))))]
         ins = [pw.packed] + [pw.packed.clone() for _ in range(7)]
@@ -617,10 +665,10 @@ def bench_unpack(dev, reps=20):
         _, per, _ = timed_launches([launch], reps, 2)
         t = float(np.median(per[0]))
         nbytes = S.packed_bytes(n, k) + (0 if name == "int8" else 4 * pw.alpha.numel()) + n * k * esize
-        res[name] = {"exact": ok, "ms": t, "gbs": nbytes / (t * 1e-3) / 1e9,
+        res[name] = {"consistent": ok, "ms": t, "gbs": nbytes / (t * 1e-3) / 1e9,
                      "frac_of_hbm_peak": nbytes / (t * 1e-3) / 1e9 / HBM_PEAK_GBS, "bytes": nbytes,
                      "output_buffers": len(outs)}
-        log(f"[unpack] 8192x8192 -> {name}: exact={ok} {t * 1e3:.1f} us, {res[name]['gbs']:.0f} GB/s")
+        log(f"[unpack] 8192x8192 -> {name}: consistent={ok} {t * 1e3:.1f} us, {res[name]['gbs']:.0f} GB/s")
         del outs, ins
     # reference write rate at the int8 output's size: torch's fill of 64 MiB
     # buffers, rotating over 1 GiB
@@ -646,7 +694,6 @@ FUSED_3B = (("qkv", (0, 1, 2)), ("o", (3,)), ("gate_up", (4, 5)), ("down", (6,))
 
 def bench_gemv_3b(dev, batches, sweeps_per_replay=8, warm_replays=30, replays=20, fused=False):
     import numpy as np
-    import oracle as O
     import workloads as WL
     import ternary_weight_quantization_sparse_amd as S
     torch = _torch()
@@ -665,20 +712,17 @@ def bench_gemv_3b(dev, batches, sweeps_per_replay=8, warm_replays=30, replays=20
             pw = S.quantize_pack(w, "per_group", 128)
             if layer == 0:
                 rep = Replicated(pw, layers, batch=1)
-                pw0 = (pw, w.cpu().numpy())
+                pw0 = (pw, w)
             else:
                 rep.packed_all[layer, :rep.nbytes] = pw.packed
                 rep.alpha_all[layer, :rep.nsc] = pw.alpha
-            del w
+                del w
         shapes.append((name, n, k, rep, pw0))
     torch.cuda.synchronize()
     res = {"layers": layers, "stack_bytes_packed_plus_scales": sum(layers * (r.nbytes + 4 * r.nsc)
                                                                    for (_, _, _, r, _) in shapes)}
-    # oracle check of layer 0 (codes/scales) on the q shape
-    name, n, k, rep, (pw, wv) = shapes[0]
-    ref_p, ref_a = O.quantize_pack(wv, "per_group", 128)
-    res["layer0_q_pack_bit_exact"] = bool(np.array_equal(to_np(pw.packed), ref_p) and
-                                          np.array_equal(to_np(pw.alpha), ref_a.reshape(-1)))
+    # layer 0 of every launch: a consistent quantization of its weight
+    res["layer0_quantize_consistent"] = all(quantize_consistent(w, pw) for (_, _, _, _, (pw, w)) in shapes)
     for b in batches:
         launches, reps_b = [], []
         for (name, n, k, rep, (pw, wv)) in shapes:
@@ -689,19 +733,16 @@ def bench_gemv_3b(dev, batches, sweeps_per_replay=8, warm_replays=30, replays=20
             rb.y = torch.empty((layers, rb.y_stride), dtype=torch.bfloat16, device=dev)
             wsb = S.workspace_bytes(2, n, k, "per_group", 128, b, layers)
             rb.ws = torch.empty(wsb, dtype=torch.uint8, device=dev) if wsb else None
-            xb, xv = WL.activations_bf16(b, k, 2000 + b)
+            xb, _ = WL.activations_bf16(b, k, 2000 + b)
             x = dev_bf16(xb, dev)
-            reps_b.append((name, n, k, rb, x, xv, pw, wv))
+            reps_b.append((name, n, k, rb, x, pw))
             launches.append(lambda r=rb, xx=x: r.gemv(xx))
-        # correctness: layer 0 of every shape against the oracle
+        # correctness: layer 0 of every launch against the fp64 GPU product
         ok_all, worst = True, 0.0
-        for (name, n, k, rb, x, xv, pw, wv) in reps_b:
-            y = to_np(rb.gemv(x))
-            a = to_np(pw.alpha)
-            wq = O.dequant(O.ternary(wv), a, "per_group", 128)
-            y_ref = O.gemv(xv, wq)
-            ok, ratio = within_tol(O.bf16_bits_to_f32(y[0, :b * n]).reshape(b, n), y_ref,
-                                   O.tolerance_bound(xv, O.alpha_per_weight(a, n, k, "per_group", 128), y_ref))
+        for (name, n, k, rb, x, pw) in reps_b:
+            y = rb.gemv(x)
+            y_ref, bound = product_reference(pw, x)
+            ok, ratio = within_bound(y[0, :b * n].reshape(b, n), y_ref, bound)
             ok_all &= ok
             worst = max(worst, ratio)
         # the sweep's 7 launches captured in a HIP graph, SWEEPS sweeps per
@@ -728,7 +769,7 @@ def bench_gemv_3b(dev, batches, sweeps_per_replay=8, warm_replays=30, replays=20
         torch.cuda.synchronize()
         ms = e0.elapsed_time(e1) / (replays * sweeps_per_replay)
         del g
-        nbytes = sum(rb.algo_bytes() for (_, _, _, rb, _, _, _, _) in reps_b)
+        nbytes = sum(rb.algo_bytes() for (_, _, _, rb, _, _) in reps_b)
         res[f"B{b}"] = {"ms_per_sweep": ms, "bytes": nbytes, "gbs": nbytes / (ms * 1e-3) / 1e9,
                         "frac_of_hbm_peak": nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
                         "layer0_within_tol": ok_all, "max_err_over_bound": worst}

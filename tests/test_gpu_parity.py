@@ -217,8 +217,8 @@ def test_gemv_ragged_and_split(n, k, batch):
     gemv_case(n, k, 60 + k, xb, xv)
 
 
-@pytest.mark.parametrize("batch", [4, 16])
-@pytest.mark.parametrize("i", [0, 1, 6])
+@pytest.mark.parametrize("batch", [1, 4, 16])
+@pytest.mark.parametrize("i", [0, 1, 3, 4, 6])
 def test_gemv_llama3b_batches(i, batch):
     name, n, k = WL.LLAMA_3B[i]
     xb, xv = WL.activations_bf16(batch, k, 2000 + batch)
@@ -476,19 +476,26 @@ def test_fake_quant_ste_gradient_passes_through():
 
 
 # ------------------------------------------------------------------ fused members
+
 @pytest.mark.parametrize("gran", ["per_group", "per_channel"])
-def test_fused_qkv_pack_and_gemv(gran):
-    """q/k/v of the 1B layer packed as one 3072x2048 weight: every member has
-    the codes and scales of packing it alone, and one GEMV launch gives each
-    member's product within tolerance."""
-    members = WL.LLAMA_1B[:3]
-    ws = [WL.latent_weight(n, k, WL.layer_1b_weight_seed(i)) for i, (_, n, k) in enumerate(members)]
+@pytest.mark.parametrize("model,batch", [("1b", 1), ("3b", 1), ("3b", 4)])
+def test_fused_qkv_pack_and_gemv(gran, model, batch):
+    """q/k/v of a 1B or 3B layer packed as one weight (3072 x 2048 or
+    5120 x 3072): every member has the codes and scales of packing it alone,
+    and one GEMV launch gives each member's product within tolerance."""
+    if model == "1b":
+        members = WL.LLAMA_1B[:3]
+        ws = [WL.latent_weight(n, k, WL.layer_1b_weight_seed(i)) for i, (_, n, k) in enumerate(members)]
+    else:
+        members = WL.LLAMA_3B[:3]
+        ws = [WL.latent_weight(n, k, WL.layer_3b_weight_seed(0, i)) for i, (_, n, k) in enumerate(members)]
     fw = S.quantize_pack_fused([dev_f32(w) for w in ws], gran, 128)
     k = members[0][2]
     t_all = to_np(S.unpack(fw.pw, "int8"))
     a_all = to_np(fw.pw.alpha)
     a_all = a_all.reshape(k // 128, -1) if gran == "per_group" else a_all.reshape(1, -1)
-    xb, xv = WL.activations_bf16(1, k, 200)
+    xb, xv = WL.activations_bf16(batch, k, 200 + batch)
+    print(f"[gemv] fused q/k/v {model} {gran} batch {batch}", flush=True)
     ys = [O.bf16_bits_to_f32(to_np(y)) for y in S.gemv_fused(fw, dev_bf16(xb))]
     r0 = 0
     for w, (name, n, _), y in zip(ws, members, ys):

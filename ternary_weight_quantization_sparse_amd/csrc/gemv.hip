@@ -282,8 +282,8 @@ __global__ __launch_bounds__(kLutThreads) void gemv_b1_lut_kernel(
 // (a table of 4-byte high-byte entries plus two v_perm_b32 per block moves
 // half that LDS traffic to the VALU and measured slower).  The byte offsets
 // (code * 8) of four blocks come out of one nibble dword and the sign dword
-// with four bit operations.  All table lookups of a superblock are issued
-// before its 16 MFMAs so their latencies overlap.
+// with four bit operations.  A tile's lookups are issued one tile ahead of
+// its MFMAs so their latencies overlap.
 //
 // Per wave and superblock: 1.5 KB of weight records from HBM, ~42 LDS
 // instructions (of which 32 table lookups, ~16 KB), ~85 VALU and 16 MFMA.
@@ -465,26 +465,32 @@ __global__ __launch_bounds__(256) void gemv_mfma_kernel(
       off_hi[i] = quad_offsets8(nd[i], sg[i], 2 * q + 1);  // blocks 2q + 1 + 8t
     }
     const bool first = MODE == kGroup1 || (MODE == kGroupN && gpos == 0);  // a group starts here
-    // every table lookup of the superblock first (their latencies overlap),
-    // then the 16 MFMAs
-    u32x4 wv[4][kMfmaTiles];
+    // Tile by tile: tile i + 1's 8 table lookups are issued before tile i's 4
+    // MFMAs, so about 8-16 lookups are in flight at a time (a wave can have at
+    // most 15 LDS operations outstanding: issuing all 32 of the superblock
+    // first stalled issue), and their latency runs under the MFMAs.
+    auto lookups = [&](int i, u32x4 (&w)[4]) {
 #pragma unroll
-    for (int t = 0; t < 4; ++t) {
-#pragma unroll
-      for (int i = 0; i < kMfmaTiles; ++i) {
+      for (int t = 0; t < 4; ++t) {
         const uint2 e0 = *reinterpret_cast<const uint2*>(
             reinterpret_cast<const char*>(dtab) + __builtin_amdgcn_ubfe(off_lo[i], 8 * t, 8));
         const uint2 e1 = *reinterpret_cast<const uint2*>(
             reinterpret_cast<const char*>(dtab) + __builtin_amdgcn_ubfe(off_hi[i], 8 * t, 8));
-        wv[t][i] = u32x4{e0.x, e0.y, e1.x, e1.y};
+        w[t] = u32x4{e0.x, e0.y, e1.x, e1.y};
       }
-    }
+    };
+    u32x4 wa[4], wb[4];
+    lookups(0, wa);
 #pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      const bf16x8 xv = __builtin_bit_cast(bf16x8, xf[t]);
+    for (int i = 0; i < kMfmaTiles; ++i) {
+      u32x4 (&wc)[4] = (i & 1) ? wb : wa;
+      u32x4 (&wn)[4] = (i & 1) ? wa : wb;
+      if (i + 1 < kMfmaTiles) lookups(i + 1, wn);
+      __builtin_amdgcn_sched_barrier(0);  // keep the next tile's lookups ahead of these MFMAs
 #pragma unroll
-      for (int i = 0; i < kMfmaTiles; ++i) {
-        const bf16x8 w8 = __builtin_bit_cast(bf16x8, wv[t][i]);
+      for (int t = 0; t < 4; ++t) {
+        const bf16x8 xv = __builtin_bit_cast(bf16x8, xf[t]);
+        const bf16x8 w8 = __builtin_bit_cast(bf16x8, wc[t]);
         if constexpr (kGroup) {
           // the group's first MFMA starts from zero instead of clearing accg
           const f32x4 cin = (t == 0 && first) ? f32x4{0.f, 0.f, 0.f, 0.f} : accg[i];
@@ -493,6 +499,7 @@ __global__ __launch_bounds__(256) void gemv_mfma_kernel(
           acc[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xv, w8, acc[i], 0, 0, 0);
         }
       }
+      __builtin_amdgcn_sched_barrier(0);
     }
     if constexpr (kGroup) {
       if (++gpos == group_sbs) {

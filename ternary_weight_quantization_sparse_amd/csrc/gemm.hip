@@ -80,7 +80,14 @@ struct GemmCfg {
   static constexpr int kTN = TN;
   static constexpr int kWN = 16 * TN;              // weight rows per wave
   static constexpr int kBN = kWN * kWaves;         // weight rows per tile
-  static constexpr int kWLoads = AR ? kBN * kRowBytes / 1024 / kWaves : 0;  // 1 KB dense-weight copies per wave per stage
+  // Arenas dense-weight operands: per_channel / per_tensor load them straight
+  // into registers one stage ahead (no LDS tile, so two workgroups fit per
+  // CU); per_group, which also holds the group accumulators, would spill, and
+  // copies a dense tile into LDS like the activations.
+  static constexpr bool kWReg = AR && GRAN != SHERRY_PER_GROUP;
+  static constexpr int kWLoads = !AR ? 0
+                               : kWReg ? TN * 4                                // 16-byte loads per lane per stage
+                               : kBN * kRowBytes / 1024 / kWaves;              // 1 KB tile copies per wave per stage
   static constexpr int kTM = TM;
   static constexpr int kBM = 16 * TM;              // rows of X per tile
   static constexpr int kXLoads = kBM * kRowBytes / 1024 / kWaves;  // 1 KB activation copies per wave per stage
@@ -101,7 +108,7 @@ using Slot = std::integral_constant<int, J>;
 // write bf16 Y; else write fp32 partial[split][m][n] (per_group already
 // scaled, per_channel / per_tensor not yet; AR: fully scaled).
 template <int GRAN, int TM, bool AR, int TN>
-__global__ __launch_bounds__(kThreads, AR ? 1 : (TN == 4 ? 2 : 3)) void gemm_kernel(const uint8_t* packed,
+__global__ __launch_bounds__(kThreads, AR ? (GRAN != SHERRY_PER_GROUP ? 2 : 1) : (TN == 4 ? 2 : 3)) void gemm_kernel(const uint8_t* packed,
                                                      const float* __restrict__ alpha,
                                                      const uint16_t* __restrict__ x,
                                                      uint16_t* __restrict__ y, float* __restrict__ partial,
@@ -116,7 +123,7 @@ __global__ __launch_bounds__(kThreads, AR ? 1 : (TN == 4 ? 2 : 3)) void gemm_ker
   // knows an LDS read of one slot never aliases the copies in flight into
   // another.  Slot: activation tile, records, and for AR the dense-weight tile.
   constexpr int kWOff = kBM * kRowBytes + kRecWave * kWaves;
-  constexpr int kSlot = kWOff + (AR ? kBN * kRowBytes : 0);
+  constexpr int kSlot = kWOff + ((AR && !C::kWReg) ? kBN * kRowBytes : 0);
   __shared__ __attribute__((aligned(16))) char sl0[kSlot], sl1[kSlot];
   __shared__ __attribute__((aligned(16))) uint2 dtab[32];
 
@@ -171,6 +178,7 @@ __global__ __launch_bounds__(kThreads, AR ? 1 : (TN == 4 ? 2 : 3)) void gemm_ker
   int64_t crow = n0 + wave * kWN + (lane % kWN);
   crow = crow < n ? crow : n - 1;
 
+  u32x4 wreg[C::kWReg ? 2 : 1][C::kWReg ? kTN : 1][4];  // dense-weight operands, one stage per slot
   auto issue = [&](auto J, int st) {
     const int64_t sb = sb0 + st;
     const uint32_t sbyte = (uint32_t)(sb * (kStageK * 2));
@@ -194,7 +202,22 @@ __global__ __launch_bounds__(kThreads, AR ? 1 : (TN == 4 ? 2 : 3)) void gemm_ker
             const_cast<float*>(alpha + (group_sbs == 1 ? sb : (int64_t)((int)sb / group_sbs)) * n + crow),
             (lds_void*)(rb + kRecAlpha), 4, 0, 0);
     }
-    if constexpr (AR) {
+    if constexpr (C::kWReg) {
+      // dense-weight operands of this stage straight into registers: lane
+      // (r, q) of tile i, k-step kk reads W[row][32 kk + 8q .. + 7] of this
+      // superblock (rows past n are clamped: their outputs are not stored).
+      // They land with the stage's copies (the wait at the end of the
+      // previous stage).
+#pragma unroll
+      for (int i = 0; i < kTN; ++i) {
+        int64_t row = n0 + wave * kWN + i * 16 + r;
+        row = row < n ? row : n - 1;
+        const uint16_t* src = wd + row * k + sb * kStageK + q * 8;
+#pragma unroll
+        for (int kk = 0; kk < kStageK / 32; ++kk)
+          wreg[decltype(J)::value][i][kk] = *reinterpret_cast<const u32x4*>(src + kk * 32);
+      }
+    } else if constexpr (AR) {
       // dense-weight tile: rows n0 .. n0+127 of W, copied like X (rows past n
       // read zeros; the host keeps (n + 128) * k * 2 below 2^31)
       const __amdgpu_buffer_rsrc_t wr = __builtin_amdgcn_make_buffer_rsrc(
@@ -289,7 +312,10 @@ __global__ __launch_bounds__(kThreads, AR ? 1 : (TN == 4 ? 2 : 3)) void gemm_ker
         }
         const int ch = kk * 4 + q;
         bf16x8 ad[AR ? kTN : 1];
-        if constexpr (AR) {
+        if constexpr (C::kWReg) {
+#pragma unroll
+          for (int i = 0; i < kTN; ++i) ad[i] = __builtin_bit_cast(bf16x8, wreg[decltype(J)::value][i][kk]);
+        } else if constexpr (AR) {
 #pragma unroll
           for (int i = 0; i < kTN; ++i)
             ad[i] = *reinterpret_cast<const bf16x8*>(WT(J) + swz(wave * kWN + i * 16 + r, ch));

@@ -38,6 +38,7 @@
 // Split K: launches with few tiles split K into `splits` ranges of whole
 // groups; each writes fp32 partial tiles to the workspace, and a second
 // kernel sums them in split order (deterministic), scales and rounds to bf16.
+#include <cmath>
 #include <type_traits>
 
 #include "sherry_internal.h"
@@ -74,17 +75,22 @@ __device__ inline int swz(int row, int ch) { return row * kRowBytes + ((ch ^ swz
 // enough tiles to fill the GPU at two workgroups per CU).
 // AR: the Arenas training forward, which adds lambda * X W^T over the dense
 // bf16 latent weight W in the same K loop.
-template <int GRAN, int TM, bool AR, int TN>
+// MERGE (Arenas, per_group): the dense product accumulates into the output
+// accumulators, and each group's sum is folded in scaled by alpha / lambda;
+// the epilogue multiplies by lambda.  One accumulator set fewer, so the
+// dense-weight operands fit in registers.  Needs lambda != 0 with alpha /
+// lambda finite (the host picks it only then).
+template <int GRAN, int TM, bool AR, int TN, bool MERGE = false>
 struct GemmCfg {
   static constexpr bool kGroup = GRAN == SHERRY_PER_GROUP;
   static constexpr int kTN = TN;
   static constexpr int kWN = 16 * TN;              // weight rows per wave
   static constexpr int kBN = kWN * kWaves;         // weight rows per tile
-  // Arenas dense-weight operands: per_channel / per_tensor load them straight
-  // into registers one stage ahead (no LDS tile, so two workgroups fit per
-  // CU); per_group, which also holds the group accumulators, would spill, and
-  // copies a dense tile into LDS like the activations.
-  static constexpr bool kWReg = AR && GRAN != SHERRY_PER_GROUP;
+  // Arenas dense-weight operands: loaded straight into registers one stage
+  // ahead (no LDS tile, so two workgroups fit per CU), except for per_group
+  // without MERGE, whose three accumulator sets leave no room: it copies a
+  // dense tile into LDS like the activations.
+  static constexpr bool kWReg = AR && (GRAN != SHERRY_PER_GROUP || MERGE);
   static constexpr int kWLoads = !AR ? 0
                                : kWReg ? TN * 4                                // 16-byte loads per lane per stage
                                : kBN * kRowBytes / 1024 / kWaves;              // 1 KB tile copies per wave per stage
@@ -107,15 +113,16 @@ using Slot = std::integral_constant<int, J>;
 // grid: x = tiles (tiles_m * tiles_n), y = K splits.  partial == nullptr:
 // write bf16 Y; else write fp32 partial[split][m][n] (per_group already
 // scaled, per_channel / per_tensor not yet; AR: fully scaled).
-template <int GRAN, int TM, bool AR, int TN>
-__global__ __launch_bounds__(kThreads, AR ? (GRAN != SHERRY_PER_GROUP ? 2 : 1) : (TN == 4 ? 2 : 3)) void gemm_kernel(const uint8_t* packed,
+template <int GRAN, int TM, bool AR, int TN, bool MERGE>
+__global__ __launch_bounds__(kThreads, AR ? (GRAN != SHERRY_PER_GROUP || MERGE ? 2 : 1) : (TN == 4 ? 2 : 3)) void gemm_kernel(const uint8_t* packed,
                                                      const float* __restrict__ alpha,
                                                      const uint16_t* __restrict__ x,
                                                      uint16_t* __restrict__ y, float* __restrict__ partial,
                                                      int64_t n, int64_t k, int64_t m, int group_sbs,
                                                      int tiles_m, int tiles_n, int sb_per_split,
                                                      const uint16_t* __restrict__ wd, float lam) {
-  using C = GemmCfg<GRAN, TM, AR, TN>;
+  using C = GemmCfg<GRAN, TM, AR, TN, MERGE>;
+  static_assert(!MERGE || (AR && GRAN == SHERRY_PER_GROUP), "MERGE is the per_group Arenas variant");
   constexpr int kTM = C::kTM, kBM = C::kBM, kXLoads = C::kXLoads, kRecWave = C::kRecWave;
   constexpr int kTN = C::kTN, kWN = C::kWN, kBN = C::kBN;
   constexpr int kRecNib = C::kRecNib, kRecSgn = C::kRecSgn, kRecAlpha = C::kRecAlpha;
@@ -133,6 +140,7 @@ __global__ __launch_bounds__(kThreads, AR ? (GRAN != SHERRY_PER_GROUP ? 2 : 1) :
   auto RC = [&](auto J) -> char* { return XS(J) + kBM * kRowBytes; };
   auto WT = [&](auto J) -> char* { return XS(J) + kWOff; };
 
+  const float rlam = MERGE ? 1.0f / lam : 0.f;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -263,7 +271,8 @@ __global__ __launch_bounds__(kThreads, AR ? (GRAN != SHERRY_PER_GROUP ? 2 : 1) :
 
   f32x4 acc[kTN][kTM];
   f32x4 accg[C::kGroup ? kTN : 1][C::kGroup ? kTM : 1];
-  f32x4 accd[AR ? kTN : 1][AR ? kTM : 1];  // AR: X W^T over the dense weight
+  constexpr bool kAccD = AR && !MERGE;
+  f32x4 accd[kAccD ? kTN : 1][kAccD ? kTM : 1];  // AR: X W^T over the dense weight
 #pragma unroll
   for (int i = 0; i < kTN; ++i)
 #pragma unroll
@@ -272,7 +281,7 @@ __global__ __launch_bounds__(kThreads, AR ? (GRAN != SHERRY_PER_GROUP ? 2 : 1) :
 #pragma unroll
     for (int i = 0; i < kTN; ++i)
 #pragma unroll
-      for (int jj = 0; jj < kTM; ++jj) accd[i][jj] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int jj = 0; jj < kTM; ++jj) accd[i][jj] = f32x4{0.f, 0.f, 0.f, 0.f};  // (unused with MERGE)
   }
   int gpos = 0;  // superblocks done in the current group (its first stage zeroes accg)
 
@@ -334,7 +343,8 @@ __global__ __launch_bounds__(kThreads, AR ? (GRAN != SHERRY_PER_GROUP ? 2 : 1) :
             } else {
               acc[i][jj] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i], b, acc[i][jj], 0, 0, 0);
             }
-            if constexpr (AR) accd[i][jj] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ad[i], b, accd[i][jj], 0, 0, 0);
+            if constexpr (MERGE) acc[i][jj] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ad[i], b, acc[i][jj], 0, 0, 0);
+            else if constexpr (AR) accd[i][jj] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ad[i], b, accd[i][jj], 0, 0, 0);
           }
         }
       }
@@ -372,7 +382,7 @@ __global__ __launch_bounds__(kThreads, AR ? (GRAN != SHERRY_PER_GROUP ? 2 : 1) :
 #pragma unroll
             for (int jj = 0; jj < kTM; ++jj) {
 #pragma unroll
-              for (int e = 0; e < 4; ++e) acc[i][jj][e] += av[i][e] * accg[i][jj][e];
+              for (int e = 0; e < 4; ++e) acc[i][jj][e] += (MERGE ? av[i][e] * rlam : av[i][e]) * accg[i][jj][e];
             }
           }
           gpos = 0;
@@ -427,8 +437,12 @@ __global__ __launch_bounds__(kThreads, AR ? (GRAN != SHERRY_PER_GROUP ? 2 : 1) :
       f32x4 v;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        v[e] = acc[i][jj][e] * sc[e];
-        if constexpr (AR) v[e] += lam * accd[i][jj][e];
+        if constexpr (MERGE) {
+          v[e] = acc[i][jj][e] * lam;
+        } else {
+          v[e] = acc[i][jj][e] * sc[e];
+          if constexpr (AR) v[e] += lam * accd[i][jj][e];
+        }
       }
       if (partial != nullptr) {
         float* dst = partial + (int64_t)kz * m * n + gm * n + gn0;
@@ -499,11 +513,11 @@ __global__ __launch_bounds__(256) void gemm_split_reduce(const float* __restrict
 // the end, stay below 2^31 bytes.
 int64_t gemm_chunk_rows(int64_t k) { return ((((int64_t)1 << 31) / (2 * k) - kMaxBM) / kMaxBM) * kMaxBM; }
 
-template <int GRAN, int TM, bool AR, int TN>
+template <int GRAN, int TM, bool AR, int TN, bool MERGE = false>
 hipError_t launch_g(const GemmPlan& p, int64_t n, int64_t k, int group_sbs, const uint8_t* packed,
                     const float* alpha, const uint16_t* x, int64_t m, uint16_t* y, float* ws,
                     const uint16_t* wd, float lam, hipStream_t s) {
-  constexpr int kBM = GemmCfg<GRAN, TM, AR, TN>::kBM, kBN = GemmCfg<GRAN, TM, AR, TN>::kBN;
+  constexpr int kBM = GemmCfg<GRAN, TM, AR, TN, MERGE>::kBM, kBN = GemmCfg<GRAN, TM, AR, TN, MERGE>::kBN;
   const int64_t chunk = gemm_chunk_rows(k);
   if (chunk < kMaxBM) return hipErrorInvalidValue;
   const int tiles_n = (int)((n + kBN - 1) / kBN);
@@ -514,7 +528,7 @@ hipError_t launch_g(const GemmPlan& p, int64_t n, int64_t k, int group_sbs, cons
   for (int64_t r0 = 0; r0 < m; r0 += chunk) {
     const int64_t mc = m - r0 < chunk ? m - r0 : chunk;
     const int tiles_m = (int)((mc + kBM - 1) / kBM);
-    hipLaunchKernelGGL((gemm_kernel<GRAN, TM, AR, TN>), dim3((unsigned)(tiles_m * tiles_n), (unsigned)splits),
+    hipLaunchKernelGGL((gemm_kernel<GRAN, TM, AR, TN, MERGE>), dim3((unsigned)(tiles_m * tiles_n), (unsigned)splits),
                        dim3(kThreads), 0, s, packed, alpha, x + r0 * k, y + r0 * n, splits > 1 ? ws : nullptr, n, k,
                        mc, group_sbs, tiles_m, tiles_n, sb_per_split, wd, lam);
     hipError_t e = hipGetLastError();
@@ -588,8 +602,15 @@ hipError_t launch_arenas_gemm(const GemmPlan& p, int64_t n, int64_t k, int gran,
                               const uint16_t* x, int64_t m, uint16_t* y, float* ws, hipStream_t s) {
   if (p.tile_n != 128) return hipErrorInvalidValue;
   const int group_sbs = gran == SHERRY_PER_GROUP ? group_size / kSuperblock : 1;
-  if (gran == SHERRY_PER_GROUP)
+  if (gran == SHERRY_PER_GROUP) {
+    // the merged-accumulator kernel scales each group by alpha / lambda: used
+    // when 1 / lambda is comfortably finite (scales are means of |w|, far
+    // below 2^60 / |1 / lambda| for any realistic weight)
+    if (std::fabs(lam) >= 0x1p-60f && std::fabs(lam) <= 0x1p60f)
+      return launch_g<SHERRY_PER_GROUP, kGemmTM, true, 2, true>(p, n, k, group_sbs, packed, alpha, x, m, y, ws, wd, lam,
+                                                                s);
     return launch_g<SHERRY_PER_GROUP, kGemmTM, true, 2>(p, n, k, group_sbs, packed, alpha, x, m, y, ws, wd, lam, s);
+  }
   if (gran == SHERRY_PER_CHANNEL)
     return launch_g<SHERRY_PER_CHANNEL, kGemmTM, true, 2>(p, n, k, group_sbs, packed, alpha, x, m, y, ws, wd, lam, s);
   return launch_g<SHERRY_PER_TENSOR, kGemmTM, true, 2>(p, n, k, group_sbs, packed, alpha, x, m, y, ws, wd, lam, s);

@@ -531,6 +531,27 @@ def test_arenas_gemm_matches_oracle(n, k, m, gran):
     check_close(y, y_ref, O.tolerance_bound(xv, mag, y_ref), f"arenas {n}x{k} M={m} {gran}")
 
 
+@pytest.mark.parametrize("lam", [1e-20, 0.003, 3.0])
+def test_arenas_gemm_lambda_range(lam):
+    """per_group runs one of two kernels: for 2^-60 <= |lambda| <= 2^60 the
+    dense product accumulates with the group sums scaled by alpha / lambda,
+    times lambda at the end; outside that range (here 1e-20) three separate
+    accumulator sets.  Both against the oracle."""
+    n, k, m = 384, 1024, 96
+    w = WL.latent_weight(n, k, 995)
+    wb = WL.f32_to_bf16_bits(w)
+    pw = S.quantize_pack(dev_f32(w), "per_group", 128)
+    a = to_np(pw.alpha)
+    xb, xv = WL.activations_bf16(m, k, 996)
+    print(f"[arenas] lambda={lam}", flush=True)
+    y = O.bf16_bits_to_f32(to_np(S.arenas_gemm(pw, dev_bf16(wb), lam, dev_bf16(xb))))
+    wv = WL.bf16_bits_to_f32(wb)
+    lam32 = float(np.float32(lam))
+    y_ref = O.arenas_forward(xv, O.dequant(O.ternary(w), a, "per_group", 128), wv, lam32)
+    mag = O.alpha_per_weight(a, n, k, "per_group", 128) + np.abs(np.float32(lam32) * wv)
+    check_close(y, y_ref, O.tolerance_bound(xv, mag, y_ref), f"arenas lambda={lam}")
+
+
 def test_arenas_gemm_lambda_zero_is_the_sherry_product():
     n, k, m = 300, 1024, 70
     w = WL.latent_weight(n, k, 990)

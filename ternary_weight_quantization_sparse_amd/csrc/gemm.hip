@@ -62,6 +62,10 @@ constexpr int kMaxBM = 128;                 // largest activation tile (rows) th
 #define SHERRY_GEMM_SPLIT_TARGET 512  // split K until a launch has this many workgroups
 #endif
 constexpr int kGemmTM = 4;                  // MFMA tiles per wave along m: 64-row tiles
+#ifndef SHERRY_AR_BAND_M
+#define SHERRY_AR_BAND_M 8  // Arenas: m-tiles per band of the tile order
+#endif
+constexpr int kArBandM = SHERRY_AR_BAND_M;
 
 // Activation LDS rows are 256 bytes = 16 chunks of 16 bytes; chunk c of row r
 // sits at physical chunk c ^ (r & 15).  An MFMA operand read (a quarter wave:
@@ -151,7 +155,23 @@ __global__ __launch_bounds__(kThreads, AR ? (GRAN != SHERRY_PER_GROUP || MERGE ?
   const int tiles = tiles_m * tiles_n;
   int bid = blockIdx.x;
   if ((tiles & 7) == 0) bid = (bid & 7) * (tiles >> 3) + (bid >> 3);
-  const int tm = bid / tiles_n, tn = bid % tiles_n;
+  int tm, tn;
+  if constexpr (AR && kArBandM > 1) {
+    // The Arenas variant also streams the bf16 latent weight: per n-tile
+    // twice the bytes of an m-tile's activations.  Walking the range in bands
+    // of kArBandM m-tiles, n-major inside a band, makes the tiles resident on
+    // one XCD at a time a kArBandM x (64 / kArBandM) block that shares both
+    // operands in L2, instead of one m-tile row that re-reads all of W.
+    const int band = tiles_n * kArBandM;
+    const int first = bid / band * kArBandM;
+    const int rows = min(tiles_m - first, kArBandM);
+    const int in = bid - first * tiles_n;
+    tm = first + in % rows;
+    tn = in / rows;
+  } else {
+    tm = bid / tiles_n;
+    tn = bid % tiles_n;
+  }
   const int64_t m0 = (int64_t)tm * kBM;
   const int64_t n0 = (int64_t)tn * kBN;
   const int kz = blockIdx.y;

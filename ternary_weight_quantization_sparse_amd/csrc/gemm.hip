@@ -577,7 +577,8 @@ hipError_t launch_g(const GemmPlan& p, int64_t n, int64_t k, int group_sbs, cons
 // LLaMA-3.2-1B shapes at M = 512 and 2048, fuller launches gain nothing from
 // splitting and deeper splits lose to their shorter K loops and partial
 // traffic.  The Arenas forward (`wide` false) keeps 128-row tiles: its dense
-// weight tile already fills the LDS of one workgroup per CU.
+// weight operands, held in registers a stage ahead, leave no room for twice
+// as many weight rows per wave.
 GemmPlan plan_gemm(int64_t n, int64_t k, int gran, int group_size, int64_t m, bool wide) {
   GemmPlan p{};
   p.tile_m = GemmCfg<SHERRY_PER_GROUP, kGemmTM, false, 2>::kBM;

@@ -511,11 +511,14 @@ def test_fused_qkv_pack_and_gemv(gran, model, batch):
 
 
 # ------------------------------------------------------------------ Arenas
-@pytest.mark.parametrize("n,k,m", [(256, 512, 64), (130, 384, 129), (512, 2048, 128), (2048, 2048, 512)])
+@pytest.mark.parametrize("n,k,m", [(256, 512, 64), (130, 384, 129), (512, 2048, 128), (2048, 2048, 512),
+                                   (1000, 1024, 600), (770, 1024, 650)])
 @pytest.mark.parametrize("gran", ["per_group", "per_channel", "per_tensor"])
 def test_arenas_gemm_matches_oracle(n, k, m, gran):
     """Y = X (T alpha)^T + lambda X W^T with W the bf16 latent weight, lambda
-    from the cosine schedule; several of these shapes split K."""
+    from the cosine schedule; several of these shapes split K.  The last two
+    have 10 x 8 and 11 x 7 tiles: a short last band of 2 or 3 m-tiles in the
+    banded tile order, with and without the per-XCD ranges (77 tiles)."""
     w = WL.latent_weight(n, k, 980 + n)
     wb = WL.f32_to_bf16_bits(w)
     pw = S.quantize_pack(dev_f32(w), gran, 128)

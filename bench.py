@@ -17,7 +17,8 @@ Also reported, each timed with HIP events on the launch stream:
   compare   the same ternary layer as Sherry 1.25-bit, 3-in-5 (1.67-bit) and
             padded 2-bit, batch-1 GEMV over cold copies: time per layer pass
   gemm      prefill GEMM on the 1B layer, M = 512 and 2048 (TFLOP/s on 2MNK),
-            and the Arenas training forward (+ lambda X W^T, 4MNK)
+            the same with q/k/v and gate/up packed as fused weights (4
+            launches), and the Arenas training forward (+ lambda X W^T, 4MNK)
   quantize  Sparse-AbsMean quantize+pack of an 8192x8192 bf16 weight with 1%
             outliers x10, per_tensor / per_channel / per_group-128, rotating 4
             input copies (GB/s on bytes read + written); and the fused
@@ -474,6 +475,16 @@ def bench_gemm(pws, dev, ms, reps=20):
     lam = S.arenas_lambda(300, 1000, 0.5)
     wds = {name: dev_bf16(WL.f32_to_bf16_bits(w), dev) for (name, n, k, pw, w) in pws}
     res = {"arenas_lambda": lam}
+    # the same layer with q/k/v and gate/up each packed as one weight (they
+    # read the same activations): four launches per layer instead of seven
+    by = {p[0]: p for p in pws}
+    fused = []
+    for members in (("q", "k", "v"), ("o",), ("gate", "up"), ("down",)):
+        if len(members) == 1:
+            fused.append((members, by[members[0]][3]))
+        else:
+            fw = S.quantize_pack_fused([dev_f32(by[mb][4], dev) for mb in members], "per_group", 128)
+            fused.append((members, fw.pw))
     for m in ms:
         xb, _ = WL.activations_bf16(m, 8192, 300 + m)
         xs = {k: dev_bf16(np.ascontiguousarray(xb[:, :k]), dev) for k in (2048, 8192)}
@@ -536,6 +547,45 @@ def bench_gemm(pws, dev, ms, reps=20):
                 res[f"arenas_{m}"] = entry
             log(f"[{'arenas' if arenas else 'gemm'}] M={m}: {tf:.1f} TFLOP/s ({tf / BF16_PEAK_TFLOPS:.1%} of bf16 "
                 f"peak); all within tol: {all(c['within_tol_sampled_rows'] for c in checks)}")
+
+        # fused weights: each member's slice checked against its own packing
+        # (fused packing gives every member the codes and scales of packing
+        # it alone)
+        launches, checks, flops = [], [], []
+        for members, fpw in fused:
+            n, k = fpw.n, fpw.k
+            y = torch.empty((m, n), dtype=torch.bfloat16, device=dev)
+            b = S.workspace_bytes(3, n, k, "per_group", 128, m)
+            ws = torch.empty(max(b, 16), dtype=torch.uint8, device=dev)
+            fn = (lambda n=n, k=k, fpw=fpw, y=y, ws=ws, b=b: S.check(lib.sherry_gemm(
+                n, k, 2, 128, fpw.packed.data_ptr(), fpw.alpha.data_ptr(), xs[k].data_ptr(), m, y.data_ptr(),
+                ws.data_ptr(), b, stream())))
+            fn()
+            r0 = 0
+            for mb in members:
+                pw = by[mb][3]
+                y_ref, bound = product_reference(pw, xs[k][rows])
+                ok, ratio = within_bound(y[rows, r0:r0 + pw.n], y_ref, bound)
+                checks.append({"shape": mb, "within_tol_sampled_rows": ok, "max_err_over_bound": ratio})
+                r0 += pw.n
+            launches.append(fn)
+            flops.append(2.0 * m * n * k)
+        t_end = time.perf_counter() + 0.3
+        while time.perf_counter() < t_end:
+            for fn in launches:
+                fn()
+            torch.cuda.synchronize()
+        total, per, _ = timed_launches(launches, reps, 5)
+        times = [float(np.median(p)) for p in per]
+        tf = sum(flops) / (sum(times) * 1e-3) / 1e12
+        res[f"fused_{m}"] = {
+            "tflops": tf, "frac_of_bf16_peak": tf / BF16_PEAK_TFLOPS,
+            "launches": [{"members": list(mb), "ms": t, "tflops": f / (t * 1e-3) / 1e12}
+                         for (mb, _), t, f in zip(fused, times, flops)],
+            "checks": checks,
+        }
+        log(f"[gemm-fused] M={m}: {tf:.1f} TFLOP/s ({tf / BF16_PEAK_TFLOPS:.1%} of bf16 peak; q/k/v and gate/up "
+            f"as fused weights, 4 launches); all within tol: {all(c['within_tol_sampled_rows'] for c in checks)}")
     return res
 
 

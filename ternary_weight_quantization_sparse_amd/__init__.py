@@ -296,6 +296,12 @@ def gemv_fused(fw: FusedWeight, x, y_dtype="bfloat16", stream=None, out=None):
     return list(y.split(list(fw.sizes), dim=1))
 
 
+def gemm_fused(fw: FusedWeight, x, stream=None, out=None):
+    """Prefill product for all members in one launch; one [M, N_i] view per member."""
+    y = gemm(fw.pw, x, stream, out)
+    return list(y.split(list(fw.sizes), dim=1))
+
+
 def gemv_batched(packed_all, alpha_all, n: int, k: int, x, count: int, packed_stride: int,
                  alpha_stride: int, granularity="per_group", group_size: int = 128,
                  y_dtype="bfloat16", y=None, y_stride=None, ws=None, stream=None):

@@ -510,6 +510,27 @@ def test_fused_qkv_pack_and_gemv(gran, model, batch):
         r0 += n
 
 
+@pytest.mark.parametrize("gran", ["per_group", "per_channel"])
+def test_fused_qkv_gemm(gran):
+    """The prefill GEMM over q/k/v of a 1B layer packed as one 3072 x 2048
+    weight (one launch of 64 x 128 tiles, no K split, where k and v alone
+    split K): each member's slice within tolerance of the oracle product."""
+    members = WL.LLAMA_1B[:3]
+    ws = [WL.latent_weight(n, k, WL.layer_1b_weight_seed(i)) for i, (_, n, k) in enumerate(members)]
+    fw = S.quantize_pack_fused([dev_f32(w) for w in ws], gran, 128)
+    k = members[0][2]
+    m = 200
+    xb, xv = WL.activations_bf16(m, k, 207)
+    print(f"[gemm] fused q/k/v 1b {gran} M={m}", flush=True)
+    ys = [O.bf16_bits_to_f32(to_np(y)) for y in S.gemm_fused(fw, dev_bf16(xb))]
+    for w, (name, n, _), y in zip(ws, members, ys):
+        a_ref = O.alpha(w, gran, 128)
+        a_ref = a_ref.reshape(k // 128, n) if gran == "per_group" else a_ref.reshape(1, n)
+        y_ref = O.gemm(xv, O.dequant(O.ternary(w), a_ref, gran, 128))
+        check_close(y, y_ref, O.tolerance_bound(xv, O.alpha_per_weight(a_ref, n, k, gran, 128), y_ref),
+                    f"fused gemm {name}")
+
+
 # ------------------------------------------------------------------ Arenas
 @pytest.mark.parametrize("n,k,m", [(256, 512, 64), (130, 384, 129), (512, 2048, 128), (2048, 2048, 512),
                                    (1000, 1024, 600), (770, 1024, 650)])

@@ -555,12 +555,13 @@ def test_arenas_gemm_matches_oracle(n, k, m, gran):
     check_close(y, y_ref, O.tolerance_bound(xv, mag, y_ref), f"arenas {n}x{k} M={m} {gran}")
 
 
-@pytest.mark.parametrize("lam", [1e-20, 0.003, 3.0])
+@pytest.mark.parametrize("lam", [1e-20, 0.003, 3.0, -0.7, 1e25])
 def test_arenas_gemm_lambda_range(lam):
     """per_group runs one of two kernels: for 2^-60 <= |lambda| <= 2^60 the
     dense product accumulates with the group sums scaled by alpha / lambda,
-    times lambda at the end; outside that range (here 1e-20) three separate
-    accumulator sets.  Both against the oracle."""
+    times lambda at the end (a negative lambda included); outside that range
+    (here 1e-20 and 1e25) three separate accumulator sets.  Both against the
+    oracle."""
     n, k, m = 384, 1024, 96
     w = WL.latent_weight(n, k, 995)
     wb = WL.f32_to_bf16_bits(w)

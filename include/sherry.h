@@ -235,7 +235,9 @@ int32_t sherry_fake_quant(int64_t n, int64_t k, int32_t granularity, int32_t gro
  *   w       [N, K] bf16 row-major: the latent weight (round an fp32 master
  *           weight to bf16 first); (N + 128) * K * 2 must stay below 2^31
  *           (SHERRY_ERR_UNSUPPORTED otherwise).
- *   lambda  the residual weight for this step (finite).
+ *   lambda  the residual weight for this step, any finite value (not
+ *           checked: a NaN or infinite lambda gives NaN or infinite outputs,
+ *           as the formula does).
  *   x, m, y, workspace: as for sherry_gemm
  *           (sherry_workspace_bytes(SHERRY_OP_ARENAS_GEMM, ...)).
  * Result within 1e-3 * sum_k |X[m,k]| * (alpha(n,k) + |lambda * W[n,k]|) of

@@ -175,7 +175,7 @@ def test_unpack_8192_bf16_outliers():
 def gemv_case(n, k, wseed, xbits, xvals, gran="per_group", g=128, y_dtype="float32"):
     w = WL.latent_weight(n, k, wseed)
     pw = S.quantize_pack(dev_f32(w), gran, g)
-    a = to_np(pw.alpha)
+    a = O.alpha(w, gran, g)
     wq = O.dequant(O.ternary(w), a, gran, g)
     y = S.gemv(pw, dev_bf16(xbits), y_dtype)
     yv = to_np(y)
@@ -231,7 +231,7 @@ def test_gemv_one_hot_exact(batch):
     n, k = 192, 384
     w = WL.latent_weight(n, k, 99)
     pw = S.quantize_pack(dev_f32(w), "per_group", 128)
-    a = to_np(pw.alpha).reshape(k // 128, n)
+    a = O.alpha(w, "per_group", 128).reshape(k // 128, n)
     t = O.ternary(w)
     cols = [0, 131, 383, 200][:batch] if batch > 1 else [131]
     xv = np.zeros((batch, k), dtype=np.float32)
@@ -268,7 +268,7 @@ def test_gemv_count_strided(batch):
         packed_all[c * ps:c * ps + nbytes] = pw.packed
         alpha_all[c * as_:c * as_ + nsc] = pw.alpha
         ws.append(w)
-        refs.append(to_np(pw.alpha))
+        refs.append(O.alpha(w, "per_group", 128))
     xb, xv = WL.activations_bf16(batch, k, 600)
     y = torch.full((count, ys), 7.0, dtype=torch.float32, device=DEV)
     S.gemv_batched(packed_all, alpha_all, n, k, dev_bf16(xb), count, ps, as_, y_dtype="float32",
@@ -293,7 +293,7 @@ def test_gemv_bench_launch_configuration():
     print(f"[gemv] bench launch q x {rep.count} copies", flush=True)
     y = rep.gemv(dev_bf16(xb))
     yv = to_np(y)
-    a = to_np(pw.alpha)
+    a = O.alpha(w, "per_group", 128)
     wq = O.dequant(O.ternary(w), a, "per_group", 128)
     y_ref = O.gemv(xv, wq)
     bound = O.tolerance_bound(xv, O.alpha_per_weight(a, n, k, "per_group", 128), y_ref)
@@ -305,7 +305,7 @@ def test_gemv_bench_launch_configuration():
 def gemm_case(n, k, m, wseed, xseed, gran="per_group", g=128, rows=None):
     w = WL.latent_weight(n, k, wseed)
     pw = S.quantize_pack(dev_f32(w), gran, g)
-    a = to_np(pw.alpha)
+    a = O.alpha(w, gran, g)
     xb, xv = WL.activations_bf16(m, k, xseed)
     y = O.bf16_bits_to_f32(to_np(S.gemm(pw, dev_bf16(xb))))
     wq = O.dequant(O.ternary(w), a, gran, g)
@@ -391,7 +391,7 @@ def test_gemm_rows_past_one_launch():
     xr = x[torch.from_numpy(rows).cuda()].float().cpu().numpy().astype(np.float64)
     yr = y[torch.from_numpy(rows).cuda()].float().cpu().numpy()
     del x, y
-    a = to_np(pw.alpha)
+    a = O.alpha(w, "per_group", 128)
     wq = O.dequant(O.ternary(w), a, "per_group", 128)
     y_ref = O.gemm(xr, wq)
     bound = O.tolerance_bound(xr, O.alpha_per_weight(a, n, k, "per_group", 128), y_ref)
@@ -406,7 +406,7 @@ def test_gemm_one_hot_exact():
     n, k = 160, 256
     w = WL.latent_weight(n, k, 17)
     pw = S.quantize_pack(dev_f32(w))
-    a = to_np(pw.alpha).reshape(k // 128, n)
+    a = O.alpha(w, "per_group", 128).reshape(k // 128, n)
     t = O.ternary(w)
     xv = np.zeros((3, k), dtype=np.float32)
     cols = [0, 129, 255]
@@ -543,7 +543,7 @@ def test_arenas_gemm_matches_oracle(n, k, m, gran):
     w = WL.latent_weight(n, k, 980 + n)
     wb = WL.f32_to_bf16_bits(w)
     pw = S.quantize_pack(dev_f32(w), gran, 128)
-    a = to_np(pw.alpha)
+    a = O.alpha(w, gran, 128)
     lam = S.arenas_lambda(300, 1000, 0.5)
     assert lam == O.arenas_lambda(300, 1000, 0.5)
     xb, xv = WL.activations_bf16(m, k, 981 + m)
@@ -553,6 +553,31 @@ def test_arenas_gemm_matches_oracle(n, k, m, gran):
     y_ref = O.arenas_forward(xv, O.dequant(O.ternary(w), a, gran, 128), wv, lam)
     mag = O.alpha_per_weight(a, n, k, gran, 128) + np.abs(np.float32(lam) * wv)
     check_close(y, y_ref, O.tolerance_bound(xv, mag, y_ref), f"arenas {n}x{k} M={m} {gran}")
+
+
+@pytest.mark.parametrize("i,m", [(4, 2048), (6, 512)])
+def test_arenas_gemm_llama1b_sampled(i, m):
+    """Full 1B shapes as bench.py launches them, per_group, the schedule's
+    lambda: gate at M = 2048 (32 x 64 tiles, four bands of 8 m-tiles) and
+    down at M = 512 (K split in 4); 96 sampled output rows against the
+    oracle."""
+    name, n, k = WL.LLAMA_1B[i]
+    w = WL.latent_weight(n, k, WL.layer_1b_weight_seed(i))
+    wb = WL.f32_to_bf16_bits(w)
+    pw = S.quantize_pack(dev_f32(w), "per_group", 128)
+    lam = S.arenas_lambda(300, 1000, 0.5)
+    lam_ref = O.arenas_lambda(300, 1000, 0.5)
+    assert lam == lam_ref
+    xb, xv = WL.activations_bf16(m, k, 1300 + m)
+    rows = np.random.default_rng(1400 + i).choice(m, size=96, replace=False)
+    print(f"[arenas] 1B {name} {n}x{k} M={m} (96 sampled rows)", flush=True)
+    y = O.bf16_bits_to_f32(to_np(S.arenas_gemm(pw, dev_bf16(wb), lam, dev_bf16(xb))))[rows]
+    a = O.alpha(w, "per_group", 128)
+    wv = WL.bf16_bits_to_f32(wb)
+    xr = xv[rows]
+    y_ref = O.arenas_forward(xr, O.dequant(O.ternary(w), a, "per_group", 128), wv, lam_ref)
+    mag = O.alpha_per_weight(a, n, k, "per_group", 128) + np.abs(np.float32(lam_ref) * wv)
+    check_close(y, y_ref, O.tolerance_bound(xr, mag, y_ref), f"arenas 1B {name} M={m}")
 
 
 @pytest.mark.parametrize("lam", [1e-20, 0.003, 3.0, -0.7, 1e25])
@@ -566,7 +591,7 @@ def test_arenas_gemm_lambda_range(lam):
     w = WL.latent_weight(n, k, 995)
     wb = WL.f32_to_bf16_bits(w)
     pw = S.quantize_pack(dev_f32(w), "per_group", 128)
-    a = to_np(pw.alpha)
+    a = O.alpha(w, "per_group", 128)
     xb, xv = WL.activations_bf16(m, k, 996)
     print(f"[arenas] lambda={lam}", flush=True)
     y = O.bf16_bits_to_f32(to_np(S.arenas_gemm(pw, dev_bf16(wb), lam, dev_bf16(xb))))
@@ -612,7 +637,7 @@ def test_compare_repack_and_gemv(n, k, fmt):
             one = O.encode_2bit(t[r:r + 1]) if fmt == 0 else O.encode_tl2(t[r:r + 1])
             for g in range(nsb):
                 assert np.array_equal(got[(g * n + r) * rec:(g * n + r + 1) * rec], one[g * rec:(g + 1) * rec]), (r, g)
-    a = to_np(pw.alpha)
+    a = O.alpha(w, "per_channel", 128)
     xb, xv = WL.activations_bf16(1, k, 1201)
     print(f"[compare] fmt {fmt} {n}x{k}", flush=True)
     y = O.bf16_bits_to_f32(to_np(S.compare_gemv(fmt, planes, pw.alpha, n, k, dev_bf16(xb))))
@@ -640,7 +665,7 @@ def test_compare_gemv_count_strides(fmt):
     S.compare_gemv(fmt, allp, alla, n, k, dev_bf16(xb), count, ps, 304, y, 304)
     yv = O.bf16_bits_to_f32(to_np(y))
     for c in range(count):
-        a = to_np(pws[c].alpha)
+        a = O.alpha(ws[c], "per_channel", 128)
         y_ref = O.gemv(xv, O.dequant(O.ternary(ws[c]), a, "per_channel", 128))
         check_close(yv[c:c + 1, :n], y_ref,
                     O.tolerance_bound(xv, O.alpha_per_weight(a, n, k, "per_channel", 128), y_ref), f"copy {c}")

@@ -580,6 +580,32 @@ def test_arenas_gemm_llama1b_sampled(i, m):
     check_close(y, y_ref, O.tolerance_bound(xr, mag, y_ref), f"arenas 1B {name} M={m}")
 
 
+def test_arenas_gemm_rows_past_one_launch():
+    """The Arenas forward with X larger than 2^31 bytes: the host runs the
+    rows in several launches, each over the whole latent weight.  Rows on
+    both sides of the launch boundary and the last rows against the oracle."""
+    n, k, m = 64, 8192, 140000
+    print(f"[arenas] {n}x{k} M={m} (two launches)", flush=True)
+    w = WL.latent_weight(n, k, 972)
+    wb = WL.f32_to_bf16_bits(w)
+    pw = S.quantize_pack(dev_f32(w))
+    lam = 0.3
+    gen = torch.Generator(device="cuda").manual_seed(973)
+    x = torch.randn((m, k), generator=gen, device="cuda", dtype=torch.float32).to(torch.bfloat16)
+    y = S.arenas_gemm(pw, dev_bf16(wb), lam, x)
+    chunk = ((2 ** 31 // (2 * k) - 128) // 128) * 128
+    rows = np.array(sorted({0, 1, chunk - 2, chunk - 1, chunk, chunk + 1, m - 2, m - 1}))
+    xr = x[torch.from_numpy(rows).cuda()].float().cpu().numpy().astype(np.float64)
+    yr = O.bf16_bits_to_f32(to_np(y[torch.from_numpy(rows).cuda()]))
+    del x, y
+    a = O.alpha(w, "per_group", 128)
+    wv = WL.bf16_bits_to_f32(wb)
+    lam32 = float(np.float32(lam))
+    y_ref = O.arenas_forward(xr, O.dequant(O.ternary(w), a, "per_group", 128), wv, lam32)
+    mag = O.alpha_per_weight(a, n, k, "per_group", 128) + np.abs(np.float32(lam32) * wv)
+    check_close(yr, y_ref, O.tolerance_bound(xr, mag, y_ref), f"arenas {n}x{k} M={m}")
+
+
 @pytest.mark.parametrize("lam", [1e-20, 0.003, 3.0, -0.7, 1e25])
 def test_arenas_gemm_lambda_range(lam):
     """per_group runs one of two kernels: for 2^-60 <= |lambda| <= 2^60 the

@@ -291,6 +291,9 @@ __global__ __launch_bounds__(kLutThreads) void gemv_b1_lut_kernel(
 // table lookups and the VALU; the lookups' bytes run at about half of what
 // 8-byte lookups into this table sustain on gfx950.
 constexpr int kMfmaTiles = 4;
+#ifndef SHERRY_REDUCE4
+#define SHERRY_REDUCE4 1  // split-K sums four outputs per thread where the shape allows
+#endif
 #ifndef SHERRY_MFMA_RING
 #define SHERRY_MFMA_RING 3  // record ring slots per wave (superblocks in flight + 1)
 #endif
@@ -593,6 +596,42 @@ __global__ void gemv_split_reduce(const float* __restrict__ partial, const float
   store_y<YBF16>(y, c * y_stride + bn, v);
 }
 
+// The same sum, four consecutive outputs per thread with 16-byte loads, for
+// launches whose per-copy output count batch * n is a multiple of 4 and
+// whose total output count fits 31 bits (32-bit index arithmetic).  Same
+// split order, so the same bits.
+template <int GRAN, bool YBF16>
+__global__ __launch_bounds__(256) void gemv_split_reduce4(const float* __restrict__ partial,
+                                                          const float* __restrict__ alpha, void* __restrict__ y,
+                                                          int64_t n, int batch, int ksplit, int count,
+                                                          int64_t alpha_stride, int64_t y_stride) {
+  typedef float f4 __attribute__((ext_vector_type(4)));
+  const uint32_t per = (uint32_t)batch * (uint32_t)n;
+  const uint32_t idx = (blockIdx.x * blockDim.x + threadIdx.x) * 4u;
+  if (idx >= per * (uint32_t)count) return;
+  const uint32_t c = idx / per;
+  const uint32_t bn = idx - c * per;
+  const float* p = partial + (size_t)c * (size_t)ksplit * per + bn;
+  f4 v = {0.f, 0.f, 0.f, 0.f};
+  for (int s0 = 0; s0 < ksplit; s0 += 8) {
+    f4 t[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      t[j] = s0 + j < ksplit ? *reinterpret_cast<const f4*>(p + (size_t)(s0 + j) * per) : f4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      if (s0 + j < ksplit) v += t[j];
+  }
+  const float* al = alpha + c * alpha_stride;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    float ve = v[e];
+    if constexpr (GRAN == SHERRY_PER_CHANNEL) ve *= al[(bn + e) % (uint32_t)n];
+    if constexpr (GRAN == SHERRY_PER_TENSOR) ve *= al[0];
+    store_y<YBF16>(y, c * y_stride + bn + e, ve);
+  }
+}
+
 template <int MODE, int WIN, int M, bool YBF16>
 void launch_lut_one(dim3 grid, size_t lds, hipStream_t s, const uint8_t* packed, const float* alpha,
                     const uint16_t* x, void* y, float* ws, int64_t n, int64_t k, int group_sbs, int ksplit,
@@ -672,8 +711,14 @@ hipError_t launch_gemv_t(const GemvPlan& p, int64_t n, int64_t k, int group_size
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || p.ksplit == 1) return e;
   const int64_t items = (int64_t)count * batch * n;
-  hipLaunchKernelGGL((gemv_split_reduce<GRAN, YBF16>), dim3((unsigned)((items + 255) / 256)), dim3(256), 0,
-                     s, ws, alpha, y, n, batch, p.ksplit, count, alpha_stride, y_stride);
+  if (SHERRY_REDUCE4 && ((int64_t)batch * n) % 4 == 0 && items < ((int64_t)1 << 31)) {
+    const int64_t threads = items / 4;
+    hipLaunchKernelGGL((gemv_split_reduce4<GRAN, YBF16>), dim3((unsigned)((threads + 255) / 256)), dim3(256), 0,
+                       s, ws, alpha, y, n, batch, p.ksplit, count, alpha_stride, y_stride);
+  } else {
+    hipLaunchKernelGGL((gemv_split_reduce<GRAN, YBF16>), dim3((unsigned)((items + 255) / 256)), dim3(256), 0,
+                       s, ws, alpha, y, n, batch, p.ksplit, count, alpha_stride, y_stride);
+  }
   return hipGetLastError();
 }
 

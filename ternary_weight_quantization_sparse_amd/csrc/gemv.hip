@@ -598,8 +598,8 @@ __global__ void gemv_split_reduce(const float* __restrict__ partial, const float
 
 // The same sum, four consecutive outputs per thread with 16-byte loads, for
 // launches whose per-copy output count batch * n is a multiple of 4 and
-// whose total output count fits 31 bits (32-bit index arithmetic).  Same
-// split order, so the same bits.
+// whose total output count is at least 2^16 and fits 31 bits (32-bit index
+// arithmetic).  Same split order, so the same bits.
 template <int GRAN, bool YBF16>
 __global__ __launch_bounds__(256) void gemv_split_reduce4(const float* __restrict__ partial,
                                                           const float* __restrict__ alpha, void* __restrict__ y,
@@ -711,7 +711,11 @@ hipError_t launch_gemv_t(const GemvPlan& p, int64_t n, int64_t k, int group_size
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || p.ksplit == 1) return e;
   const int64_t items = (int64_t)count * batch * n;
-  if (SHERRY_REDUCE4 && ((int64_t)batch * n) % 4 == 0 && items < ((int64_t)1 << 31)) {
+  // four outputs per thread only for large outputs: a single call (N <= 8192
+  // outputs, often tens of splits) needs the thread count of one output per
+  // thread to keep enough loads in flight
+  if (SHERRY_REDUCE4 && ((int64_t)batch * n) % 4 == 0 && items >= ((int64_t)1 << 16) &&
+      items < ((int64_t)1 << 31)) {
     const int64_t threads = items / 4;
     hipLaunchKernelGGL((gemv_split_reduce4<GRAN, YBF16>), dim3((unsigned)((threads + 255) / 256)), dim3(256), 0,
                        s, ws, alpha, y, n, batch, p.ksplit, count, alpha_stride, y_stride);

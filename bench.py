@@ -27,8 +27,10 @@ Also reported, each timed with HIP events on the launch stream:
   gemv_3b   the 28-layer LLaMA-3.2-3B linear stack at batch 1, 4, 16 (each
             shape one launch over its 28 layers), and the same stack with
             q/k/v and gate/up packed as fused weights
-  cpu_baseline  the CPU oracle (NumPy, one thread) on a bounded sample of the
-            headline workload: one 1B layer from packed bytes to fp64 outputs.
+  cpu_baseline  the CPU oracle (NumPy, BLAS on every host core this process
+            may use) on bounded samples: one 1B layer from packed bytes to
+            fp64 outputs (the headline's unit), one 1B layer at M = 512
+            (TFLOP/s), and 4096 rows of the quantize workload (GB/s).
 Every timed configuration is first cross-checked on the GPU: products against
 an fp64 product over the library's unpacked weight, to the parity tolerance;
 quantizations for their invariants.  Parity with the CPU oracle of these same
@@ -830,19 +832,49 @@ def bench_gemv_3b(dev, batches, sweeps_per_replay=8, warm_replays=30, replays=20
     return res
 
 
-def cpu_baseline(pws, min_seconds=10.0):
-    """The oracle on a bounded sample of the headline workload: whole passes
-    over one 1B layer (7 linears, batch 1) from packed bytes to fp64 outputs,
-    repeated until ``min_seconds`` have elapsed, NumPy/BLAS held to one
-    thread."""
+def _host_cpu():
+    """Host cores this process may use, the CPU model, and the BLAS NumPy
+    calls (threadpoolctl)."""
+    cores = len(os.sched_getaffinity(0))
+    model = "unknown"
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    blas = []
+    try:
+        from threadpoolctl import threadpool_info
+        blas = [{"api": i.get("internal_api"), "threads": i.get("num_threads")} for i in threadpool_info()]
+    except Exception:  # threadpoolctl missing: report no BLAS details
+        pass
+    return cores, model, blas
+
+
+def cpu_baseline(pws, min_seconds=10.0, gemm_m=512, quant_rows=4096):
+    """The oracle, as it stands, on the host cores (BLAS threads = the cores
+    this process may use), on bounded samples of the measured workloads:
+
+    * value: whole passes over one 1B layer (7 linears, batch 1) from packed
+      bytes to fp64 outputs, repeated until ``min_seconds`` have elapsed
+      (the headline's unit and bytes definition);
+    * gemm: one pass over the 1B layer at M = ``gemm_m`` (unpack, fp64
+      dequant, fp64 product), TFLOP/s on 2MNK like the GPU rows;
+    * quantize: ``quant_rows`` rows of the 8192 x 8192 bf16 outlier weight,
+      quantize + pack (per_group 128), GB/s on bytes read + written like the
+      GPU rows."""
     import numpy as np
     import oracle as O
     import workloads as WL
     from threadpoolctl import threadpool_limits
+    cores, model, _ = _host_cpu()
     host = [(n, k, to_np(pw.packed), to_np(pw.alpha), WL.activations_bf16(1, k, 200)[1])
             for (name, n, k, pw, _) in pws]
     total_bytes, passes = 0, 0
-    with threadpool_limits(limits=1):
+    with threadpool_limits(limits=cores):
+        blas = _host_cpu()[2]
         t0 = time.perf_counter()
         while True:
             for (n, k, packed, alpha, xv) in host:
@@ -853,11 +885,38 @@ def cpu_baseline(pws, min_seconds=10.0):
             if time.perf_counter() - t0 >= min_seconds:
                 break
         secs = time.perf_counter() - t0
-    return {"value": total_bytes / secs / 1e9, "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "seconds": secs, "passes": passes,
+
+        # one 1B layer at M = gemm_m
+        flops = 0.0
+        t1 = time.perf_counter()
+        for (n, k, packed, alpha, _) in host:
+            xm = WL.activations_bf16(gemm_m, k, 300 + gemm_m)[1]
+            t = O.decode_codes(O.unpack(packed, n, k))
+            O.gemm(xm, O.dequant(t, alpha, "per_group", 128))
+            flops += 2.0 * gemm_m * n * k
+        gemm_secs = time.perf_counter() - t1
+
+        # quantize + pack of a row sample of the 8192 x 8192 bf16 weight
+        _, wv = WL.latent_weight_outliers_bf16(8192, 8192, 5000)
+        ws = np.ascontiguousarray(wv[:quant_rows])
+        del wv
+        t2 = time.perf_counter()
+        packed_q, alpha_q = O.quantize_pack(ws, "per_group", 128)
+        q_secs = time.perf_counter() - t2
+        q_bytes = ws.size * 2 + packed_q.size + alpha_q.size * 4
+    return {"value": total_bytes / secs / 1e9, "unit": "GB/s", "cores": cores, "kind": "oracle",
+            "cpu_model": model, "blas": blas, "seconds": secs, "passes": passes,
             "sample": f"{passes} passes over one LLaMA-3.2-1B layer (7 linears, batch 1, group 128): "
-                      "packed bytes -> unpack -> fp64 dequant -> fp64 product, NumPy with BLAS held to "
-                      "1 thread; same algorithmic-bytes definition as the headline"}
+                      f"packed bytes -> unpack -> fp64 dequant -> fp64 product, NumPy with BLAS on {cores} "
+                      "threads; same algorithmic-bytes definition as the headline",
+            "gemm": {"value": flops / gemm_secs / 1e12, "unit": "TFLOP/s", "seconds": gemm_secs,
+                     "sample": f"one LLaMA-3.2-1B layer (7 linears) at M = {gemm_m}: unpack, fp64 dequant, "
+                               "fp64 product (2MNK flops, as the GPU GEMM rows)"},
+            "quantize": {"value": q_bytes / q_secs / 1e9, "unit": "GB/s", "seconds": q_secs,
+                         "gweights_per_s": ws.size / q_secs / 1e9,
+                         "sample": f"{quant_rows} of the 8192 rows of the 8192 x 8192 bf16 weight with 1% "
+                                   "outliers x10, per_group 128 quantize + pack (bytes read + written, as "
+                                   "the GPU quantize rows)"}}
 
 
 # ----------------------------------------------------------------------------
@@ -909,7 +968,9 @@ def main():
         del src, dst
     cpu = cpu_baseline(pws) if "cpu" in sections else None
     if cpu:
-        log(f"[cpu] oracle {cpu['value']:.3f} GB/s in {cpu['seconds']:.1f} s (1 thread)")
+        log(f"[cpu] oracle {cpu['value']:.3f} GB/s in {cpu['seconds']:.1f} s ({cpu['cores']} cores, "
+            f"{cpu['cpu_model']}); GEMM {cpu['gemm']['value']:.4f} TFLOP/s; quantize "
+            f"{cpu['quantize']['value']:.4f} GB/s")
 
     ctr = counters_for_current_source()
     traffic = None

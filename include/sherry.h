@@ -51,7 +51,7 @@
 extern "C" {
 #endif
 
-#define SHERRY_ABI_VERSION 1
+#define SHERRY_ABI_VERSION 2
 
 /* Status codes. */
 typedef enum {
@@ -228,8 +228,8 @@ int32_t sherry_fake_quant(int64_t n, int64_t k, int32_t granularity, int32_t gro
  * Quantization via Fine-grained Sparsification", agihunt digest, the
  * weight-trapping paragraph: the residual weight lambda_t decays to 0 on a
  * cosine schedule and is gone at inference).  One kernel runs both products
- * in the same K loop on bf16 MFMA with fp32 accumulation; the schedule is the
- * caller's (the Python binding has it).
+ * in the same K loop on bf16 MFMA with fp32 accumulation; the residual weight
+ * of a step comes from sherry_arenas_lambda (below) or from the caller.
  *
  *   packed, alpha   the quantized weight, as for sherry_gemm.
  *   w       [N, K] bf16 row-major: the latent weight (round an fp32 master
@@ -247,6 +247,21 @@ int32_t sherry_arenas_gemm(int64_t n, int64_t k, int32_t granularity, int32_t gr
                            const void* packed, const float* alpha, const void* w, float lambda,
                            const void* x, int64_t m, void* y, void* workspace, size_t workspace_bytes,
                            void* stream);
+
+/*
+ * sherry_arenas_lambda -- the residual weight of the Arenas forward at a
+ * training step: the weight decays from lambda0 to 0 along half a cosine wave
+ * over the annealing steps and is gone afterwards, so inference runs the
+ * plain Sherry product ("Sherry: Hardware-Efficient 1.25-Bit Ternary
+ * Quantization via Fine-grained Sparsification", agihunt digest, the
+ * weight-trapping paragraph).
+ *
+ *   returns lambda0 * (1 + cos(pi * step / total_steps)) / 2 in fp64 for
+ *   step < total_steps, and 0 when step >= total_steps or total_steps <= 0.
+ *   Host arithmetic only: no device, no stream, no error status.  Pass the
+ *   result (rounded to fp32) as sherry_arenas_gemm's lambda.
+ */
+double sherry_arenas_lambda(int64_t step, int64_t total_steps, double lambda0);
 
 /*
  * Comparison packings of the same ternary matrix -- the two ways of storing

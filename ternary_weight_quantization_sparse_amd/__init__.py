@@ -22,7 +22,7 @@ __all__ = [
     "PackedWeight", "quantize_pack", "unpack", "gemv", "gemm", "packed_bytes", "num_scales",
     "workspace_bytes", "SherryError", "load", "fake_quant", "fake_quant_ste", "gemv_batched",
     "FusedWeight", "quantize_pack_fused", "gemv_fused", "arenas_lambda", "arenas_gemm",
-    "compare_repack", "compare_gemv",
+    "compare_repack", "compare_gemv", "gemm_fused",
 ]
 
 
@@ -37,6 +37,14 @@ def _stream(stream):
     return s.cuda_stream
 
 
+def _on_stream(stream):
+    """Context in which the binding allocates its temporaries: the caller's
+    stream when one is given, so the caching allocator never hands a
+    workspace or a copy to another stream while the kernels still use it."""
+    import contextlib
+    return _torch().cuda.stream(stream) if stream is not None else contextlib.nullcontext()
+
+
 def _ptr(t):
     return None if t is None else t.data_ptr()
 
@@ -48,6 +56,53 @@ def _gran(granularity) -> int:
         return _lib.GRANULARITY[granularity]
     except KeyError:
         raise ValueError(f"unsupported granularity: {granularity!r}") from None
+
+
+def _need_gpu(t, name, device=None):
+    """Every tensor handed to the library must live on the GPU (and on the
+    same one as the weight): the kernels dereference its address."""
+    if not getattr(t, "is_cuda", False):
+        raise ValueError(f"{name} must be a CUDA (HIP) tensor")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+
+
+def _need_out(t, name, dtype, numel, device):
+    """A caller-supplied output: right dtype and device, contiguous, at least
+    ``numel`` elements (the library cannot see buffer sizes)."""
+    _need_gpu(t, name, device)
+    if t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if t.numel() < numel:
+        raise ValueError(f"{name} holds {t.numel()} elements, {numel} needed")
+
+
+def _check_pw(pw):
+    """Packed planes and scales of the sizes their shape implies."""
+    torch = _torch()
+    _need_gpu(pw.packed, "packed")
+    _need_gpu(pw.alpha, "alpha", pw.packed.device)
+    lib = load()
+    nbytes = int(lib.sherry_packed_bytes(pw.n, pw.k))
+    nsc = int(lib.sherry_num_scales(pw.n, pw.k, _gran(pw.granularity), pw.group_size))
+    if pw.packed.dtype != torch.uint8 or not pw.packed.is_contiguous() or pw.packed.numel() < nbytes:
+        raise ValueError(f"packed must be a contiguous uint8 tensor of {nbytes} bytes")
+    if pw.alpha.dtype != torch.float32 or not pw.alpha.is_contiguous() or pw.alpha.numel() < max(nsc, 0):
+        raise ValueError(f"alpha must be a contiguous float32 tensor of {nsc} scales")
+
+
+def _activations(x, k, device, rank=2):
+    """bf16 activations [rows, K] on the weight's device (a copy only if x is
+    not contiguous)."""
+    torch = _torch()
+    _need_gpu(x, "x", device)
+    if x.dtype != torch.bfloat16:
+        raise ValueError("x must be bfloat16")
+    if x.dim() != rank or x.shape[-1] != k:
+        raise ValueError(f"x must be [rows, {k}], got {tuple(x.shape)}")
+    return x.contiguous()
 
 
 def packed_bytes(n: int, k: int) -> int:
@@ -90,21 +145,23 @@ def quantize_pack(w, granularity: str = "per_group", group_size: int = 128, stre
     torch = _torch()
     if w.dim() != 2:
         raise ValueError("Sherry quantization expects a 2-D weight")
+    _need_gpu(w, "w")
     n, k = w.shape
     gran = _gran(granularity)
     dtype = {torch.float32: _lib.F32, torch.bfloat16: _lib.BF16}.get(w.dtype)
     if dtype is None:
         raise ValueError("w must be float32 or bfloat16")
-    w = w.contiguous()
     lib = load()
     nbytes = int(lib.sherry_packed_bytes(n, k))
     nsc = int(lib.sherry_num_scales(n, k, gran, group_size))
-    packed = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=w.device)
-    alpha = torch.empty(max(nsc, 1), dtype=torch.float32, device=w.device)
     ws_bytes = int(lib.sherry_workspace_bytes(_lib.OP_QUANTIZE_PACK, n, k, gran, group_size, 1, 1))
-    ws = _workspace(ws_bytes if ws_bytes != (1 << 64) - 1 else 0, w.device)
-    check(lib.sherry_quantize_pack(n, k, gran, group_size, _ptr(w), dtype, _ptr(packed), _ptr(alpha),
-                                   _ptr(ws), 0 if ws is None else ws.numel(), _stream(stream)))
+    with _on_stream(stream):
+        w = w.contiguous()
+        packed = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=w.device)
+        alpha = torch.empty(max(nsc, 1), dtype=torch.float32, device=w.device)
+        ws = _workspace(ws_bytes if ws_bytes != (1 << 64) - 1 else 0, w.device)
+        check(lib.sherry_quantize_pack(n, k, gran, group_size, _ptr(w), dtype, _ptr(packed), _ptr(alpha),
+                                       _ptr(ws), 0 if ws is None else ws.numel(), _stream(stream)))
     return PackedWeight(packed[:nbytes], alpha[:nsc], n, k, granularity, group_size)
 
 
@@ -115,6 +172,7 @@ def fake_quant(w, granularity: str = "per_group", group_size: int = 128, out_dty
     torch = _torch()
     if w.dim() != 2:
         raise ValueError("Sherry quantization expects a 2-D weight")
+    _need_gpu(w, "w")
     n, k = w.shape
     gran = _gran(granularity)
     dtype = {torch.float32: _lib.F32, torch.bfloat16: _lib.BF16}.get(w.dtype)
@@ -124,15 +182,16 @@ def fake_quant(w, granularity: str = "per_group", group_size: int = 128, out_dty
     ocode = {torch.float32: _lib.F32, torch.bfloat16: _lib.BF16}.get(odt)
     if ocode is None:
         raise ValueError("out_dtype must be float32 or bfloat16")
-    w = w.contiguous()
     lib = load()
     nsc = int(lib.sherry_num_scales(n, k, gran, group_size))
-    out = torch.empty((n, k), dtype=odt, device=w.device)
-    alpha = torch.empty(max(nsc, 1), dtype=torch.float32, device=w.device)
     ws_bytes = int(lib.sherry_workspace_bytes(_lib.OP_FAKE_QUANT, n, k, gran, group_size, 1, 1))
-    ws = _workspace(ws_bytes if ws_bytes != (1 << 64) - 1 else 0, w.device)
-    check(lib.sherry_fake_quant(n, k, gran, group_size, _ptr(w), dtype, _ptr(out), ocode, _ptr(alpha),
-                                _ptr(ws), 0 if ws is None else ws.numel(), _stream(stream)))
+    with _on_stream(stream):
+        w = w.contiguous()
+        out = torch.empty((n, k), dtype=odt, device=w.device)
+        alpha = torch.empty(max(nsc, 1), dtype=torch.float32, device=w.device)
+        ws = _workspace(ws_bytes if ws_bytes != (1 << 64) - 1 else 0, w.device)
+        check(lib.sherry_fake_quant(n, k, gran, group_size, _ptr(w), dtype, _ptr(out), ocode, _ptr(alpha),
+                                    _ptr(ws), 0 if ws is None else ws.numel(), _stream(stream)))
     return out, alpha[:nsc]
 
 
@@ -175,43 +234,54 @@ def unpack(pw: PackedWeight, out_dtype="int8", stream=None):
     torch = _torch()
     tdt, code = {"int8": (torch.int8, _lib.I8), "float32": (torch.float32, _lib.F32),
                  "bfloat16": (torch.bfloat16, _lib.BF16)}[str(out_dtype).replace("torch.", "")]
-    out = torch.empty((pw.n, pw.k), dtype=tdt, device=pw.packed.device)
-    check(load().sherry_unpack(pw.n, pw.k, _gran(pw.granularity), pw.group_size, _ptr(pw.packed),
-                               _ptr(pw.alpha), _ptr(out), code, _stream(stream)))
+    _check_pw(pw)
+    with _on_stream(stream):
+        out = torch.empty((pw.n, pw.k), dtype=tdt, device=pw.packed.device)
+        check(load().sherry_unpack(pw.n, pw.k, _gran(pw.granularity), pw.group_size, _ptr(pw.packed),
+                                   _ptr(pw.alpha), _ptr(out), code, _stream(stream)))
     return out
+
+
+_Y_DTYPES = {"bfloat16": _lib.BF16, "float32": _lib.F32}
+
+
+def _y_dtype(y_dtype):
+    torch = _torch()
+    key = str(y_dtype).replace("torch.", "")
+    if key not in _Y_DTYPES:
+        raise ValueError("y_dtype must be bfloat16 or float32")
+    return getattr(torch, key), _Y_DTYPES[key]
 
 
 def gemv(pw: PackedWeight, x, y_dtype="bfloat16", stream=None, out=None):
     """y = x @ (T*alpha)^T for a decode batch ``x`` [B, K] bf16 (B = 1..16)."""
     torch = _torch()
+    _check_pw(pw)
+    dev = pw.packed.device
     if x.dim() == 1:
         x = x.unsqueeze(0)
-    if x.dtype != torch.bfloat16:
-        raise ValueError("x must be bfloat16")
-    x = x.contiguous()
-    b = x.shape[0]
-    ydt, code = {"bfloat16": (torch.bfloat16, _lib.BF16), "float32": (torch.float32, _lib.F32)}[
-        str(y_dtype).replace("torch.", "")]
-    y = out if out is not None else torch.empty((b, pw.n), dtype=ydt, device=x.device)
+    ydt, code = _y_dtype(y_dtype)
     gran = _gran(pw.granularity)
     lib = load()
-    ws_bytes = int(lib.sherry_workspace_bytes(_lib.OP_GEMV, pw.n, pw.k, gran, pw.group_size, b, 1))
-    ws = _workspace(ws_bytes if ws_bytes != (1 << 64) - 1 else 0, x.device)
-    check(lib.sherry_gemv(pw.n, pw.k, gran, pw.group_size, _ptr(pw.packed), _ptr(pw.alpha), _ptr(x), b,
-                          _ptr(y), code, 1, 0, 0, 0, _ptr(ws), 0 if ws is None else ws.numel(),
-                          _stream(stream)))
+    with _on_stream(stream):
+        x = _activations(x, pw.k, dev)
+        b = x.shape[0]
+        if out is not None:
+            _need_out(out, "out", ydt, b * pw.n, dev)
+        y = out if out is not None else torch.empty((b, pw.n), dtype=ydt, device=dev)
+        ws_bytes = int(lib.sherry_workspace_bytes(_lib.OP_GEMV, pw.n, pw.k, gran, pw.group_size, b, 1))
+        ws = _workspace(ws_bytes if ws_bytes != (1 << 64) - 1 else 0, dev)
+        check(lib.sherry_gemv(pw.n, pw.k, gran, pw.group_size, _ptr(pw.packed), _ptr(pw.alpha), _ptr(x), b,
+                              _ptr(y), code, 1, 0, 0, 0, _ptr(ws), 0 if ws is None else ws.numel(),
+                              _stream(stream)))
     return y
 
 
 def arenas_lambda(step: int, total_steps: int, lambda0: float) -> float:
-    """Cosine-annealed residual weight of the Arenas forward: lambda0 at step 0,
-    0 at ``total_steps`` and after ("Sherry: Hardware-Efficient 1.25-Bit
-    Ternary Quantization via Fine-grained Sparsification", agihunt digest,
-    weight-trapping paragraph)."""
-    import math
-    if total_steps <= 0 or step >= total_steps:
-        return 0.0
-    return lambda0 * 0.5 * (1.0 + math.cos(math.pi * step / total_steps))
+    """Cosine-annealed residual weight of the Arenas forward (lambda0 at step
+    0, 0 at ``total_steps`` and after), computed by the library's
+    ``sherry_arenas_lambda``."""
+    return float(load().sherry_arenas_lambda(int(step), int(total_steps), float(lambda0)))
 
 
 def arenas_gemm(pw: PackedWeight, w, lam: float, x, stream=None, out=None):
@@ -219,21 +289,25 @@ def arenas_gemm(pw: PackedWeight, w, lam: float, x, stream=None, out=None):
     activations ``x`` [M, K] bf16 and the latent weight ``w`` [N, K] (bf16;
     an fp32 master weight is rounded to bf16 here) -> [M, N] bf16."""
     torch = _torch()
-    if x.dtype != torch.bfloat16 or x.dim() != 2:
-        raise ValueError("x must be a 2-D bfloat16 tensor")
+    _check_pw(pw)
+    dev = pw.packed.device
     if tuple(w.shape) != (pw.n, pw.k):
         raise ValueError("w must be [N, K] of the packed weight")
-    wb = w.to(torch.bfloat16).contiguous()
-    x = x.contiguous()
-    m = x.shape[0]
-    y = out if out is not None else torch.empty((m, pw.n), dtype=torch.bfloat16, device=x.device)
+    _need_gpu(w, "w", dev)
     gran = _gran(pw.granularity)
     lib = load()
-    ws_bytes = int(lib.sherry_workspace_bytes(_lib.OP_ARENAS_GEMM, pw.n, pw.k, gran, pw.group_size, m, 1))
-    ws = _workspace(ws_bytes if ws_bytes != (1 << 64) - 1 else 0, x.device)
-    check(lib.sherry_arenas_gemm(pw.n, pw.k, gran, pw.group_size, _ptr(pw.packed), _ptr(pw.alpha), _ptr(wb),
-                                 float(lam), _ptr(x), m, _ptr(y), _ptr(ws), 0 if ws is None else ws.numel(),
-                                 _stream(stream)))
+    with _on_stream(stream):
+        x = _activations(x, pw.k, dev)
+        wb = w.to(torch.bfloat16).contiguous()
+        m = x.shape[0]
+        if out is not None:
+            _need_out(out, "out", torch.bfloat16, m * pw.n, dev)
+        y = out if out is not None else torch.empty((m, pw.n), dtype=torch.bfloat16, device=dev)
+        ws_bytes = int(lib.sherry_workspace_bytes(_lib.OP_ARENAS_GEMM, pw.n, pw.k, gran, pw.group_size, m, 1))
+        ws = _workspace(ws_bytes if ws_bytes != (1 << 64) - 1 else 0, dev)
+        check(lib.sherry_arenas_gemm(pw.n, pw.k, gran, pw.group_size, _ptr(pw.packed), _ptr(pw.alpha), _ptr(wb),
+                                     float(lam), _ptr(x), m, _ptr(y), _ptr(ws), 0 if ws is None else ws.numel(),
+                                     _stream(stream)))
     return y
 
 
@@ -241,12 +315,14 @@ def compare_repack(pw: PackedWeight, fmt: int, stream=None):
     """Re-encode a packed weight as padded 2-bit (fmt 0) or three weights in 5
     bits (fmt 1): the comparison packings of the same ternary matrix."""
     torch = _torch()
+    _check_pw(pw)
     lib = load()
     nbytes = int(lib.sherry_compare_bytes(fmt, pw.n, pw.k))
     if nbytes == 0:
         raise ValueError("invalid comparison format or shape")
-    out = torch.empty(nbytes, dtype=torch.uint8, device=pw.packed.device)
-    check(lib.sherry_compare_repack(fmt, pw.n, pw.k, _ptr(pw.packed), _ptr(out), _stream(stream)))
+    with _on_stream(stream):
+        out = torch.empty(nbytes, dtype=torch.uint8, device=pw.packed.device)
+        check(lib.sherry_compare_repack(fmt, pw.n, pw.k, _ptr(pw.packed), _ptr(out), _stream(stream)))
     return out
 
 
@@ -254,13 +330,26 @@ def compare_gemv(fmt: int, planes, alpha, n: int, k: int, x, count: int = 1, pla
                  alpha_stride: int = 0, y=None, y_stride: int = 0, stream=None):
     """Batch-1 GEMV over a comparison packing with per-channel scales."""
     torch = _torch()
+    lib = load()
+    nbytes = int(lib.sherry_compare_bytes(fmt, n, k))
+    if nbytes == 0:
+        raise ValueError("invalid comparison format or shape")
+    if count < 1:
+        raise ValueError("count must be >= 1")
+    _need_out(planes, "planes", torch.uint8, (count - 1) * planes_stride + nbytes, planes.device)
+    dev = planes.device
+    _need_out(alpha, "alpha", torch.float32, (count - 1) * alpha_stride + n, dev)
     if x.dim() == 2:
         x = x.reshape(-1)
-    if y is None:
-        y = torch.empty((count, n), dtype=torch.bfloat16, device=x.device)
-        y_stride = n
-    check(load().sherry_compare_gemv(fmt, n, k, _ptr(planes), _ptr(alpha), _ptr(x), _ptr(y), count,
-                                     planes_stride, alpha_stride, y_stride, _stream(stream)))
+    with _on_stream(stream):
+        x = _activations(x, k, dev, rank=1)
+        if y is None:
+            y = torch.empty((count, n), dtype=torch.bfloat16, device=dev)
+            y_stride = n
+        else:
+            _need_out(y, "y", torch.bfloat16, (count - 1) * y_stride + n, dev)
+        check(lib.sherry_compare_gemv(fmt, n, k, _ptr(planes), _ptr(alpha), _ptr(x), _ptr(y), count,
+                                      planes_stride, alpha_stride, y_stride, _stream(stream)))
     return y
 
 
@@ -285,7 +374,8 @@ def quantize_pack_fused(weights, granularity: str = "per_group", group_size: int
     ks = {int(w.shape[1]) for w in weights}
     if len(ks) != 1:
         raise ValueError("fused members must share K")
-    w = torch.cat([t.contiguous() for t in weights], dim=0)
+    with _on_stream(stream):
+        w = torch.cat([t.contiguous() for t in weights], dim=0)
     pw = quantize_pack(w, granularity, group_size, stream)
     return FusedWeight(pw, tuple(int(t.shape[0]) for t in weights))
 
@@ -309,38 +399,57 @@ def gemv_batched(packed_all, alpha_all, n: int, k: int, x, count: int, packed_st
     matrix c reads ``packed_all`` at byte c*packed_stride and ``alpha_all`` at
     element c*alpha_stride, and writes y[c]."""
     torch = _torch()
-    if x.dim() == 1:
-        x = x.unsqueeze(0)
-    b = x.shape[0]
-    ydt, code = {"bfloat16": (torch.bfloat16, _lib.BF16), "float32": (torch.float32, _lib.F32)}[
-        str(y_dtype).replace("torch.", "")]
-    if y_stride is None:
-        y_stride = b * n
-    if y is None:
-        y = torch.empty((count, y_stride), dtype=ydt, device=x.device)
     gran = _gran(granularity)
     lib = load()
-    if ws is None:
+    nbytes = int(lib.sherry_packed_bytes(n, k))
+    nsc = int(lib.sherry_num_scales(n, k, gran, group_size))
+    if nbytes == 0 or nsc < 0:
+        raise ValueError("invalid shape, granularity or group size")
+    if count < 1:
+        raise ValueError("count must be >= 1")
+    dev = packed_all.device
+    _need_out(packed_all, "packed_all", torch.uint8, (count - 1) * packed_stride + nbytes, dev)
+    _need_out(alpha_all, "alpha_all", torch.float32, (count - 1) * alpha_stride + nsc, dev)
+    if x.dim() == 1:
+        x = x.unsqueeze(0)
+    ydt, code = _y_dtype(y_dtype)
+    with _on_stream(stream):
+        x = _activations(x, k, dev)
+        b = x.shape[0]
+        if y_stride is None:
+            y_stride = b * n
+        if y is None:
+            y = torch.empty((count, y_stride), dtype=ydt, device=dev)
+        else:
+            _need_out(y, "y", ydt, (count - 1) * y_stride + b * n, dev)
         ws_bytes = int(lib.sherry_workspace_bytes(_lib.OP_GEMV, n, k, gran, group_size, b, count))
-        ws = _workspace(ws_bytes, x.device)
-    check(lib.sherry_gemv(n, k, gran, group_size, _ptr(packed_all), _ptr(alpha_all), _ptr(x), b, _ptr(y),
-                          code, count, packed_stride, alpha_stride, y_stride, _ptr(ws),
-                          0 if ws is None else ws.numel(), _stream(stream)))
+        if ws_bytes == (1 << 64) - 1:
+            raise ValueError("invalid batch or count")
+        if ws is None:
+            ws = _workspace(ws_bytes, dev)
+        elif ws_bytes:
+            _need_out(ws, "ws", torch.uint8, ws_bytes, dev)
+        check(lib.sherry_gemv(n, k, gran, group_size, _ptr(packed_all), _ptr(alpha_all), _ptr(x), b, _ptr(y),
+                              code, count, packed_stride, alpha_stride, y_stride, _ptr(ws),
+                              0 if ws is None else ws.numel(), _stream(stream)))
     return y
 
 
 def gemm(pw: PackedWeight, x, stream=None, out=None):
     """Y = X @ (T*alpha)^T for prefill activations ``x`` [M, K] bf16 -> [M, N] bf16."""
     torch = _torch()
-    if x.dtype != torch.bfloat16 or x.dim() != 2:
-        raise ValueError("x must be a 2-D bfloat16 tensor")
-    x = x.contiguous()
-    m = x.shape[0]
-    y = out if out is not None else torch.empty((m, pw.n), dtype=torch.bfloat16, device=x.device)
+    _check_pw(pw)
+    dev = pw.packed.device
     gran = _gran(pw.granularity)
     lib = load()
-    ws_bytes = int(lib.sherry_workspace_bytes(_lib.OP_GEMM, pw.n, pw.k, gran, pw.group_size, m, 1))
-    ws = _workspace(ws_bytes if ws_bytes != (1 << 64) - 1 else 0, x.device)
-    check(lib.sherry_gemm(pw.n, pw.k, gran, pw.group_size, _ptr(pw.packed), _ptr(pw.alpha), _ptr(x), m,
-                          _ptr(y), _ptr(ws), 0 if ws is None else ws.numel(), _stream(stream)))
+    with _on_stream(stream):
+        x = _activations(x, pw.k, dev)
+        m = x.shape[0]
+        if out is not None:
+            _need_out(out, "out", torch.bfloat16, m * pw.n, dev)
+        y = out if out is not None else torch.empty((m, pw.n), dtype=torch.bfloat16, device=dev)
+        ws_bytes = int(lib.sherry_workspace_bytes(_lib.OP_GEMM, pw.n, pw.k, gran, pw.group_size, m, 1))
+        ws = _workspace(ws_bytes if ws_bytes != (1 << 64) - 1 else 0, dev)
+        check(lib.sherry_gemm(pw.n, pw.k, gran, pw.group_size, _ptr(pw.packed), _ptr(pw.alpha), _ptr(x), m,
+                              _ptr(y), _ptr(ws), 0 if ws is None else ws.numel(), _stream(stream)))
     return y

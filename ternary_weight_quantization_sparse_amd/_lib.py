@@ -29,7 +29,7 @@ SYMBOLS = (
     "sherry_abi_version", "sherry_status_string", "sherry_packed_bytes", "sherry_num_scales",
     "sherry_workspace_bytes", "sherry_quantize_pack", "sherry_unpack", "sherry_gemv", "sherry_gemm",
     "sherry_fake_quant", "sherry_arenas_gemm", "sherry_compare_bytes", "sherry_compare_repack",
-    "sherry_compare_gemv",
+    "sherry_compare_gemv", "sherry_arenas_lambda",
 )
 
 _i32, _i64, _sz, _vp = ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t, ctypes.c_void_p
@@ -48,6 +48,7 @@ _SIGNATURES = {
     "sherry_fake_quant": ([_i64, _i64, _i32, _i32, _vp, _i32, _vp, _i32, _vp, _vp, _sz, _vp], _i32),
     "sherry_arenas_gemm": ([_i64, _i64, _i32, _i32, _vp, _vp, _vp, ctypes.c_float, _vp, _i64, _vp, _vp, _sz, _vp],
                            _i32),
+    "sherry_arenas_lambda": ([_i64, _i64, ctypes.c_double], ctypes.c_double),
     "sherry_compare_bytes": ([_i32, _i64, _i64], _sz),
     "sherry_compare_repack": ([_i32, _i64, _i64, _vp, _vp, _vp], _i32),
     "sherry_compare_gemv": ([_i32, _i64, _i64, _vp, _vp, _vp, _vp, _i32, _i64, _i64, _i64, _vp], _i32),

@@ -8,6 +8,7 @@
 // the HIP runtime map to SHERRY_ERR_HIP.
 #include <hip/hip_runtime.h>
 
+#include <cmath>
 #include <cstdint>
 
 #include "sherry_internal.h"
@@ -217,6 +218,12 @@ int32_t sherry_arenas_gemm(int64_t n, int64_t k, int32_t granularity, int32_t gr
                                        alpha, static_cast<const uint16_t*>(w), lambda,
                                        static_cast<const uint16_t*>(x), m, static_cast<uint16_t*>(y),
                                        static_cast<float*>(workspace), static_cast<hipStream_t>(stream)));
+}
+
+double sherry_arenas_lambda(int64_t step, int64_t total_steps, double lambda0) {
+  if (total_steps <= 0 || step >= total_steps) return 0.0;
+  const double pi = 3.141592653589793;
+  return lambda0 * 0.5 * (1.0 + std::cos(pi * (double)step / (double)total_steps));
 }
 
 size_t sherry_compare_bytes(int32_t format, int64_t n, int64_t k) {

@@ -35,14 +35,14 @@ def _declared_symbols():
 
 def test_exports_every_declared_symbol(lib):
     declared = _declared_symbols()
-    assert len(declared) == 14
+    assert len(declared) == 15
     assert set(declared) == set(L.SYMBOLS)
     for name in declared:
         assert hasattr(lib, name), name
 
 
 def test_version_and_status_strings(lib):
-    assert lib.sherry_abi_version() == 1
+    assert lib.sherry_abi_version() == 2
     for code in range(11):
         assert lib.sherry_status_string(code).decode().startswith("SHERRY_")
     assert b"unknown" in lib.sherry_status_string(99)
@@ -236,3 +236,42 @@ def test_binding_raises_value_error():
     with pytest.raises(S.SherryError):
         L.check(L.ERR_HIP)
     L.check(L.OK)
+
+
+def test_arenas_lambda_matches_oracle(lib):
+    """The library's cosine schedule against the oracle's, whose values are
+    pinned in tests/test_oracle_matmul.py (lambda0 at t = 0, lambda0 (1/2 +
+    sqrt(2)/4) at T/4, lambda0 / 2 at T/2, 0 at and after T); the binding
+    returns the library's value."""
+    import math
+    import oracle as O
+    lam0, T = 0.75, 1000
+    assert lib.sherry_arenas_lambda(0, T, lam0) == lam0
+    assert abs(lib.sherry_arenas_lambda(T // 4, T, lam0) - lam0 * (0.5 + math.sqrt(2.0) / 4)) < 1e-15
+    assert abs(lib.sherry_arenas_lambda(T // 2, T, lam0) - lam0 / 2) < 1e-15
+    assert lib.sherry_arenas_lambda(T, T, lam0) == 0.0
+    assert lib.sherry_arenas_lambda(T + 5, T, lam0) == 0.0
+    assert lib.sherry_arenas_lambda(3, 0, lam0) == 0.0
+    for t in range(0, T + 7, 13):
+        assert lib.sherry_arenas_lambda(t, T, lam0) == O.arenas_lambda(t, T, lam0), t
+        assert S.arenas_lambda(t, T, lam0) == O.arenas_lambda(t, T, lam0), t
+    assert lib.sherry_arenas_lambda(300, 1000, -2.5) == O.arenas_lambda(300, 1000, -2.5)
+
+
+def test_binding_rejects_host_tensors():
+    """The binding refuses tensors that are not on the GPU before calling
+    the library: the kernels would dereference a host address."""
+    torch = pytest.importorskip("torch")
+    w = torch.zeros((64, 256))
+    with pytest.raises(ValueError, match="CUDA"):
+        S.quantize_pack(w)
+    with pytest.raises(ValueError, match="CUDA"):
+        S.fake_quant(w)
+    pw = S.PackedWeight(torch.zeros(64 * 256 * 5 // 32, dtype=torch.uint8), torch.zeros(128), 64, 256)
+    x = torch.zeros((1, 256), dtype=torch.bfloat16)
+    for call in (lambda: S.gemv(pw, x), lambda: S.gemm(pw, x), lambda: S.unpack(pw),
+                 lambda: S.arenas_gemm(pw, w, 0.5, x), lambda: S.compare_repack(pw, 0),
+                 lambda: S.gemv_batched(pw.packed, pw.alpha, 64, 256, x, 1, 0, 0),
+                 lambda: S.compare_gemv(0, pw.packed, pw.alpha, 64, 256, x)):
+        with pytest.raises(ValueError):
+            call()

@@ -323,7 +323,7 @@ def test_gemm_llama1b_m512(i):
     gemm_case(n, k, 512, WL.layer_1b_weight_seed(i), 812)
 
 
-@pytest.mark.parametrize("i", [0, 4, 6])
+@pytest.mark.parametrize("i", range(7))
 def test_gemm_llama1b_m2048_sampled(i):
     name, n, k = WL.LLAMA_1B[i]
     rows = np.random.default_rng(i).choice(2048, size=96, replace=False)
@@ -529,6 +529,172 @@ def test_fused_qkv_gemm(gran):
         y_ref = O.gemm(xv, O.dequant(O.ternary(w), a_ref, gran, 128))
         check_close(y, y_ref, O.tolerance_bound(xv, O.alpha_per_weight(a_ref, n, k, gran, 128), y_ref),
                     f"fused gemm {name}")
+
+
+@pytest.mark.parametrize("gran", ["per_group", "per_channel"])
+@pytest.mark.parametrize("members,m", [("qkv", 512), ("qkv", 2048), ("gateup", 512), ("gateup", 2048)])
+def test_fused_gemm_llama1b_bench_sizes(members, m, gran):
+    """The fused-weight prefill GEMM at the sizes the benchmark times: q/k/v
+    (3072 x 2048) and gate/up (16384 x 2048) of the 1B layer as one weight
+    each, at M = 512 (every output of q/k/v; 128 sampled rows of gate/up) and
+    M = 2048 (128 sampled rows); each member's slice against the oracle."""
+    idx = (0, 1, 2) if members == "qkv" else (4, 5)
+    mem = [WL.LLAMA_1B[i] for i in idx]
+    ws = [WL.latent_weight(n, k, WL.layer_1b_weight_seed(i)) for i, (_, n, k) in zip(idx, mem)]
+    fw = S.quantize_pack_fused([dev_f32(w) for w in ws], gran, 128)
+    k = mem[0][2]
+    xb, xv = WL.activations_bf16(m, k, 300 + m)
+    print(f"[gemm] fused {members} 1b {gran} M={m}", flush=True)
+    ys = [O.bf16_bits_to_f32(to_np(y.contiguous())) for y in S.gemm_fused(fw, dev_bf16(xb))]
+    rows = None
+    if m > 512 or members == "gateup":
+        rows = np.random.default_rng(m + len(idx)).choice(m, size=128, replace=False)
+    for w, (name, n, _), y in zip(ws, mem, ys):
+        a_ref = O.alpha(w, gran, 128)
+        a_ref = a_ref.reshape(k // 128, n) if gran == "per_group" else a_ref.reshape(1, n)
+        xr, yr = (xv, y) if rows is None else (xv[rows], y[rows])
+        y_ref = O.gemm(xr, O.dequant(O.ternary(w), a_ref, gran, 128))
+        check_close(yr, y_ref, O.tolerance_bound(xr, O.alpha_per_weight(a_ref, n, k, gran, 128), y_ref),
+                    f"fused gemm {members}/{name} M={m}")
+
+
+# ------------------------------------------------------------------ binding safety
+def test_binding_rejects_mismatched_operands():
+    """Wrong K, wrong output dtype or size, a non-contiguous output and
+    host-side activations are refused with ValueError before any launch."""
+    w = WL.latent_weight(128, 256, 11)
+    pw = S.quantize_pack(dev_f32(w))
+    x_bad_k = torch.zeros((2, 384), dtype=torch.bfloat16, device=DEV)
+    x = torch.zeros((2, 256), dtype=torch.bfloat16, device=DEV)
+    for call in (lambda: S.gemv(pw, x_bad_k), lambda: S.gemm(pw, x_bad_k),
+                 lambda: S.gemv(pw, x.float()), lambda: S.gemv(pw, x.cpu()),
+                 lambda: S.gemv(pw, x, "float32", out=torch.empty((2, 128), dtype=torch.bfloat16, device=DEV)),
+                 lambda: S.gemv(pw, x, "float32", out=torch.empty((2, 100), dtype=torch.float32, device=DEV)),
+                 lambda: S.gemm(pw, x, out=torch.empty((128, 2), dtype=torch.bfloat16, device=DEV).t()),
+                 lambda: S.gemm(pw, x, out=torch.empty((2, 128), dtype=torch.float32, device=DEV)),
+                 lambda: S.arenas_gemm(pw, dev_f32(w), 0.5, x_bad_k),
+                 lambda: S.gemv_batched(pw.packed, pw.alpha, 128, 256, x, 2, pw.packed.numel(), 256),
+                 lambda: S.gemv_batched(pw.packed, pw.alpha, 128, 512, x, 1, 0, 0),
+                 lambda: S.unpack(S.PackedWeight(pw.packed[:100], pw.alpha, 128, 256))):
+        with pytest.raises(ValueError):
+            call()
+    torch.cuda.synchronize()
+
+
+def test_split_k_on_a_side_stream():
+    """Split-K GEMV and GEMM launched on a non-default stream: the binding
+    allocates their workspaces on that stream, so the caching allocator
+    cannot hand the memory to other work while the kernels run.  Other work
+    queued on the default stream meanwhile must not disturb the results."""
+    n, k = 512, 2048
+    w = WL.latent_weight(n, k, 1500)
+    pw = S.quantize_pack(dev_f32(w))
+    a = O.alpha(w, "per_group", 128)
+    wq = O.dequant(O.ternary(w), a, "per_group", 128)
+    for m, kind in ((1, "gemv"), (4, "gemv"), (128, "gemm")):
+        assert S.workspace_bytes(2 if kind == "gemv" else 3, n, k, "per_group", 128, m, 1) > 0
+        xb, xv = WL.activations_bf16(m, k, 1501 + m)
+        x = dev_bf16(xb)
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        outs = []
+        for rep in range(3):
+            with torch.cuda.stream(side):
+                y = S.gemv(pw, x, "float32", stream=side) if kind == "gemv" else S.gemm(pw, x, stream=side)
+            outs.append(y)
+            junk = torch.full((1 << 22,), float(rep), device=DEV)   # default-stream traffic
+            junk.mul_(3.0)
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        y_ref = O.gemv(xv, wq)
+        bound = O.tolerance_bound(xv, O.alpha_per_weight(a, n, k, "per_group", 128),
+                                  y_ref if kind == "gemm" else None)
+        for y in outs:
+            yv = to_np(y)
+            if kind == "gemm":
+                yv = O.bf16_bits_to_f32(yv)
+            check_close(yv, y_ref, bound, f"{kind} on a side stream, M={m}")
+
+
+# ------------------------------------------------------------------ GEMV splits at scale
+@pytest.mark.parametrize("gran", ["per_channel", "per_tensor", "per_group"])
+def test_gemv_3b_gate_batch16_all_granularities(gran):
+    """8192 x 3072 at batch 16 (131072 outputs, K split over workgroups):
+    every output of every granularity against the oracle."""
+    n, k = 8192, 3072
+    xb, xv = WL.activations_bf16(16, k, 2016)
+    print(f"[gemv] 8192x3072 B=16 {gran}", flush=True)
+    gemv_case(n, k, WL.layer_3b_weight_seed(0, 4), xb, xv, gran, 128, y_dtype="bfloat16")
+
+
+@pytest.mark.parametrize("batch,n", [(16, 1024), (3, 2731)])
+@pytest.mark.parametrize("gran", ["per_group", "per_channel"])
+def test_gemv_batched_many_copies_split(batch, n, gran):
+    """count = 8 matrices in one launch with K split and batch * N * count
+    above 2^16 outputs; (3, 2731) makes batch * N odd.  Every copy against
+    the oracle."""
+    k, count = 3072, 8
+    nbytes, nsc = S.packed_bytes(n, k), S.num_scales(n, k, gran, 128)
+    ps, as_, ys = (nbytes + 255) // 256 * 256, (nsc + 63) // 64 * 64, (batch * n + 7) // 8 * 8 + 8
+    packed_all = torch.zeros(count * ps, dtype=torch.uint8, device=DEV)
+    alpha_all = torch.zeros(count * as_, dtype=torch.float32, device=DEV)
+    wl, refs = [], []
+    for c in range(count):
+        w = WL.latent_weight(n, k, 1700 + c)
+        pw = S.quantize_pack(dev_f32(w), gran)
+        packed_all[c * ps:c * ps + nbytes] = pw.packed
+        alpha_all[c * as_:c * as_ + nsc] = pw.alpha
+        wl.append(w)
+        refs.append(O.alpha(w, gran, 128))
+    xb, xv = WL.activations_bf16(batch, k, 1710 + batch)
+    print(f"[gemv] batched count={count} {n}x{k} B={batch} {gran}", flush=True)
+    y = torch.full((count, ys), -3.0, dtype=torch.float32, device=DEV)
+    S.gemv_batched(packed_all, alpha_all, n, k, dev_bf16(xb), count, ps, as_, gran, 128, y_dtype="float32",
+                   y=y, y_stride=ys)
+    yv = to_np(y)
+    for c in range(count):
+        wq = O.dequant(O.ternary(wl[c]), refs[c], gran, 128)
+        bound = O.tolerance_bound(xv, O.alpha_per_weight(refs[c], n, k, gran, 128))
+        check_close(yv[c, :batch * n].reshape(batch, n), O.gemv(xv, wq), bound, f"copy {c}")
+        assert np.all(yv[c, batch * n:] == -3.0)
+
+
+def test_gemv_3b_stack_bench_inputs():
+    """The 3B-stack weights exactly as the benchmark draws them (torch's
+    seeded Philox generator on the GPU) and the launch it times (one batched
+    GEMV over the 28 layers' copies, bench.Replicated), for the q and down
+    shapes at batch 1 and 4: layers 0 and 27 are copied back, quantized by
+    the oracle, and their products checked against the oracle's."""
+    import bench
+    for i in (0, 6):
+        name, n, k = WL.LLAMA_3B[i]
+        wl, rep = {}, None
+        for layer in range(WL.LLAMA_3B_LAYERS):
+            wd = WL.latent_weight_device(n, k, WL.layer_3b_weight_seed(layer, i), DEV)
+            pw = S.quantize_pack(wd, "per_group", 128)
+            if rep is None:
+                rep = bench.Replicated(pw, WL.LLAMA_3B_LAYERS, batch=4)
+            else:
+                rep.packed_all[layer, :rep.nbytes] = pw.packed
+                rep.alpha_all[layer, :rep.nsc] = pw.alpha
+            if layer in (0, WL.LLAMA_3B_LAYERS - 1):
+                wl[layer] = wd.cpu().numpy()
+            del wd, pw
+        for batch in (1, 4):
+            rep.batch = batch
+            wsb = S.workspace_bytes(2, n, k, "per_group", 128, batch, WL.LLAMA_3B_LAYERS)
+            rep.ws = torch.empty(wsb, dtype=torch.uint8, device=DEV) if wsb else None
+            xb, xv = WL.activations_bf16(batch, k, 2000 + batch)
+            print(f"[gemv] 3B bench launch {name} x {WL.LLAMA_3B_LAYERS} layers B={batch}", flush=True)
+            y = to_np(rep.gemv(dev_bf16(xb)))
+            for layer, w in wl.items():
+                a = O.alpha(w, "per_group", 128)
+                y_ref = O.gemv(xv, O.dequant(O.ternary(w), a, "per_group", 128))
+                got = O.bf16_bits_to_f32(y[layer, :batch * n]).reshape(batch, n)
+                check_close(got, y_ref, O.tolerance_bound(xv, O.alpha_per_weight(a, n, k, "per_group", 128), y_ref),
+                            f"3B {name} layer {layer} B={batch}")
+        del rep
+        torch.cuda.empty_cache()
 
 
 # ------------------------------------------------------------------ Arenas

@@ -134,3 +134,69 @@ def test_arenas_forward_one_hot_and_zero_lambda():
         assert np.array_equal(y[0], wq[:, c] + lam * w[:, c].astype(np.float64))
     x = rng.standard_normal((3, k))
     assert np.array_equal(O.arenas_forward(x, wq, w, 0.0), O.gemm(x, wq))
+
+
+# ---------------------------------------------------------------- tolerance pin
+def _tolerance_fixture():
+    import os
+    from conftest import GOLDEN
+    w, x, alpha, bound, y, bound_bf16 = [], [], {}, {}, {}, {}
+    for line in open(os.path.join(GOLDEN, "tolerance_hand.txt")):
+        line = line.split("#")[0].split()
+        if not line:
+            continue
+        tag, rest = line[0], line[1:]
+        if tag == "W":
+            w.append([float(v) for v in rest])
+        elif tag == "X":
+            x.append([float(v) for v in rest])
+        else:
+            key = (rest[0], int(rest[1]))
+            vals = [float(v) for v in rest[2:]]
+            {"ALPHA": alpha, "BOUND": bound, "Y": y, "BOUND_BF16": bound_bf16}[tag][key] = vals
+    return (np.array(w, dtype=np.float32), np.array(x, dtype=np.float32), alpha, bound, y, bound_bf16)
+
+
+@pytest.mark.parametrize("gran,g", [("per_group", 4), ("per_channel", 8), ("per_tensor", 8)])
+def test_tolerance_bound_hand_worked(gran, g):
+    """The bound 1e-3 * sum_k |x_k| alpha(n, k) on a hand-worked 2 x 8 case
+    (tests/golden/tolerance_hand.txt): the scales of all three granularities
+    exactly (two distinct per_channel scales, four per_group scales in their
+    group-major layout), then the bound of every (row of x, output) pair.  The
+    values change if the factor, either absolute value, the granule broadcast
+    or the range of the sum (all k, pruned positions included) changes."""
+    w, x, alpha, bound, _, _ = _tolerance_fixture()
+    a = O.alpha(w, gran, g)
+    assert np.array_equal(a.reshape(-1), np.array(alpha[(gran, g)], dtype=np.float32))
+    got = O.tolerance_bound(x, O.alpha_per_weight(a, 2, 8, gran, g))
+    want = np.array(bound[(gran, g)]).reshape(2, 2)
+    assert got.shape == (2, 2)
+    assert np.allclose(got, want, rtol=1e-12, atol=0)
+
+
+def test_tolerance_bound_bf16_term_hand_worked():
+    """With the fp64 result passed in, half a bf16 ulp of it is added: the
+    hand-worked per_group output y[0, 0] = 5.75 and its bound 0.0255."""
+    w, x, _, _, y, bound_bf16 = _tolerance_fixture()
+    a = O.alpha(w, "per_group", 4)
+    t = O.ternary(w)
+    y_ref = O.gemv(x, O.dequant(t, a, "per_group", 4))
+    b, n, yv = y[("per_group", 4)]
+    assert y_ref[int(b), int(n)] == yv
+    got = O.tolerance_bound(x, O.alpha_per_weight(a, 2, 8, "per_group", 4), y_ref)
+    b2, n2, bv = bound_bf16[("per_group", 4)]
+    assert abs(got[int(b2), int(n2)] - bv) <= 1e-15
+
+
+def test_alpha_per_weight_per_channel_two_rows():
+    """per_channel broadcast: every weight of row n gets that row's scale
+    (0.75 and 1.125 in the hand-worked case), and the dequantized weight is
+    T times it, exactly."""
+    w, _, alpha, _, _, _ = _tolerance_fixture()
+    a = O.alpha(w, "per_channel", 8)
+    aw = O.alpha_per_weight(a, 2, 8, "per_channel")
+    assert np.array_equal(aw[0], np.full(8, 0.75, dtype=np.float32))
+    assert np.array_equal(aw[1], np.full(8, 1.125, dtype=np.float32))
+    wq = O.dequant(O.ternary(w), a, "per_channel")
+    assert np.array_equal(wq[0], np.array([1, -1, 1, 0, -1, 0, 1, -1]) * 0.75)
+    assert np.array_equal(wq[1], np.array([1, -1, 0, 1, 1, -1, 0, 1]) * 1.125)

@@ -17,8 +17,9 @@
  *    K = in_features).  Blocks and groups run along K.
  *  - Pointers are DEVICE pointers (hipMalloc'd or torch CUDA tensors) unless
  *    stated otherwise; the caller owns all memory.  The library never
- *    allocates, frees or synchronizes.  It keeps no state between calls and is
- *    thread-safe.
+ *    allocates, frees or synchronizes, and is thread-safe.  Its only state is
+ *    the static device workspace of sherry_quantize_pack_noalloc (one per
+ *    device, with its address cached on first use).
  *  - `stream` is a hipStream_t passed as void* (NULL = the null stream).  All
  *    work is enqueued asynchronously on it.
  *  - Argument checks run on the host before any launch.  A bad argument
@@ -140,6 +141,32 @@ size_t sherry_workspace_bytes(int32_t op, int64_t n, int64_t k, int32_t granular
 int32_t sherry_quantize_pack(int64_t n, int64_t k, int32_t granularity, int32_t group_size,
                              const void* w, int32_t w_dtype, void* packed, float* alpha,
                              void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * sherry_quantize_pack_noalloc -- for callers that cannot allocate memory:
+ * code under HIP graph capture, tight serving or training loops that
+ * re-quantize every step, harnesses that forbid hipMalloc.  The same
+ * operation, results and argument rules as sherry_quantize_pack, with the
+ * workspace taken from a static device buffer of the library
+ * (SHERRY_QUANTIZE_SCRATCH_BYTES, 8 MiB, on each device the library runs on,
+ * held until the process ends) instead of a caller's buffer.  Nothing is
+ * allocated.
+ *
+ *   Limit: sherry_workspace_bytes(SHERRY_OP_QUANTIZE_PACK, ...) must not
+ *   exceed SHERRY_QUANTIZE_SCRATCH_BYTES (N*K/128 fp32 superblock sums plus
+ *   the per_tensor tree partials: up to about 2^28 weights), else
+ *   SHERRY_ERR_WORKSPACE and nothing is launched.  per_group with G == 128
+ *   needs no workspace and has no limit.
+ *   The buffer belongs to the current device: `stream` must be a stream of
+ *   the current device.  Every call on a device shares that device's buffer
+ *   and leaves its contents behind (every value is written before it is read,
+ *   so nothing needs clearing): calls that overlap on one device (two
+ *   streams, two threads) race and must be serialized by the caller.
+ */
+#define SHERRY_QUANTIZE_SCRATCH_BYTES ((size_t)8 << 20)
+int32_t sherry_quantize_pack_noalloc(int64_t n, int64_t k, int32_t granularity, int32_t group_size,
+                                     const void* w, int32_t w_dtype, void* packed, float* alpha,
+                                     void* stream);
 
 /*
  * sherry_unpack -- decode packed planes back to the ternary matrix or the

@@ -22,7 +22,7 @@ __all__ = [
     "PackedWeight", "quantize_pack", "unpack", "gemv", "gemm", "packed_bytes", "num_scales",
     "workspace_bytes", "SherryError", "load", "fake_quant", "fake_quant_ste", "gemv_batched",
     "FusedWeight", "quantize_pack_fused", "gemv_fused", "arenas_lambda", "arenas_gemm",
-    "compare_repack", "compare_gemv", "gemm_fused",
+    "compare_repack", "compare_gemv", "gemm_fused", "quantize_pack_noalloc",
 ]
 
 
@@ -162,6 +162,35 @@ def quantize_pack(w, granularity: str = "per_group", group_size: int = 128, stre
         ws = _workspace(ws_bytes if ws_bytes != (1 << 64) - 1 else 0, w.device)
         check(lib.sherry_quantize_pack(n, k, gran, group_size, _ptr(w), dtype, _ptr(packed), _ptr(alpha),
                                        _ptr(ws), 0 if ws is None else ws.numel(), _stream(stream)))
+    return PackedWeight(packed[:nbytes], alpha[:nsc], n, k, granularity, group_size)
+
+
+def quantize_pack_noalloc(w, packed, alpha, granularity: str = "per_group", group_size: int = 128,
+                          stream=None) -> PackedWeight:
+    """quantize_pack into caller-provided ``packed`` (uint8, packed_bytes)
+    and ``alpha`` (float32, num_scales) through the library's allocation-free
+    entry point: no memory is allocated (the workspace is the library's static
+    device buffer), so the call can run under HIP graph capture.  ``w`` must
+    be contiguous.  Calls that overlap on one device race on that buffer."""
+    torch = _torch()
+    if w.dim() != 2:
+        raise ValueError("Sherry quantization expects a 2-D weight")
+    _need_gpu(w, "w")
+    if not w.is_contiguous():
+        raise ValueError("w must be contiguous (no copy is made)")
+    n, k = w.shape
+    gran = _gran(granularity)
+    dtype = {torch.float32: _lib.F32, torch.bfloat16: _lib.BF16}.get(w.dtype)
+    if dtype is None:
+        raise ValueError("w must be float32 or bfloat16")
+    lib = load()
+    nbytes = int(lib.sherry_packed_bytes(n, k))
+    nsc = int(lib.sherry_num_scales(n, k, gran, group_size))
+    _need_out(packed, "packed", torch.uint8, nbytes, w.device)
+    _need_out(alpha, "alpha", torch.float32, nsc, w.device)
+    with torch.cuda.device(w.device):
+        check(lib.sherry_quantize_pack_noalloc(n, k, gran, group_size, _ptr(w), dtype, _ptr(packed), _ptr(alpha),
+                                               _stream(stream)))
     return PackedWeight(packed[:nbytes], alpha[:nsc], n, k, granularity, group_size)
 
 

@@ -23,13 +23,14 @@ GRANULARITY = {"per_tensor": PER_TENSOR, "per_channel": PER_CHANNEL, "per_group"
 CMP_2BIT, CMP_TL2 = 0, 1
 F32, BF16, I8 = 0, 1, 2
 OP_QUANTIZE_PACK, OP_UNPACK, OP_GEMV, OP_GEMM, OP_FAKE_QUANT, OP_ARENAS_GEMM = 0, 1, 2, 3, 4, 5
+QUANTIZE_SCRATCH_BYTES = 8 << 20   # SHERRY_QUANTIZE_SCRATCH_BYTES
 
 # every symbol include/sherry.h declares
 SYMBOLS = (
     "sherry_abi_version", "sherry_status_string", "sherry_packed_bytes", "sherry_num_scales",
     "sherry_workspace_bytes", "sherry_quantize_pack", "sherry_unpack", "sherry_gemv", "sherry_gemm",
     "sherry_fake_quant", "sherry_arenas_gemm", "sherry_compare_bytes", "sherry_compare_repack",
-    "sherry_compare_gemv", "sherry_arenas_lambda",
+    "sherry_compare_gemv", "sherry_arenas_lambda", "sherry_quantize_pack_noalloc",
 )
 
 _i32, _i64, _sz, _vp = ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t, ctypes.c_void_p
@@ -41,6 +42,7 @@ _SIGNATURES = {
     "sherry_num_scales": ([_i64, _i64, _i32, _i32], _i64),
     "sherry_workspace_bytes": ([_i32, _i64, _i64, _i32, _i32, _i64, _i32], _sz),
     "sherry_quantize_pack": ([_i64, _i64, _i32, _i32, _vp, _i32, _vp, _vp, _vp, _sz, _vp], _i32),
+    "sherry_quantize_pack_noalloc": ([_i64, _i64, _i32, _i32, _vp, _i32, _vp, _vp, _vp], _i32),
     "sherry_unpack": ([_i64, _i64, _i32, _i32, _vp, _vp, _vp, _i32, _vp], _i32),
     "sherry_gemv": ([_i64, _i64, _i32, _i32, _vp, _vp, _vp, _i32, _vp, _i32, _i32, _i64, _i64, _i64,
                      _vp, _sz, _vp], _i32),

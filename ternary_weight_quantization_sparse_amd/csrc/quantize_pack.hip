@@ -12,10 +12,22 @@
 // the per-superblock reductions (kept-|w| sum, sign dword, nibble dwords) are
 // cross-lane DPP moves inside rows of 16 lanes that reproduce the pairwise
 // tree's additions exactly.
+#include <mutex>
+
 #include "sherry_internal.h"
 
 namespace sherry {
 namespace {
+
+// Static workspace of the allocation-free quantize entry point: superblock
+// sums and tree partials live here instead of in a caller-provided buffer.
+// Host code never names this array (in host code the name is a stand-in, not
+// a device address); quantize_scratch() looks up its address on each device.
+static __device__ __align__(256) float scratch[kQuantizeScratchBytes / sizeof(float)];
+
+constexpr int kMaxScratchDevices = 64;
+std::mutex g_scratch_mu;
+float* g_scratch_ptr[kMaxScratchDevices] = {};
 
 #ifndef SHERRY_Q_BPL
 #define SHERRY_Q_BPL 2  // blocks per lane
@@ -587,6 +599,24 @@ hipError_t launch_fake_quant(const FakeQuantPlan& p, int64_t n, int64_t k, int g
                                       reinterpret_cast<float*>(ws + p.quant_ws_offset), s);
   if (e != hipSuccess) return e;
   return launch_unpack(n, k, gran, group_size, packed, alpha, out, out_dtype, s);
+}
+
+// Device address of `scratch` on the current device, looked up once per
+// device (each device holds its own copy of the array) and cached.
+hipError_t quantize_scratch(float** ptr) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxScratchDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    g_scratch_ptr[dev] = static_cast<float*>(p);
+  }
+  *ptr = g_scratch_ptr[dev];
+  return hipSuccess;
 }
 
 }  // namespace sherry

@@ -121,6 +121,23 @@ int32_t sherry_quantize_pack(int64_t n, int64_t k, int32_t granularity, int32_t 
                                          static_cast<hipStream_t>(stream)));
 }
 
+int32_t sherry_quantize_pack_noalloc(int64_t n, int64_t k, int32_t granularity, int32_t group_size,
+                                     const void* w, int32_t w_dtype, void* packed, float* alpha,
+                                     void* stream) {
+  int st = check_shape(n, k, granularity, group_size);
+  if (st != SHERRY_OK) return st;
+  if (w_dtype != SHERRY_F32 && w_dtype != SHERRY_BF16) return SHERRY_ERR_DTYPE;
+  if (!w || !packed || !alpha) return SHERRY_ERR_NULL;
+  if (!aligned16(w) || !aligned16(packed) || !aligned16(alpha)) return SHERRY_ERR_ALIGN;
+  const QuantizePlan plan = plan_quantize(n, k, granularity, group_size);
+  if (plan.workspace_bytes > kQuantizeScratchBytes) return SHERRY_ERR_WORKSPACE;
+  float* ws = nullptr;
+  if (plan.workspace_bytes > 0 && quantize_scratch(&ws) != hipSuccess) return SHERRY_ERR_HIP;
+  return hip_status(launch_quantize_pack(plan, n, k, granularity, group_size, w, w_dtype == SHERRY_BF16,
+                                         static_cast<uint8_t*>(packed), alpha, ws,
+                                         static_cast<hipStream_t>(stream)));
+}
+
 int32_t sherry_unpack(int64_t n, int64_t k, int32_t granularity, int32_t group_size,
                       const void* packed, const float* alpha, void* out, int32_t out_dtype,
                       void* stream) {

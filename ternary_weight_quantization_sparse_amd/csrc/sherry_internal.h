@@ -29,6 +29,10 @@ QuantizePlan plan_quantize(int64_t n, int64_t k, int gran, int group_size);
 hipError_t launch_quantize_pack(const QuantizePlan& p, int64_t n, int64_t k, int gran,
                                 int group_size, const void* w, bool w_bf16, uint8_t* packed,
                                 float* alpha, float* ws, hipStream_t s);
+// Static quantize workspace on the current device (the allocation-free entry
+// point's): its device address, looked up on the first call per device.
+constexpr size_t kQuantizeScratchBytes = SHERRY_QUANTIZE_SCRATCH_BYTES;
+hipError_t quantize_scratch(float** ptr);
 
 // ---------------------------------------------------------------- fake quant
 struct FakeQuantPlan {

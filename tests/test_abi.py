@@ -35,7 +35,7 @@ def _declared_symbols():
 
 def test_exports_every_declared_symbol(lib):
     declared = _declared_symbols()
-    assert len(declared) == 15
+    assert len(declared) == 16
     assert set(declared) == set(L.SYMBOLS)
     for name in declared:
         assert hasattr(lib, name), name
@@ -275,3 +275,19 @@ def test_binding_rejects_host_tensors():
                  lambda: S.compare_gemv(0, pw.packed, pw.alpha, 64, 256, x)):
         with pytest.raises(ValueError):
             call()
+
+
+def test_quantize_noalloc_rejects_before_any_launch(lib):
+    """The allocation-free quantize checks its arguments like
+    sherry_quantize_pack, and refuses a weight whose workspace exceeds the
+    static buffer (8 MiB) before touching the device."""
+    f = lib.sherry_quantize_pack_noalloc
+    assert f(64, 514, L.PER_GROUP, 128, FAKE, L.F32, FAKE2, FAKE, None) == L.ERR_SHAPE
+    assert f(64, 512, L.PER_GROUP, 128, FAKE, L.I8, FAKE2, FAKE, None) == L.ERR_DTYPE
+    assert f(64, 512, L.PER_GROUP, 128, None, L.F32, FAKE2, FAKE, None) == L.ERR_NULL
+    assert f(64, 512, L.PER_GROUP, 128, MIS, L.F32, FAKE2, FAKE, None) == L.ERR_ALIGN
+    # 8192 x 65536 per_tensor: 4 Mi superblock sums = 16 MiB of workspace
+    need = lib.sherry_workspace_bytes(L.OP_QUANTIZE_PACK, 8192, 65536, L.PER_TENSOR, 128, 1, 1)
+    assert need > L.QUANTIZE_SCRATCH_BYTES
+    assert f(8192, 65536, L.PER_TENSOR, 128, FAKE, L.BF16, FAKE2, FAKE, None) == L.ERR_WORKSPACE
+    assert f(8192, 65536, L.PER_CHANNEL, 128, FAKE, L.BF16, FAKE2, FAKE, None) == L.ERR_WORKSPACE

@@ -36,7 +36,7 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kLutThreads = 256;
 #ifndef SHERRY_GEMV_SPLIT_TARGET
-#define SHERRY_GEMV_SPLIT_TARGET 2048      // batch 1: split K until a launch has ~this many workgroups
+#define SHERRY_GEMV_SPLIT_TARGET 2048      // batch 1: split K until a launch has ~this many 256-row workgroups
 #endif
 #ifndef SHERRY_GEMV_MFMA_SPLIT_TARGET
 #define SHERRY_GEMV_MFMA_SPLIT_TARGET 768  // batch 2..16: the same, for the MFMA kernel
@@ -67,8 +67,7 @@ __device__ inline uint32_t quad_offsets(uint32_t nib_dword, uint32_t sign_word, 
 // z = 2h, 2h+1 with both sign bits.  Entry index = s<<4 | z<<2 | p1<<1 | p0;
 // value = (x_k0 +- x_k1) +- x_k2 over the kept positions k0 < k1 < k2 (all
 // but z), negated when s = 1.  Writes entries [8h, 8h+8) and [16+8h, 24+8h).
-__device__ inline void build_block_half(float* blk_tbl, const uint16_t* __restrict__ xblk, int h) {
-  const uint2 xv = *reinterpret_cast<const uint2*>(xblk);
+__device__ inline void build_block_half_x(float* blk_tbl, const uint2 xv, int h) {
   const float xs[4] = {__uint_as_float(xv.x << 16), __uint_as_float(xv.x & 0xFFFF0000u),
                        __uint_as_float(xv.y << 16), __uint_as_float(xv.y & 0xFFFF0000u)};
   float e[8];
@@ -90,6 +89,10 @@ __device__ inline void build_block_half(float* blk_tbl, const uint16_t* __restri
   pos[1] = make_float4(e[4], e[5], e[6], e[7]);
   neg[0] = make_float4(-e[0], -e[1], -e[2], -e[3]);
   neg[1] = make_float4(-e[4], -e[5], -e[6], -e[7]);
+}
+
+__device__ inline void build_block_half(float* blk_tbl, const uint16_t* __restrict__ xblk, int h) {
+  build_block_half_x(blk_tbl, *reinterpret_cast<const uint2*>(xblk), h);
 }
 
 template <bool BF16>
@@ -183,37 +186,47 @@ __device__ inline void window_accumulate(const float* tbl, const RowWindow<MODE,
   }
 }
 
-// Batch-1 GEMV.  Workgroup = 256 threads = 256 rows x M row slots; K range =
-// one split; LDS holds the tables of WIN superblocks at a time (WIN*4 KB).
-// For each window: build the tables, then per row slot issue the whole
-// row-window of loads (WIN x 24 bytes per lane, non-temporal: read once) and
-// consume it.  Latency is hidden by occupancy: at ~55 VGPRs and 16 KB of LDS
-// per workgroup, 8 waves share each SIMD.
-template <int MODE, int WIN, int M, bool YBF16>
-__global__ __launch_bounds__(kLutThreads) void gemv_b1_lut_kernel(
+// Batch-1 GEMV.  Workgroup = RW x KW waves: RW row waves (64 rows each, M
+// row slots per lane) times KW K-slices.  Slice s owns superblocks
+// [s S, (s + 1) S) of the row range (S = K / 128 / KW, whole groups), and its
+// RW waves share that slice's tables.  For each window of WIN superblocks:
+// the workgroup builds every slice's tables (one 32-entry table per block of
+// 4 activations, 4 KB per superblock), then each lane issues its row-window
+// of loads (WIN x 24 bytes, non-temporal: read once) and consumes it.  With
+// KW > 1 the slices' partial sums of a row are added in slice order through
+// LDS at the end (deterministic): launches with few rows split K inside the
+// workgroup instead of across workgroups, so a call is one kernel with no
+// workspace.  Latency is hidden by occupancy: ~55 VGPRs and 16-64 KB of LDS
+// per workgroup, 8 waves per SIMD.
+template <int MODE, int WIN, int M, bool YBF16, int RW, int KW>
+__global__ __launch_bounds__(64 * RW * KW) void gemv_b1_lut_kernel(
     const uint8_t* __restrict__ packed, const float* __restrict__ alpha,
-    const uint16_t* __restrict__ x, void* __restrict__ y, float* __restrict__ partial, int64_t n,
-    int64_t k, int group_sbs, int ksplit, int64_t packed_stride, int64_t alpha_stride,
-    int64_t y_stride) {
-  __shared__ __attribute__((aligned(16))) float tbl[WIN * kTableFloatsPerSb];
+    const uint16_t* __restrict__ x, void* __restrict__ y, float* __restrict__ partial, int64_t n, int64_t k,
+    int group_sbs, int ksplit, int64_t packed_stride, int64_t alpha_stride, int64_t y_stride) {
+  constexpr int kRows = 64 * RW;  // rows per row slot
+  constexpr int kThreadsWg = 64 * RW * KW;
+  __shared__ __attribute__((aligned(16))) float tbl[KW][WIN * kTableFloatsPerSb];
+  __shared__ float red[KW > 1 ? KW : 1][KW > 1 ? kRows * M : 1];
   const int tid = threadIdx.x;
+  const int slice = tid / kRows;      // K-slice of this thread
+  const int rtid = tid % kRows;       // row inside a row slot
   const int64_t c = blockIdx.y;
-  const int kz = blockIdx.z;
-  const int64_t nsb = k / kSuperblock;
-  const int64_t sb_per_split = nsb / ksplit;
-  const int64_t sb_begin = kz * sb_per_split;
-  const int nwin = (int)(sb_per_split / WIN);
+  const int kz = blockIdx.z;  // split across workgroups (KW == 1 only)
+  const int64_t nsb = k / kSuperblock / ksplit;
+  const int64_t per_slice = nsb / KW;
+  const int64_t sb_begin = kz * nsb + slice * per_slice;
+  const int nwin = (int)(per_slice / WIN);
 
   const uint8_t* pk = packed + c * packed_stride;
   const uint8_t* __restrict__ sgn_base = pk + nibble_plane_bytes(n, k);
   const float* __restrict__ al = alpha + c * alpha_stride;
-  const int64_t row_base = (int64_t)blockIdx.x * (kLutThreads * M) + tid;
+  const int64_t row_base = (int64_t)blockIdx.x * (kRows * M) + rtid;
 
   // rows past the end are clamped for loads (their results are not stored)
   uint32_t rows[M];
 #pragma unroll
   for (int i = 0; i < M; ++i) {
-    const int64_t r = row_base + (int64_t)i * kLutThreads;
+    const int64_t r = row_base + (int64_t)i * kRows;
     rows[i] = (uint32_t)(r < n ? r : n - 1);
   }
 
@@ -225,25 +238,78 @@ __global__ __launch_bounds__(kLutThreads) void gemv_b1_lut_kernel(
     gpos[i] = 0;
   }
 
-  for (int w = 0; w < nwin; ++w) {
-    const int64_t g0 = sb_begin + (int64_t)w * WIN;
-    __syncthreads();  // previous window's lookups are done
-    for (int task = tid; task < WIN * kBlocksPerSb * 2; task += kLutThreads) {
-      const int blk = task >> 1;
-      build_block_half(tbl + blk * 32, x + g0 * kSuperblock + blk * 4, task & 1);
-    }
-    __syncthreads();
+  // Split launches (few workgroups, several windows per slice) issue window
+  // w + 1's loads (packed data and the activations of the next tables)
+  // before consuming window w, so their latency runs under the lookups and
+  // the next table build.  Full launches keep one window of registers: their
+  // occupancy (8 waves per SIMD) hides the latency.
+  constexpr bool kAhead = KW > 1;
+  if constexpr (kAhead) {
+    // the plan gives every thread at most one table task per window
+    // (KW * WIN * 64 <= threads), so each thread also prefetches the 8 bytes
+    // of activations its next task needs
+    constexpr int kTasks = KW * WIN * kBlocksPerSb * 2;
+    static_assert(kTasks <= kThreadsWg, "one table task per thread and window");
+    const bool has_task = tid < kTasks;
+    const int ts = tid / (WIN * kBlocksPerSb * 2);
+    const int blk = (tid >> 1) % (WIN * kBlocksPerSb);
+    const uint16_t* xsrc = x + (has_task ? (kz * nsb + ts * per_slice) * kSuperblock + blk * 4 : 0);
+    float* tdst = tbl[has_task ? ts : 0] + blk * 32;
+    RowWindow<MODE, WIN> cur[M], nxt[M];
+    uint2 xcur = has_task ? *reinterpret_cast<const uint2*>(xsrc) : make_uint2(0u, 0u), xnxt = xcur;
 #pragma unroll
-    for (int i = 0; i < M; ++i) {
-      RowWindow<MODE, WIN> rw;
-      load_row_window<MODE, WIN>(rw, pk, sgn_base, al, n, rows[i], g0, group_sbs);
-      window_accumulate<MODE, WIN>(tbl, rw, acc[i], accg[i], gpos[i], group_sbs);
+    for (int i = 0; i < M; ++i) load_row_window<MODE, WIN>(cur[i], pk, sgn_base, al, n, rows[i], sb_begin, group_sbs);
+    for (int w = 0; w < nwin; ++w) {
+      __syncthreads();  // previous window's lookups are done
+      if (has_task) build_block_half_x(tdst, xcur, tid & 1);
+      __syncthreads();
+      if (w + 1 < nwin) {
+        const int64_t g1 = sb_begin + (int64_t)(w + 1) * WIN;
+#pragma unroll
+        for (int i = 0; i < M; ++i) load_row_window<MODE, WIN>(nxt[i], pk, sgn_base, al, n, rows[i], g1, group_sbs);
+        if (has_task) xnxt = *reinterpret_cast<const uint2*>(xsrc + (int64_t)(w + 1) * WIN * kSuperblock);
+      }
+#pragma unroll
+      for (int i = 0; i < M; ++i) {
+        window_accumulate<MODE, WIN>(tbl[slice], cur[i], acc[i], accg[i], gpos[i], group_sbs);
+        cur[i] = nxt[i];
+      }
+      xcur = xnxt;
+    }
+  } else {
+    for (int w = 0; w < nwin; ++w) {
+      const int64_t g0 = sb_begin + (int64_t)w * WIN;
+      __syncthreads();  // previous window's lookups are done
+      for (int task = tid; task < WIN * kBlocksPerSb * 2; task += kThreadsWg) {
+        const int blk = task >> 1;
+        build_block_half(tbl[0] + blk * 32, x + g0 * kSuperblock + blk * 4, task & 1);
+      }
+      __syncthreads();
+#pragma unroll
+      for (int i = 0; i < M; ++i) {
+        RowWindow<MODE, WIN> rw;
+        load_row_window<MODE, WIN>(rw, pk, sgn_base, al, n, rows[i], g0, group_sbs);
+        window_accumulate<MODE, WIN>(tbl[0], rw, acc[i], accg[i], gpos[i], group_sbs);
+      }
     }
   }
 
+  if constexpr (KW > 1) {
+#pragma unroll
+    for (int i = 0; i < M; ++i) red[slice][i * kRows + rtid] = acc[i];
+    __syncthreads();
+    if (slice != 0) return;
+#pragma unroll
+    for (int i = 0; i < M; ++i) {
+      float v = red[0][i * kRows + rtid];
+#pragma unroll
+      for (int t = 1; t < KW; ++t) v += red[t][i * kRows + rtid];
+      acc[i] = v;
+    }
+  }
 #pragma unroll
   for (int i = 0; i < M; ++i) {
-    const int64_t row = row_base + (int64_t)i * kLutThreads;
+    const int64_t row = row_base + (int64_t)i * kRows;
     if (row >= n) continue;
     float v = acc[i];
     if (ksplit == 1) {
@@ -632,46 +698,40 @@ __global__ __launch_bounds__(256) void gemv_split_reduce4(const float* __restric
   }
 }
 
-template <int MODE, int WIN, int M, bool YBF16>
-void launch_lut_one(dim3 grid, size_t lds, hipStream_t s, const uint8_t* packed, const float* alpha,
-                    const uint16_t* x, void* y, float* ws, int64_t n, int64_t k, int group_sbs, int ksplit,
-                    int64_t ps, int64_t as, int64_t ys) {
-  hipLaunchKernelGGL((gemv_b1_lut_kernel<MODE, WIN, M, YBF16>), grid, dim3(kLutThreads), lds, s, packed,
+template <int MODE, int WIN, int M, bool YBF16, int RW, int KW>
+void launch_lut_one(dim3 grid, hipStream_t s, const uint8_t* packed, const float* alpha, const uint16_t* x,
+                    void* y, float* ws, int64_t n, int64_t k, int group_sbs, int ksplit, int64_t ps, int64_t as,
+                    int64_t ys) {
+  hipLaunchKernelGGL((gemv_b1_lut_kernel<MODE, WIN, M, YBF16, RW, KW>), grid, dim3(64 * RW * KW), 0, s, packed,
                      alpha, x, y, ws, n, k, group_sbs, ksplit, ps, as, ys);
 }
 
-template <int MODE, int WIN, bool YBF16>
-void launch_lut_m(int m, dim3 grid, size_t lds, hipStream_t s, const uint8_t* packed, const float* alpha,
-                  const uint16_t* x, void* y, float* ws, int64_t n, int64_t k, int group_sbs, int ksplit,
-                  int64_t ps, int64_t as, int64_t ys) {
-  if (m >= 4) launch_lut_one<MODE, WIN, 4, YBF16>(grid, lds, s, packed, alpha, x, y, ws, n, k, group_sbs, ksplit, ps, as, ys);
-  else if (m == 2) launch_lut_one<MODE, WIN, 2, YBF16>(grid, lds, s, packed, alpha, x, y, ws, n, k, group_sbs, ksplit, ps, as, ys);
-  else launch_lut_one<MODE, WIN, 1, YBF16>(grid, lds, s, packed, alpha, x, y, ws, n, k, group_sbs, ksplit, ps, as, ys);
-}
-
+// (rw, kw, win, m) -> instantiation; the plan only produces these shapes
 template <int MODE, bool YBF16>
-void launch_lut_w(int win, int m, dim3 grid, size_t lds, hipStream_t s, const uint8_t* packed,
-                  const float* alpha, const uint16_t* x, void* y, float* ws, int64_t n, int64_t k,
-                  int group_sbs, int ksplit, int64_t ps, int64_t as, int64_t ys) {
-  switch (win) {
-    case 16: launch_lut_m<MODE, 16, YBF16>(m, grid, lds, s, packed, alpha, x, y, ws, n, k, group_sbs, ksplit, ps, as, ys); break;
-    case 8: launch_lut_m<MODE, 8, YBF16>(m, grid, lds, s, packed, alpha, x, y, ws, n, k, group_sbs, ksplit, ps, as, ys); break;
-    case 4: launch_lut_m<MODE, 4, YBF16>(m, grid, lds, s, packed, alpha, x, y, ws, n, k, group_sbs, ksplit, ps, as, ys); break;
-    case 2: launch_lut_m<MODE, 2, YBF16>(m, grid, lds, s, packed, alpha, x, y, ws, n, k, group_sbs, ksplit, ps, as, ys); break;
-    default: launch_lut_m<MODE, 1, YBF16>(m, grid, lds, s, packed, alpha, x, y, ws, n, k, group_sbs, ksplit, ps, as, ys); break;
-  }
-}
-
-template <bool YBF16>
-void launch_lut(int mode, int win, int m, dim3 grid, size_t lds, hipStream_t s, const uint8_t* packed,
-                const float* alpha, const uint16_t* x, void* y, float* ws, int64_t n, int64_t k, int group_sbs,
-                int ksplit, int64_t ps, int64_t as, int64_t ys) {
-  switch (mode) {
-    case kGroup1: launch_lut_w<kGroup1, YBF16>(win, m, grid, lds, s, packed, alpha, x, y, ws, n, k, group_sbs, ksplit, ps, as, ys); break;
-    case kGroupN: launch_lut_w<kGroupN, YBF16>(win, m, grid, lds, s, packed, alpha, x, y, ws, n, k, group_sbs, ksplit, ps, as, ys); break;
-    case kChannel: launch_lut_w<kChannel, YBF16>(win, m, grid, lds, s, packed, alpha, x, y, ws, n, k, group_sbs, ksplit, ps, as, ys); break;
-    default: launch_lut_w<kTensor, YBF16>(win, m, grid, lds, s, packed, alpha, x, y, ws, n, k, group_sbs, ksplit, ps, as, ys); break;
-  }
+hipError_t launch_lut(const GemvPlan& p, dim3 grid, hipStream_t s, const uint8_t* packed, const float* alpha,
+                      const uint16_t* x, void* y, float* ws, int64_t n, int64_t k, int group_sbs, int64_t ps,
+                      int64_t as, int64_t ys) {
+#define SHERRY_LUT(W, M_, RW_, KW_) \
+  launch_lut_one<MODE, W, M_, YBF16, RW_, KW_>(grid, s, packed, alpha, x, y, ws, n, k, group_sbs, p.ksplit, ps, as, ys)
+#define SHERRY_LUT_WIN(M_, RW_, KW_)                 \
+  do {                                               \
+    if (p.window_sbs >= 4) SHERRY_LUT(4, M_, RW_, KW_); \
+    else if (p.window_sbs == 2) SHERRY_LUT(2, M_, RW_, KW_); \
+    else SHERRY_LUT(1, M_, RW_, KW_);                \
+  } while (0)
+  const int cfg = p.rw * 100 + p.kw;
+  if (cfg == 401 && p.rows_per_thread == 4) SHERRY_LUT_WIN(4, 4, 1);
+  else if (cfg == 401) SHERRY_LUT_WIN(1, 4, 1);
+  else if (cfg == 402) SHERRY_LUT_WIN(1, 4, 2);
+  else if (cfg == 404) SHERRY_LUT_WIN(1, 4, 4);
+  else if (cfg == 208) {
+    if (p.window_sbs >= 2) SHERRY_LUT(2, 1, 2, 8);
+    else SHERRY_LUT(1, 1, 2, 8);
+  } else if (cfg == 116) SHERRY_LUT(1, 1, 1, 16);
+  else return hipErrorInvalidValue;
+#undef SHERRY_LUT_WIN
+#undef SHERRY_LUT
+  return hipSuccess;
 }
 
 template <int GRAN, bool YBF16>
@@ -682,12 +742,15 @@ hipError_t launch_gemv_t(const GemvPlan& p, int64_t n, int64_t k, int group_size
   const int group_sbs = GRAN == SHERRY_PER_GROUP ? group_size / kSuperblock : 1;
   const dim3 grid((unsigned)p.panels, (unsigned)count, (unsigned)p.ksplit);
   if (p.kind == 0) {
-    const size_t lds = 0;  // the table is static LDS sized by the window
     const int mode = GRAN == SHERRY_PER_CHANNEL ? kChannel
                    : GRAN == SHERRY_PER_TENSOR  ? kTensor
                    : (group_sbs == 1 ? kGroup1 : kGroupN);
-    launch_lut<YBF16>(mode, p.window_sbs, p.rows_per_thread, grid, lds, s, packed, alpha, x, y, ws, n, k,
-                      group_sbs, p.ksplit, packed_stride, alpha_stride, y_stride);
+    hipError_t le;
+    if (mode == kGroup1) le = launch_lut<kGroup1, YBF16>(p, grid, s, packed, alpha, x, y, ws, n, k, group_sbs, packed_stride, alpha_stride, y_stride);
+    else if (mode == kGroupN) le = launch_lut<kGroupN, YBF16>(p, grid, s, packed, alpha, x, y, ws, n, k, group_sbs, packed_stride, alpha_stride, y_stride);
+    else if (mode == kChannel) le = launch_lut<kChannel, YBF16>(p, grid, s, packed, alpha, x, y, ws, n, k, group_sbs, packed_stride, alpha_stride, y_stride);
+    else le = launch_lut<kTensor, YBF16>(p, grid, s, packed, alpha, x, y, ws, n, k, group_sbs, packed_stride, alpha_stride, y_stride);
+    if (le != hipSuccess) return le;
   } else {
     const int mode = GRAN == SHERRY_PER_CHANNEL ? kChannel
                    : GRAN == SHERRY_PER_TENSOR  ? kTensor
@@ -732,30 +795,66 @@ GemvPlan plan_gemv(int64_t n, int64_t k, int gran, int group_size, int batch, in
   GemvPlan p{};
   const int64_t nsb = k / kSuperblock;
   const int64_t group_sbs = gran == SHERRY_PER_GROUP ? group_size / kSuperblock : 1;
-  p.kind = batch == 1 ? 0 : 1;
-  int64_t rows_per_wg;
-  if (p.kind == 0) {
-    // four row slots per thread amortize the table build once the grid is large
-    const int64_t wg1 = ((n + kLutThreads - 1) / kLutThreads) * count;
-    p.rows_per_thread = wg1 >= 4096 ? SHERRY_LUT_ROWS : 1;
-    rows_per_wg = (int64_t)kLutThreads * p.rows_per_thread;
-  } else {
-    p.rows_per_thread = 1;
-    rows_per_wg = 64 * kMfmaTiles;
-  }
-  p.panels = (n + rows_per_wg - 1) / rows_per_wg;
-  // Split K (in whole groups) until the launch has ~2048 workgroups (batch 1;
-  // the table kernel keeps 8 per CU resident) or ~768 (batch > 1, 3-5 per CU resident).
-  const int64_t wgs = p.panels * count;
   const int64_t groups = nsb / group_sbs;
+  p.ksplit = 1;
+  if (batch == 1) {
+    // Batch 1: 256-row workgroups sharing one set of tables (four row slots
+    // per thread on very large grids).  A launch with fewer than
+    // SHERRY_GEMV_SPLIT_TARGET of them splits K: inside the workgroup (KW
+    // K-slices of 64-256 rows each, partial sums added through LDS, one
+    // kernel) when every slice then holds a single window of tables -- this
+    // is what single calls with K up to 2048 get -- and otherwise across
+    // workgroups into fp32 partials summed by a second kernel in split order
+    // (measured faster for long K and for the batched launches, whose
+    // workgroups then need no barrier coupling between slices).
+    p.kind = 0;
+    p.rw = 4;
+    p.kw = 1;
+    const int64_t wg256 = (n + kLutThreads - 1) / kLutThreads * count;
+    p.rows_per_thread = wg256 >= 4096 ? SHERRY_LUT_ROWS : 1;
+    p.panels = (n + 256 * p.rows_per_thread - 1) / (256 * p.rows_per_thread);
+    int64_t split = 1;
+    while (p.panels * count * split * 2 <= SHERRY_GEMV_SPLIT_TARGET && groups % (split * 2) == 0) split *= 2;
+    if (split > 1) {
+      static const int cand[4][2] = {{1, 16}, {2, 8}, {4, 4}, {4, 2}};
+      int64_t best_waves = 0;
+      for (int i = 0; i < 4; ++i) {
+        const int rw = cand[i][0], kw = cand[i][1];
+        const int win_max = 16 / kw < 4 ? 16 / kw : 4;
+        if (groups % kw != 0 || nsb / kw > win_max) continue;  // one window per slice
+        const int64_t waves = (n + 64 * rw - 1) / (64 * rw) * count * rw * kw;
+        if (waves > best_waves) {
+          best_waves = waves;
+          p.rw = rw;
+          p.kw = kw;
+        }
+      }
+      if (p.kw > 1) {
+        split = 1;
+        p.rows_per_thread = 1;
+        p.panels = (n + 64 * p.rw - 1) / (64 * p.rw);
+      }
+    }
+    p.ksplit = (int)split;
+    const int64_t per_slice = nsb / split / p.kw;
+    int win = SHERRY_LUT_WIN_MAX < 4 ? SHERRY_LUT_WIN_MAX : 4;
+    while (win > 1 && (per_slice % win != 0 || win * p.kw > 16)) win >>= 1;
+    p.window_sbs = win;
+    p.workspace_bytes = split > 1 ? (size_t)count * split * n * sizeof(float) : 0;
+    return p;
+  }
+  // Batch 2..16: split K (in whole groups) across workgroups until the
+  // launch has ~768 of them (3-5 per CU resident); a second kernel sums the
+  // partials.
+  p.kind = 1;
+  p.rows_per_thread = 1;
+  p.rw = p.kw = 1;
+  p.panels = (n + 64 * kMfmaTiles - 1) / (64 * kMfmaTiles);
+  const int64_t wgs = p.panels * count;
   int64_t split = 1;
-  const int64_t target = p.kind == 0 ? SHERRY_GEMV_SPLIT_TARGET : SHERRY_GEMV_MFMA_SPLIT_TARGET;
-  while (wgs * split * 2 <= target && groups % (split * 2) == 0) split *= 2;
+  while (wgs * split * 2 <= SHERRY_GEMV_MFMA_SPLIT_TARGET && groups % (split * 2) == 0) split *= 2;
   p.ksplit = (int)split;
-  const int64_t sb_per_split = nsb / split;
-  int win = SHERRY_LUT_WIN_MAX;
-  while (sb_per_split % win != 0) win >>= 1;
-  p.window_sbs = win;
+  p.window_sbs = 1;
   p.workspace_bytes = split > 1 ? (size_t)count * split * batch * n * sizeof(float) : 0;
   return p;
 }

@@ -64,7 +64,8 @@ struct GemvPlan {
   int kind;               // 0 = table-lookup kernel (batch 1), 1 = MFMA kernel (batch 2..16)
   int rows_per_thread;    // kind 0
   int window_sbs;         // kind 0: superblocks per LDS table window
-  int ksplit;             // split of K across workgroups (1 = none)
+  int ksplit;             // kind 1: split of K across workgroups (1 = none)
+  int rw, kw;             // kind 0: row waves x K-slices per workgroup
   int64_t panels;         // workgroups along N
   size_t workspace_bytes; // ksplit > 1: fp32 partials [count][ksplit][batch][N]
 };

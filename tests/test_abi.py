@@ -122,11 +122,13 @@ def test_gemv_rejects(lib, kw, code):
 
 
 def test_gemv_workspace_rejected_when_needed(lib):
-    # a 64x512 single call is split along K, which needs a workspace
-    need = lib.sherry_workspace_bytes(L.OP_GEMV, 64, 512, L.PER_GROUP, 128, 1, 1)
+    # a batch-1 call splits K inside its workgroups (no workspace); at batch 4
+    # a 64x512 single call is split across workgroups, which needs one
+    assert lib.sherry_workspace_bytes(L.OP_GEMV, 64, 512, L.PER_GROUP, 128, 1, 1) == 0
+    need = lib.sherry_workspace_bytes(L.OP_GEMV, 64, 512, L.PER_GROUP, 128, 4, 1)
     assert need > 0
-    assert gv(lib) == L.ERR_WORKSPACE
-    assert gv(lib, ws=FAKE, wsb=need - 4) == L.ERR_WORKSPACE
+    assert gv(lib, b=4) == L.ERR_WORKSPACE
+    assert gv(lib, b=4, ws=FAKE, wsb=need - 4) == L.ERR_WORKSPACE
 
 
 def gm(lib, n=64, k=512, gran=L.PER_GROUP, g=128, packed=FAKE, alpha=FAKE2, x=FAKE, m=32, y=FAKE2):

@@ -60,6 +60,8 @@ BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
 METRIC = "Sherry 1.25-bit GEMV HBM GB/s (% of peak) + GEMM TFLOP/s, 1B/3B shapes"
 COUNTERS_FILE = os.path.join(ROOT, "profiles", "gemv_b1_lut_counters.json")
 GEMV_SOURCE = os.path.join(ROOT, "ternary_weight_quantization_sparse_amd", "csrc", "gemv.hip")
+GEMM_COUNTERS_FILE = os.path.join(ROOT, "profiles", "gemm_counters.json")
+GEMM_SOURCE = os.path.join(ROOT, "ternary_weight_quantization_sparse_amd", "csrc", "gemm.hip")
 
 
 def log(*a):
@@ -209,17 +211,38 @@ def timed_launches(launches, steps, warmup, per_launch=True):
     return t0.elapsed_time(t1), per, wall
 
 
-def counters_for_current_source():
-    """HBM traffic per launch measured with rocprofv3 counters, if it was
-    taken on the current GEMV source (else None)."""
-    if not os.path.exists(COUNTERS_FILE):
+def counters_for_current_source(path=COUNTERS_FILE, source=GEMV_SOURCE, key="gemv_source_sha256"):
+    """Counter record measured with rocprofv3 (HBM traffic per launch, MFMA
+    busy), if it was taken on the current kernel source (else None)."""
+    if not os.path.exists(path):
         return None
-    with open(COUNTERS_FILE) as f:
+    with open(path) as f:
         rec = json.load(f)
-    with open(GEMV_SOURCE, "rb") as f:
+    with open(source, "rb") as f:
         digest = hashlib.sha256(f.read()).hexdigest()
-    if rec.get("gemv_source_sha256") != digest:
+    if rec.get(key) != digest:
         return None
+    return rec
+
+
+def gemm_roofline(gemm):
+    """MFMA roofline of the prefill GEMM at M = 2048 (the 1B layer's seven
+    launches, per_group 128): issued TFLOP/s on 2MNK against the 2.5 PFLOP/s
+    dense bf16 peak, the algorithmic 1.5MNK beside it, and the counter-backed
+    MFMA busy fraction and HBM traffic when profiles/gemm_counters.json was
+    taken on the current gemm.hip."""
+    entry = gemm.get("2048")
+    if entry is None:
+        return None
+    ctr = counters_for_current_source(GEMM_COUNTERS_FILE, GEMM_SOURCE, "gemm_source_sha256")
+    rec = {"bound": "mfma", "achieved": entry["tflops"], "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+           "frac": entry["tflops"] / BF16_PEAK_TFLOPS, "achieved_algorithmic_1.5mnk": entry["tflops"] * 0.75,
+           "kernel": "gemm_kernel", "m": 2048, "flops_counted": "2MNK (issued MFMA work)",
+           "mfma_busy": None, "traffic": None, "counters": None}
+    if ctr is not None:
+        rec["mfma_busy"] = ctr.get("mfma_busy_m2048_layer")
+        rec["traffic"] = ctr.get("traffic_bytes_m2048_layer")
+        rec["counters"] = os.path.relpath(GEMM_COUNTERS_FILE, ROOT)
     return rec
 
 
@@ -993,6 +1016,7 @@ def main():
                    "bytes_per_step": gemv["bytes_per_step"]},
         "hbm_frac": gemv["value"] / HBM_PEAK_GBS,
         "roofline": roofline,
+        "gemm_roofline": gemm_roofline(extra["gemm"]) if "gemm" in extra else None,
         "cpu_baseline": cpu,
         "gemv_shapes": gemv["shapes"],
         "parity": gemv["checks"],

@@ -614,6 +614,45 @@ def bench_gemm(pws, dev, ms, reps=20):
     return res
 
 
+def bench_gemm_shapes(pws, dev, ms=(512, 2048), launches=10):
+    """For counter collection: each 1B shape's plain GEMM (per_group 128)
+    launched ``launches`` times back to back, M = 512 then 2048, shapes in
+    q, k, v, o, gate, up, down order, so a profiler's dispatch sequence maps
+    to (M, shape) by position.  Returns the per-shape median ms."""
+    import numpy as np
+    import workloads as WL
+    import ternary_weight_quantization_sparse_amd as S
+    torch = _torch()
+    lib = S.load()
+    stream = torch.cuda.current_stream().cuda_stream
+    # bring the clock up under matrix load first (torch's bf16 matmul, not
+    # this library's kernels, so the profiled dispatch sequence is unchanged)
+    a = torch.randn((4096, 4096), device=dev).to(torch.bfloat16)
+    t_end = time.perf_counter() + 0.4
+    while time.perf_counter() < t_end:
+        torch.matmul(a, a)
+        torch.cuda.synchronize()
+    del a
+    out = {}
+    for m in ms:
+        xb, _ = WL.activations_bf16(m, 8192, 300 + m)
+        xs = {k: dev_bf16(np.ascontiguousarray(xb[:, :k]), dev) for k in (2048, 8192)}
+        for (name, n, k, pw, _) in pws:
+            y = torch.empty((m, n), dtype=torch.bfloat16, device=dev)
+            b = S.workspace_bytes(3, n, k, "per_group", 128, m)
+            ws = torch.empty(max(b, 16), dtype=torch.uint8, device=dev)
+            ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                  for _ in range(launches)]
+            for e0, e1 in ev:
+                e0.record()
+                S.check(lib.sherry_gemm(n, k, 2, 128, pw.packed.data_ptr(), pw.alpha.data_ptr(), xs[k].data_ptr(),
+                                        m, y.data_ptr(), ws.data_ptr(), b, stream))
+                e1.record()
+            torch.cuda.synchronize()
+            out[f"{m}/{name}"] = float(np.median([a.elapsed_time(c) for a, c in ev]))
+    return out
+
+
 def quantize_consistent(w, pw):
     """GPU checks of a quantization that need no oracle: one zero per block,
     the zero on a smallest |w| of its block, kept signs +1 iff w > 0, scales
@@ -950,7 +989,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--sections", default="gemv,single,layer,compare,gemm,quantize,unpack,gemv3b,cpu",
                     help="comma list of: gemv (always), single, layer, compare, gemm, quantize, unpack, gemv3b, cpu, "
-                         "copycal (a 1 GiB device copy for scaling HBM counters)")
+                         "copycal (a 1 GiB device copy for scaling HBM counters), gemmshapes (each GEMM shape "
+                         "launched 10 times in a fixed order, for counter collection)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU: this build has no multi-GPU path (asked for {args.gpus}). "
@@ -974,6 +1014,8 @@ def main():
         extra["compare_formats"] = bench_compare(pws, dev)
     if "gemm" in sections:
         extra["gemm"] = bench_gemm(pws, dev, (512, 2048))
+    if "gemmshapes" in sections:
+        extra["gemm_shapes_ms"] = bench_gemm_shapes(pws, dev)
     if "quantize" in sections:
         extra["quantize"] = bench_quantize(dev)
     if "unpack" in sections:

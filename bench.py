@@ -30,7 +30,8 @@ Also reported, each timed with HIP events on the launch stream:
   cpu_baseline  the CPU oracle (NumPy, BLAS on every host core this process
             may use) on bounded samples: one 1B layer from packed bytes to
             fp64 outputs (the headline's unit), one 1B layer at M = 512
-            (TFLOP/s), and 4096 rows of the quantize workload (GB/s).
+            (TFLOP/s), and 4096 rows of the quantize workload, quantized and
+            unpacked (GB/s).
 Every timed configuration is first cross-checked on the GPU: products against
 an fp64 product over the library's unpacked weight, to the parity tolerance;
 quantizations for their invariants.  Parity with the CPU oracle of these same
@@ -966,6 +967,13 @@ def cpu_baseline(pws, min_seconds=10.0, gemm_m=512, quant_rows=4096):
         packed_q, alpha_q = O.quantize_pack(ws, "per_group", 128)
         q_secs = time.perf_counter() - t2
         q_bytes = ws.size * 2 + packed_q.size + alpha_q.size * 4
+
+        # unpack of the same sample's planes to the dense T * alpha (fp32)
+        t3 = time.perf_counter()
+        t_q = O.decode_codes(O.unpack(packed_q, quant_rows, 8192))
+        wq = O.dequant(t_q, alpha_q, "per_group", 128).astype(np.float32)
+        u_secs = time.perf_counter() - t3
+        u_bytes = packed_q.size + alpha_q.size * 4 + wq.size * 4
     return {"value": total_bytes / secs / 1e9, "unit": "GB/s", "cores": cores, "kind": "oracle",
             "cpu_model": model, "blas": blas, "seconds": secs, "passes": passes,
             "sample": f"{passes} passes over one LLaMA-3.2-1B layer (7 linears, batch 1, group 128): "
@@ -978,7 +986,10 @@ def cpu_baseline(pws, min_seconds=10.0, gemm_m=512, quant_rows=4096):
                          "gweights_per_s": ws.size / q_secs / 1e9,
                          "sample": f"{quant_rows} of the 8192 rows of the 8192 x 8192 bf16 weight with 1% "
                                    "outliers x10, per_group 128 quantize + pack (bytes read + written, as "
-                                   "the GPU quantize rows)"}}
+                                   "the GPU quantize rows)"},
+            "unpack": {"value": u_bytes / u_secs / 1e9, "unit": "GB/s", "seconds": u_secs,
+                       "sample": f"the planes + scales of those {quant_rows} rows to fp32 T * alpha (planes + "
+                                 "scales read, dense output written, as the GPU unpack rows)"}}
 
 
 # ----------------------------------------------------------------------------
@@ -1035,7 +1046,7 @@ def main():
     if cpu:
         log(f"[cpu] oracle {cpu['value']:.3f} GB/s in {cpu['seconds']:.1f} s ({cpu['cores']} cores, "
             f"{cpu['cpu_model']}); GEMM {cpu['gemm']['value']:.4f} TFLOP/s; quantize "
-            f"{cpu['quantize']['value']:.4f} GB/s")
+            f"{cpu['quantize']['value']:.4f} GB/s; unpack {cpu['unpack']['value']:.4f} GB/s")
 
     ctr = counters_for_current_source()
     traffic = None

@@ -103,7 +103,8 @@ __device__ inline float dpp(float v) {
   return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
 }
 constexpr int kShr1 = 0x111, kShr2 = 0x112, kShr4 = 0x114, kShr8 = 0x118, kRor4 = 0x124, kRor8 = 0x128;
-// row_shl:n / row_shr:n (lane i gets lane i + n / i - n of its row), n = 1..7
+// row_shl:n (n = 1..15) / row_shr:n (n = 1..7): lane i gets lane i + n /
+// i - n of its row
 template <typename T>
 __device__ inline T dpp_shl(T v, int n) {
   switch (n) {
@@ -113,7 +114,15 @@ __device__ inline T dpp_shl(T v, int n) {
     case 4: return dpp<0x104>(v);
     case 5: return dpp<0x105>(v);
     case 6: return dpp<0x106>(v);
-    default: return dpp<0x107>(v);
+    case 7: return dpp<0x107>(v);
+    case 8: return dpp<0x108>(v);
+    case 9: return dpp<0x109>(v);
+    case 10: return dpp<0x10A>(v);
+    case 11: return dpp<0x10B>(v);
+    case 12: return dpp<0x10C>(v);
+    case 13: return dpp<0x10D>(v);
+    case 14: return dpp<0x10E>(v);
+    default: return dpp<0x10F>(v);
   }
 }
 template <typename T>
@@ -491,6 +500,257 @@ __global__ __launch_bounds__(256) void tree_level_kernel(const float* __restrict
   }
 }
 
+// ---------------------------------------------------------------------------
+// Row-group quantize + pack (K up to kRowsMaxSb superblocks): the codes as
+// above with fewer instructions per block, and the scales of every
+// granularity finished in the same launch (per_tensor: down to one partial
+// per row group).
+//
+// Work unit: one chunk (four superblocks) of a group of 8 rows, one wave: lane
+// (s, i) reads blocks 2i, 2i + 1 of superblock 4c + s of each of the 8 rows,
+// all 8 loads first.  Per block, block_zero gives the zero position and the
+// kept-|w| sum, a dot product of the positive-flag bytes gives the table
+// index 4 * pos + z, and one LDS table read returns the block's nibble and
+// sign bit already placed for the lane's byte.  The 16 lanes of a superblock
+// combine with row_ror DPP moves: the four nibble dwords, the sign dword (in
+// every lane), and the superblock's kept-|w| sum, which lane 15 ends with as
+// the index-order pairwise tree over the 32 blocks (every add pairs the same
+// two subtrees as the tree; fp32 addition is commutative).  Each row's sign
+// dword and sum are then gathered into lane 15 - row of the group, so one
+// store covers the 8 rows.
+//
+// per_group G = 128 (kRowsDirect): workgroup (x, y) = chunk x of rows 32 y ..
+// (four waves, 8 rows each) -- consecutive workgroups read adjacent spans of
+// the same rows -- and each superblock sum over 96 is stored at once.  Every
+// other scale needs a row's sums from all chunks, so there a workgroup of
+// min(4, chunks) waves owns one row group and walks its chunks, the sums wait
+// in LDS, and after a barrier:
+//   kRowsGroup    per_group G = 128 r: the pairwise tree over each group's r
+//                 sums, over 96 r;
+//   kRowsChannel  per_channel: the tree over the row's nsb sums (E per lane,
+//                 then an XOR butterfly: the index-order tree over 64 E values,
+//                 i.e. over the row padded to a power of two), over 96 nsb;
+//   kRowsTensor   per_tensor with nsb a power of two: a row is then an aligned
+//                 subtree of the tree over the flat weight order, and so is
+//                 the row group; the workgroup writes that subtree's root for
+//                 the tree levels that follow;
+//   kRowsSums     per_tensor otherwise: the superblock sums, row-major, for
+//                 the tree levels.
+// Measured on the 8192 x 8192 bf16 weight against the superblock-tile kernel
+// and its second-stage launches: per_channel 33.0 vs 33.6 us, per_tensor
+// 35.4 vs 37.0 us, per_group 128 30.0 vs 29.6 us, with 21% fewer VALU
+// instructions -- the time is set by the memory pipeline, not the ALU.
+constexpr int kRowsGroup = 0, kRowsChannel = 1, kRowsTensor = 2, kRowsSums = 3, kRowsDirect = 4;
+constexpr int64_t kRowsMaxSb = 512;  // 8 rows x 512 superblock sums in LDS = 16 KB
+constexpr int kRgRows = kRowsPerWave;  // rows per wave and per row group
+constexpr int kRgWaves = 4;            // waves per workgroup (at most)
+constexpr int kRor1 = 0x121, kRor2 = 0x122;
+
+// row_ror moves: every lane of the row has a source, so no bound control
+template <int CTRL>
+__device__ inline uint32_t dpp_ror(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xF, 0xF, true);
+}
+template <int CTRL>
+__device__ inline float dpp_ror(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, true));
+}
+
+// bytes 0..3 = 0xFF where bf16 weights w0..w3 are > 0 (d0 = w0 | w1 << 16,
+// d1 = w2 | w3 << 16): the sign bit of each saturated 16-bit 0 - w (set
+// exactly for w in 1 .. 0x7FFF; -0, 0x8000, saturates to 0x7FFF), gathered
+// by v_perm's sign-replicating selectors 8..11 (bits 15 / 31 of each source).
+__device__ inline uint32_t positive_bytes_bf16(uint32_t d0, uint32_t d1) {
+  uint32_t t0, t1;
+  asm("v_pk_sub_i16 %0, 0, %2 clamp\n"
+      "v_pk_sub_i16 %1, 0, %3 clamp"
+      : "=&v"(t0), "=&v"(t1)
+      : "v"(d0), "v"(d1));
+  return __builtin_amdgcn_perm(t1, t0, 0x0B0A0908u);
+}
+
+// Table index of block j (0, 1) of a lane: 4 * pos + z, pos = the positive
+// flags of weights 0..3 in bits 0..3; kept = the block's kept-|w| sum.
+template <bool BF16>
+__device__ inline uint32_t lane_block(const LaneRaw<BF16, 2>& r, int j, float& kept) {
+  float v[4];
+  if constexpr (BF16) {
+    const uint32_t d0 = j ? r.q[0].z : r.q[0].x, d1 = j ? r.q[0].w : r.q[0].y;
+    v[0] = __uint_as_float(d0 << 16);
+    v[1] = __uint_as_float(d0 & 0xFFFF0000u);
+    v[2] = __uint_as_float(d1 << 16);
+    v[3] = __uint_as_float(d1 & 0xFFFF0000u);
+    const uint32_t z = block_zero(v, kept);
+    // bytes of -1 (0xFF) where positive, times -4, -8, -16, -32, plus z
+    return (uint32_t)__builtin_amdgcn_sdot4((int)positive_bytes_bf16(d0, d1), (int)0xE0F0F8FCu, (int)z, false);
+  } else {
+    const uint4 u = r.q[j];
+    v[0] = __uint_as_float(u.x); v[1] = __uint_as_float(u.y);
+    v[2] = __uint_as_float(u.z); v[3] = __uint_as_float(u.w);
+    const uint32_t z = block_zero(v, kept);
+    return z | (v[0] > 0.f ? 4u : 0u) | (v[1] > 0.f ? 8u : 0u) | (v[2] > 0.f ? 16u : 0u) | (v[3] > 0.f ? 32u : 0u);
+  }
+}
+
+// In-place pairwise tree over x[0 .. r) padded with +0 to a power of two
+// (adds that would take a padded +0 leave the value as it is).
+__device__ inline float tree_inplace(float* x, int64_t r) {
+  int64_t width = 1;
+  while (width < r) width <<= 1;
+  for (int64_t h = 1; h < width; h <<= 1)
+    for (int64_t j = 0; j + h < r; j += 2 * h) x[j] = x[j] + x[j + h];
+  return x[0];
+}
+
+template <bool BF16, int MODE, int E>
+// (eight waves per SIMD: the register budget is 64)
+__global__ __launch_bounds__(64 * kRgWaves) __attribute__((amdgpu_waves_per_eu(8)))
+void quantize_rowgroup_kernel(
+    const void* __restrict__ w, int64_t n, int64_t k, int group_r, uint8_t* __restrict__ packed,
+    float* __restrict__ alpha, float* __restrict__ ws) {
+  constexpr int RW = kRgRows;
+  extern __shared__ float sb_lds[];  // [RW][4 C] superblock kept-|w| sums (unless per_group 128)
+  __shared__ uint16_t tab[128];      // per index: block 2i's entry, block 2i + 1's entry
+  __shared__ float roots[RW];
+  const int64_t nsb = k / kSuperblock;
+  const int64_t C = (nsb + 3) / 4;  // chunks of four superblocks
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, W = blockDim.x >> 6;
+  const int s = lane >> 4, i = lane & 15;
+  constexpr bool direct = MODE == kRowsDirect;
+  const int64_t grp = blockIdx.x;  // row group (modes other than direct)
+  const int64_t row0 = direct ? ((int64_t)blockIdx.y * W + wave) * RW : grp * RW;
+
+  // entry = the block's nibble and sign bit where the lane's byte wants them:
+  // block 2i: nibble bits 0..3, sign bit 8; block 2i + 1: bits 4..7, bit 9
+  if (threadIdx.x < 64) {
+    const uint32_t code = block_code(threadIdx.x & 3, threadIdx.x >> 2);
+    tab[2 * threadIdx.x] = (uint16_t)((code & 15u) | ((code >> 4) << 8));
+    tab[2 * threadIdx.x + 1] = (uint16_t)(((code & 15u) << 4) | ((code >> 4) << 9));
+  }
+  constexpr int64_t kElem = BF16 ? 2 : 4;
+  // v_perm selector putting the low byte of its second source at byte i / 4
+  const uint32_t sel_nib = 0x0C0C0C0Cu & ~(0xFFu << (8 * (i >> 2)));
+  uint32_t* nib_plane = reinterpret_cast<uint32_t*>(packed);
+  uint32_t* sgn_plane = reinterpret_cast<uint32_t*>(packed + nibble_plane_bytes(n, k));
+
+  // one chunk of the 8 rows, from registers already loaded
+  auto process = [&](const LaneRaw<BF16, 2>(&lw)[RW], int64_t c) {
+    const int64_t g = 4 * c + s;  // this lane's superblock
+    const bool gv = g < nsb;
+    const int64_t rec0 = g * n + row0;  // record of (g, row0); rows follow
+    uint32_t* nib_rec = nib_plane + rec0 * 4 + i;
+    float sv = 0.f;
+    uint32_t sgv = 0;
+#pragma unroll
+    for (int it = 0; it < RW; ++it) {
+      const int64_t row = row0 + it;
+      float k0, k1;
+      const uint32_t i0 = lane_block<BF16>(lw[it], 0, k0);
+      const uint32_t i1 = lane_block<BF16>(lw[it], 1, k1);
+      const uint32_t comb = (uint32_t)tab[2 * i0] + (uint32_t)tab[2 * i1 + 1];
+      // nibble dwords: lane i's byte is byte i / 4 of dword i % 4
+      uint32_t nib = __builtin_amdgcn_perm(0u, comb, sel_nib);
+      nib |= dpp_ror<kRor4>(nib);
+      nib |= dpp_ror<kRor8>(nib);
+      if (gv && row < n && i < 4) nib_rec[it * 4] = nib;
+      // sign dword (every lane of the group): bit b = sign bit of block b
+      uint32_t sg = ((comb >> 8) & 3u) << (2 * i);
+      sg |= dpp_ror<kRor1>(sg);
+      sg |= dpp_ror<kRor2>(sg);
+      sg |= dpp_ror<kRor4>(sg);
+      sg |= dpp_ror<kRor8>(sg);
+      // superblock sum: lane 15 pairs (14, 15), then (13, 15), (11, 15), (7, 15)
+      float sum = k0 + k1;
+      sum += dpp_ror<kRor1>(sum);
+      sum += dpp_ror<kRor2>(sum);
+      sum += dpp_ror<kRor4>(sum);
+      sum += dpp_ror<kRor8>(sum);
+      // lane 15 - it of each group keeps row it's sum (from lane 15) and sign
+      // dword (its own), so one store of each serves the 8 rows
+      if (it == 0) {
+        sv = sum;
+        sgv = sg;
+      } else {
+        const float sh = dpp_shl(sum, it);
+        if (i == 15 - it) { sv = sh; sgv = sg; }
+      }
+    }
+    const int rit = 15 - i;  // the row this lane now holds
+    if (gv && rit < RW && row0 + rit < n) {
+      sgn_plane[rec0 + rit] = sgv;
+      if (direct) alpha[rec0 + rit] = (float)((double)sv / 96.0);
+      else sb_lds[rit * 4 * C + g] = sv;
+    }
+  };
+  // every load of a chunk at once, from clamped in-bounds addresses (rows
+  // past n and superblocks past K repeat the last valid ones, never stored)
+  const int64_t last = n - 1 - row0;  // rows past it repeat it
+  auto load = [&](LaneRaw<BF16, 2>(&lw)[RW], int64_t c) {
+    const int64_t g = 4 * c + s < nsb ? 4 * c + s : nsb - 1;
+    const char* p = reinterpret_cast<const char*>(w) + (row0 * k + g * kSuperblock + 8 * i) * kElem;
+#pragma unroll
+    for (int it = 0; it < RW; ++it) lw[it] = load_lane<BF16, 2>(p + (it < last ? it : last) * k * kElem);
+  };
+
+  // direct: this wave's one chunk; otherwise the row group's chunks in turn
+  const int64_t stride = direct ? C : W;
+  int64_t c = direct ? (int64_t)blockIdx.x : wave;
+  __syncthreads();  // the table is written
+  for (; c < C; c += stride) {
+    LaneRaw<BF16, 2> lw[RW];
+    load(lw, c);
+    process(lw, c);
+  }
+  if constexpr (!direct) {
+    __syncthreads();  // every superblock sum of the row group is in LDS
+    if constexpr (MODE == kRowsGroup) {
+      const int64_t groups = nsb / group_r;
+      const double denom = (double)group_r * kSuperblock / 4.0 * 3.0;
+      for (int64_t t = threadIdx.x; t < RW * groups; t += blockDim.x) {
+        const int64_t rit = t / groups, gg = t % groups;
+        if (row0 + rit < n)
+          alpha[gg * n + row0 + rit] =
+              (float)((double)tree_inplace(sb_lds + rit * 4 * C + gg * group_r, group_r) / denom);
+      }
+    } else if constexpr (MODE == kRowsSums) {
+      for (int64_t t = threadIdx.x; t < RW * nsb; t += blockDim.x) {
+        const int64_t rit = t / nsb, g = t % nsb;
+        if (row0 + rit < n) ws[(row0 + rit) * nsb + g] = sb_lds[rit * 4 * C + g];
+      }
+    } else {
+      for (int rit = wave; rit < RW; rit += W) {
+        const float* rs = sb_lds + rit * 4 * C;
+        float v[E];
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+          const int64_t idx = (int64_t)lane * E + e;
+          v[e] = (row0 + rit < n && idx < nsb) ? rs[idx] : 0.f;
+        }
+#pragma unroll
+        for (int h = E; h > 1; h >>= 1)
+#pragma unroll
+          for (int e = 0; e < h / 2; ++e) v[e] = v[2 * e] + v[2 * e + 1];
+        float sum = v[0];
+        sum += __shfl_xor(sum, 1);
+        sum += __shfl_xor(sum, 2);
+        sum += __shfl_xor(sum, 4);
+        sum += __shfl_xor(sum, 8);
+        sum += __shfl_xor(sum, 16);
+        sum += __shfl_xor(sum, 32);
+        if constexpr (MODE == kRowsChannel) {
+          if (lane == 0 && row0 + rit < n) alpha[row0 + rit] = (float)((double)sum / ((double)k / 4.0 * 3.0));
+        } else {
+          if (lane == 0) roots[rit] = sum;  // rows past n: +0
+        }
+      }
+      if constexpr (MODE == kRowsTensor) {
+        __syncthreads();
+        if (threadIdx.x == 0) ws[grp] = tree_inplace(roots, RW);
+      }
+    }
+  }
+}
+
 // Grid: x = groups of 2*BPL superblocks, y = tiles of kRowsPerWg rows, so
 // consecutive workgroups read adjacent spans of the same rows.
 inline dim3 quantize_grid(int64_t n, int64_t nsb) {
@@ -503,6 +763,24 @@ inline dim3 quantize_grid(int64_t n, int64_t nsb) {
 QuantizePlan plan_quantize(int64_t n, int64_t k, int gran, int group_size) {
   QuantizePlan p{};
   const int64_t nsb = k / kSuperblock;
+  if (nsb <= kRowsMaxSb) {
+    p.rows = true;
+    p.wg_rows = kRgRows;
+    const int64_t wgs = (n + p.wg_rows - 1) / p.wg_rows;
+    if (gran == SHERRY_PER_GROUP) {
+      p.rows_mode = kRowsGroup;
+    } else if (gran == SHERRY_PER_CHANNEL) {
+      p.rows_mode = kRowsChannel;
+    } else {
+      const bool pow2 = (nsb & (nsb - 1)) == 0;
+      p.rows_mode = pow2 ? kRowsTensor : kRowsSums;
+      p.sb_sums = pow2 ? wgs : n * nsb;  // workgroup subtree roots, or superblock sums
+      p.chunk = kTreeChunk;
+      p.chunks = 2 * ((p.sb_sums + kTreeChunk - 1) / kTreeChunk);
+    }
+    p.workspace_bytes = (size_t)(p.sb_sums + p.chunks) * sizeof(float);
+    return p;
+  }
   p.direct_alpha = (gran == SHERRY_PER_GROUP && group_size == kSuperblock);
   if (p.direct_alpha) return p;
   p.sb_sums = n * nsb;
@@ -514,10 +792,78 @@ QuantizePlan plan_quantize(int64_t n, int64_t k, int gran, int group_size) {
   return p;
 }
 
+namespace {
+
+// per_tensor: tree levels over `real` partials at ws (each level one launch
+// of aligned 4096-value chunks) down to the one scale.
+void launch_tree_levels(const QuantizePlan& p, const float* in, int64_t real, double denom, float* alpha,
+                        float* ws, hipStream_t s) {
+  float* bufs[2] = {ws + p.sb_sums, ws + p.sb_sums + p.chunks / 2};
+  for (int level = 0;; ++level) {
+    const int64_t chunks = (real + kTreeChunk - 1) / kTreeChunk;
+    if (chunks == 1) {
+      hipLaunchKernelGGL(tree_level_kernel, dim3(1), dim3(256), 0, s, in, real, alpha, denom);
+      break;
+    }
+    float* out = bufs[level & 1];
+    hipLaunchKernelGGL(tree_level_kernel, dim3((unsigned)chunks), dim3(256), 0, s, in, real, out, 0.0);
+    in = out;
+    real = chunks;
+  }
+}
+
+template <bool BF16, int MODE, int E>
+void launch_rows(const QuantizePlan& p, int64_t n, int64_t k, int group_r, const void* w, uint8_t* packed,
+                 float* alpha, float* ws, hipStream_t s) {
+  const int64_t nsb = k / kSuperblock;
+  const int64_t chunks = (nsb + 3) / 4;
+  constexpr bool direct = MODE == kRowsDirect;
+  const int waves = direct ? kRgWaves : (int)(chunks < kRgWaves ? chunks : kRgWaves);
+  const size_t lds = direct ? 0 : (size_t)kRgRows * 4 * chunks * sizeof(float);
+  const int64_t groups = (n + kRgRows - 1) / kRgRows;
+  const dim3 grid = direct ? dim3((unsigned)chunks, (unsigned)((groups + waves - 1) / waves)) : dim3((unsigned)groups);
+  hipLaunchKernelGGL((quantize_rowgroup_kernel<BF16, MODE, E>), grid, dim3(64 * waves), lds, s, w, n, k, group_r,
+                     packed, alpha, ws);
+}
+
+template <bool BF16>
+void launch_rows_mode(const QuantizePlan& p, int64_t n, int64_t k, int group_r, const void* w, uint8_t* packed,
+                      float* alpha, float* ws, hipStream_t s) {
+  const int64_t nsb = k / kSuperblock;
+  const int64_t e = (nsb + 63) / 64;
+  switch (p.rows_mode) {
+    case kRowsGroup:
+      if (group_r == 1) launch_rows<BF16, kRowsDirect, 1>(p, n, k, group_r, w, packed, alpha, ws, s);
+      else launch_rows<BF16, kRowsGroup, 1>(p, n, k, group_r, w, packed, alpha, ws, s);
+      break;
+    case kRowsSums: launch_rows<BF16, kRowsSums, 1>(p, n, k, group_r, w, packed, alpha, ws, s); break;
+#define SHERRY_ROWS_E(M)                                                                        \
+  if (e <= 1) launch_rows<BF16, M, 1>(p, n, k, group_r, w, packed, alpha, ws, s);               \
+  else if (e <= 2) launch_rows<BF16, M, 2>(p, n, k, group_r, w, packed, alpha, ws, s);          \
+  else if (e <= 4) launch_rows<BF16, M, 4>(p, n, k, group_r, w, packed, alpha, ws, s);          \
+  else launch_rows<BF16, M, 8>(p, n, k, group_r, w, packed, alpha, ws, s);
+    case kRowsChannel: SHERRY_ROWS_E(kRowsChannel) break;
+    default: SHERRY_ROWS_E(kRowsTensor) break;
+#undef SHERRY_ROWS_E
+  }
+}
+
+}  // namespace
+
 hipError_t launch_quantize_pack(const QuantizePlan& p, int64_t n, int64_t k, int gran,
                                 int group_size, const void* w, bool w_bf16, uint8_t* packed,
                                 float* alpha, float* ws, hipStream_t s) {
   const int64_t nsb = k / kSuperblock;
+  if (p.rows) {
+    static_assert(kRowsMaxSb <= 64 * 8, "row trees hold at most 8 sums per lane");
+    const int group_r = gran == SHERRY_PER_GROUP ? group_size / kSuperblock : 1;
+    if (w_bf16) launch_rows_mode<true>(p, n, k, group_r, w, packed, alpha, ws, s);
+    else launch_rows_mode<false>(p, n, k, group_r, w, packed, alpha, ws, s);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || gran != SHERRY_PER_TENSOR) return e;
+    launch_tree_levels(p, ws, p.sb_sums, (double)n * (double)k / 4.0 * 3.0, alpha, ws, s);
+    return hipGetLastError();
+  }
   const dim3 grid = quantize_grid(n, nsb);
   float* direct = p.direct_alpha ? alpha : nullptr;
   if (w_bf16) {
@@ -545,21 +891,7 @@ hipError_t launch_quantize_pack(const QuantizePlan& p, int64_t n, int64_t k, int
     else hipLaunchKernelGGL(alpha_channel_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s,
                             ws, n, nsb, k, alpha);
   } else {
-    const double denom = (double)n * (double)k / 4.0 * 3.0;
-    const float* in = ws;
-    float* bufs[2] = {ws + p.sb_sums, ws + p.sb_sums + p.chunks / 2};
-    int64_t real = p.sb_sums;
-    for (int level = 0;; ++level) {
-      const int64_t chunks = (real + kTreeChunk - 1) / kTreeChunk;
-      if (chunks == 1) {
-        hipLaunchKernelGGL(tree_level_kernel, dim3(1), dim3(256), 0, s, in, real, alpha, denom);
-        break;
-      }
-      float* out = bufs[level & 1];
-      hipLaunchKernelGGL(tree_level_kernel, dim3((unsigned)chunks), dim3(256), 0, s, in, real, out, 0.0);
-      in = out;
-      real = chunks;
-    }
+    launch_tree_levels(p, ws, p.sb_sums, (double)n * (double)k / 4.0 * 3.0, alpha, ws, s);
   }
   return hipGetLastError();
 }

@@ -56,11 +56,18 @@ def test_size_queries(lib):
     assert lib.sherry_num_scales(8192, 8192, L.PER_CHANNEL, 128) == 8192
     assert lib.sherry_num_scales(8192, 8192, L.PER_TENSOR, 128) == 1
     assert lib.sherry_num_scales(8, 130, L.PER_GROUP, 128) == -1
-    # quantize workspace: none for G=128, N*K/128 sums otherwise (+ chunk partials per tensor)
+    # quantize workspace, rows of up to 512 superblocks: none for per_group and
+    # per_channel (the scales are finished in the pack kernel); per_tensor keeps
+    # one partial per 8-row group when K/128 is a power of two (else every
+    # superblock sum), plus two level buffers of ceil(partials / 4096)
     assert lib.sherry_workspace_bytes(L.OP_QUANTIZE_PACK, 64, 512, L.PER_GROUP, 128, 1, 1) == 0
-    assert lib.sherry_workspace_bytes(L.OP_QUANTIZE_PACK, 64, 512, L.PER_CHANNEL, 128, 1, 1) == 64 * 4 * 4
-    # per_tensor: 256 superblock sums + two level buffers of ceil(256/4096) partials
-    assert lib.sherry_workspace_bytes(L.OP_QUANTIZE_PACK, 64, 512, L.PER_TENSOR, 128, 1, 1) == (256 + 2) * 4
+    assert lib.sherry_workspace_bytes(L.OP_QUANTIZE_PACK, 64, 512, L.PER_GROUP, 256, 1, 1) == 0
+    assert lib.sherry_workspace_bytes(L.OP_QUANTIZE_PACK, 64, 512, L.PER_CHANNEL, 128, 1, 1) == 0
+    assert lib.sherry_workspace_bytes(L.OP_QUANTIZE_PACK, 64, 512, L.PER_TENSOR, 128, 1, 1) == (8 + 2) * 4
+    assert lib.sherry_workspace_bytes(L.OP_QUANTIZE_PACK, 64, 384, L.PER_TENSOR, 128, 1, 1) == (64 * 3 + 2) * 4
+    # longer rows: superblock sums, N*K/128 of them
+    assert lib.sherry_workspace_bytes(L.OP_QUANTIZE_PACK, 8, 128 * 600, L.PER_CHANNEL, 128, 1, 1) == 8 * 600 * 4
+    assert lib.sherry_workspace_bytes(L.OP_QUANTIZE_PACK, 8, 128 * 600, L.PER_GROUP, 128, 1, 1) == 0
     assert lib.sherry_workspace_bytes(L.OP_UNPACK, 64, 512, L.PER_TENSOR, 128, 1, 1) == 0
     assert lib.sherry_workspace_bytes(L.OP_GEMV, 64, 512, L.PER_GROUP, 128, 17, 1) == (1 << 64) - 1
     assert lib.sherry_workspace_bytes(9, 64, 512, L.PER_GROUP, 128, 1, 1) == (1 << 64) - 1
@@ -80,8 +87,9 @@ def qp(lib, n=64, k=512, gran=L.PER_GROUP, g=128, w=FAKE, wd=L.F32, packed=FAKE,
     (dict(wd=L.I8), L.ERR_DTYPE), (dict(wd=7), L.ERR_DTYPE),
     (dict(w=None), L.ERR_NULL), (dict(packed=None), L.ERR_NULL), (dict(alpha=None), L.ERR_NULL),
     (dict(w=MIS), L.ERR_ALIGN), (dict(packed=MIS), L.ERR_ALIGN), (dict(alpha=MIS), L.ERR_ALIGN),
-    (dict(gran=L.PER_TENSOR), L.ERR_WORKSPACE), (dict(gran=L.PER_CHANNEL, ws=FAKE, wsb=4), L.ERR_WORKSPACE),
-    (dict(g=256), L.ERR_WORKSPACE),
+    (dict(gran=L.PER_TENSOR), L.ERR_WORKSPACE), (dict(gran=L.PER_TENSOR, ws=FAKE, wsb=4), L.ERR_WORKSPACE),
+    (dict(k=128 * 600, gran=L.PER_CHANNEL, ws=FAKE, wsb=4), L.ERR_WORKSPACE),
+    (dict(k=128 * 600, g=256), L.ERR_WORKSPACE),
 ])
 def test_quantize_pack_rejects(lib, kw, code):
     assert qp(lib, **kw) == code
@@ -184,7 +192,7 @@ def test_fake_quant_workspace_sizes(lib):
     # per_group 128 is one fused kernel; the rest pack into the workspace first
     assert lib.sherry_workspace_bytes(L.OP_FAKE_QUANT, 64, 512, L.PER_GROUP, 128, 1, 1) == 0
     need = lib.sherry_workspace_bytes(L.OP_FAKE_QUANT, 64, 512, L.PER_CHANNEL, 128, 1, 1)
-    assert need >= 64 * 512 * 5 // 32 + 64 * 4 * 4
+    assert need >= 64 * 512 * 5 // 32  # the packed planes
     assert fq(lib, gran=L.PER_CHANNEL, ws=FAKE, wsb=need - 4) == L.ERR_WORKSPACE
 
 
@@ -288,8 +296,10 @@ def test_quantize_noalloc_rejects_before_any_launch(lib):
     assert f(64, 512, L.PER_GROUP, 128, FAKE, L.I8, FAKE2, FAKE, None) == L.ERR_DTYPE
     assert f(64, 512, L.PER_GROUP, 128, None, L.F32, FAKE2, FAKE, None) == L.ERR_NULL
     assert f(64, 512, L.PER_GROUP, 128, MIS, L.F32, FAKE2, FAKE, None) == L.ERR_ALIGN
-    # 8192 x 65536 per_tensor: 4 Mi superblock sums = 16 MiB of workspace
-    need = lib.sherry_workspace_bytes(L.OP_QUANTIZE_PACK, 8192, 65536, L.PER_TENSOR, 128, 1, 1)
+    # 8192 x 131072 (1024 superblocks a row): 8 Mi superblock sums = 32 MiB
+    need = lib.sherry_workspace_bytes(L.OP_QUANTIZE_PACK, 8192, 131072, L.PER_TENSOR, 128, 1, 1)
     assert need > L.QUANTIZE_SCRATCH_BYTES
-    assert f(8192, 65536, L.PER_TENSOR, 128, FAKE, L.BF16, FAKE2, FAKE, None) == L.ERR_WORKSPACE
-    assert f(8192, 65536, L.PER_CHANNEL, 128, FAKE, L.BF16, FAKE2, FAKE, None) == L.ERR_WORKSPACE
+    assert f(8192, 131072, L.PER_TENSOR, 128, FAKE, L.BF16, FAKE2, FAKE, None) == L.ERR_WORKSPACE
+    assert f(8192, 131072, L.PER_CHANNEL, 128, FAKE, L.BF16, FAKE2, FAKE, None) == L.ERR_WORKSPACE
+    # 8192 x 49152 per_tensor (384 superblocks, not a power of two): 12 MiB of sums
+    assert f(8192, 49152, L.PER_TENSOR, 128, FAKE, L.BF16, FAKE2, FAKE, None) == L.ERR_WORKSPACE

@@ -426,11 +426,26 @@ def test_quantize_per_channel_reduction_paths(n, nsb):
     check_quantize(dev_f32(w), w, "per_channel")
 
 
-@pytest.mark.parametrize("n,k", [(1000, 128 * 9), (4096, 128), (33, 128 * 131)])
+@pytest.mark.parametrize("n,k", [(1000, 128 * 9), (4096, 128), (33, 128 * 131), (70000, 128),
+                                 (40, 128 * 64)])
 def test_quantize_per_tensor_multi_level(n, k):
-    """More than 4096 superblock sums: the tree runs over two or three levels."""
+    """More than 4096 superblock sums (or, for power-of-two rows, more than
+    4096 16-row partials): the tree runs over two or three levels."""
     w = WL.latent_weight(n, k, 90 + n)
     check_quantize(dev_f32(w), w, "per_tensor")
+
+
+@pytest.mark.parametrize("gran,g", [("per_group", 128), ("per_group", 256), ("per_channel", 128),
+                                    ("per_tensor", 128)])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_quantize_rows_past_512_superblocks(gran, g, dtype):
+    """Rows longer than 512 superblocks take the superblock-tile kernel."""
+    w = WL.latent_weight(5, 128 * 600, 61)
+    if dtype == "bf16":
+        bits = WL.f32_to_bf16_bits(w)
+        check_quantize(dev_bf16(bits), WL.bf16_bits_to_f32(bits), gran, g)
+    else:
+        check_quantize(dev_f32(w), w, gran, g)
 
 
 # ------------------------------------------------------------------ fake quant

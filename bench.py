@@ -181,6 +181,22 @@ def ternary_structure_ok(pw):
     return ok
 
 
+def clock_ramp(launches, seconds=0.3):
+    """Run passes over ``launches`` for at least ``seconds`` of wall time, untimed.
+
+    The part lowers its clocks while idle and needs tens of milliseconds of
+    sustained load to return to its steady-state clocks; with a few warm-up
+    passes alone (say 5 of ~1.2 ms) the first timed passes ran ~7% slower
+    than the steady state.  This brings the device to that state before the
+    warm-up passes; it is not part of any timed region."""
+    torch = _torch()
+    t_end = time.perf_counter() + seconds
+    while time.perf_counter() < t_end:
+        for fn in launches:
+            fn()
+        torch.cuda.synchronize()
+
+
 def timed_launches(launches, steps, warmup, per_launch=True):
     """Run ``steps`` passes over ``launches`` (callables) after ``warmup``
     passes.  Returns (total ms from events around the whole region, per-launch
@@ -273,8 +289,10 @@ def bench_gemv_1b(args, dev):
         pws.append((name, n, k, pw, w))
 
     launches = [(lambda r=rep, xx=x: r.gemv(xx)) for (_, rep, x) in reps]
-    # the timed region: W warm-up steps, then exactly K steps with nothing
-    # but the launches between the bracketing events
+    # the timed region: clocks brought to their steady state, W warm-up
+    # steps, then exactly K steps with nothing but the launches between the
+    # bracketing events
+    clock_ramp(launches)
     total_ms, _, wall = timed_launches(launches, args.steps, args.warmup, per_launch=False)
     # then the same K steps again with an event pair around every launch, for
     # the per-kernel durations the roofline uses

@@ -135,8 +135,12 @@ size_t sherry_workspace_bytes(int32_t op, int64_t n, int64_t k, int32_t granular
  *   the kept |w| of the granule in flat index order (padded with +0 to a power
  *   of two), alpha = fp32(fp64(S) / fp64(L/4*3)).  Codes, bytes and scales
  *   are deterministic.
- *   workspace: sherry_workspace_bytes(SHERRY_OP_QUANTIZE_PACK, ...) bytes
- *   (0 for per_group with G == 128; otherwise N*K/128 fp32 partial sums).
+ *   workspace: sherry_workspace_bytes(SHERRY_OP_QUANTIZE_PACK, ...) bytes.
+ *   For K up to 65536 (512 superblocks) per_group and per_channel need none
+ *   and per_tensor needs ceil(N/8) fp32 partials when K/128 is a power of two
+ *   (else N*K/128); longer rows need N*K/128 fp32 superblock sums except
+ *   per_group with G == 128.  Per_tensor adds two level buffers of
+ *   ceil(partials / 4096) values.
  */
 int32_t sherry_quantize_pack(int64_t n, int64_t k, int32_t granularity, int32_t group_size,
                              const void* w, int32_t w_dtype, void* packed, float* alpha,
@@ -153,10 +157,11 @@ int32_t sherry_quantize_pack(int64_t n, int64_t k, int32_t granularity, int32_t 
  * allocated.
  *
  *   Limit: sherry_workspace_bytes(SHERRY_OP_QUANTIZE_PACK, ...) must not
- *   exceed SHERRY_QUANTIZE_SCRATCH_BYTES (N*K/128 fp32 superblock sums plus
- *   the per_tensor tree partials: up to about 2^28 weights), else
- *   SHERRY_ERR_WORKSPACE and nothing is launched.  per_group with G == 128
- *   needs no workspace and has no limit.
+ *   exceed SHERRY_QUANTIZE_SCRATCH_BYTES, else SHERRY_ERR_WORKSPACE and
+ *   nothing is launched.  Weights that need no workspace (per_group and
+ *   per_channel with K up to 65536, per_group G == 128 at any K) have no
+ *   limit; per_tensor with K/128 a power of two allows about 16 M rows;
+ *   the other cases keep N*K/128 fp32 sums: about 2^28 weights.
  *   The buffer belongs to the current device: `stream` must be a stream of
  *   the current device.  Every call on a device shares that device's buffer
  *   and leaves its contents behind (every value is written before it is read,

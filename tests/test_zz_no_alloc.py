@@ -1,8 +1,11 @@
 """The allocation-free quantize entry point (sherry_quantize_pack_noalloc),
 called through the C ABI, against sherry_quantize_pack: packed bytes and
 scales bit for bit, on two calls in a row (the second on a smaller weight, so
-it reuses the static workspace the first one filled), for the granularities
-that need a workspace and for per_group 128 (none)."""
+it reuses the static workspace the first one filled).  The cases that use the
+static workspace: per_tensor (one partial per 8 rows when K/128 is a power of
+two, else every superblock sum) and rows longer than 512 superblocks
+(superblock sums for per_channel and per_group G > 128); and cases that need
+none (per_group 128, per_channel and per_group 256 on shorter rows)."""
 
 import ctypes
 
@@ -45,10 +48,19 @@ def _same(pw, packed, alpha, what):
     assert torch.equal(pw.alpha.view(torch.int32), alpha.view(torch.int32)), f"{what}: scales differ"
 
 
-@pytest.mark.parametrize("gran,g", [("per_tensor", 128), ("per_channel", 128), ("per_group", 256),
-                                    ("per_group", 128)])
-def test_noalloc_matches_quantize_pack_two_calls(gran, g):
-    shapes = [(2048, 8192, 5100), (300, 1024, 5101)]   # second call smaller
+POW2 = [(2048, 8192, 5100), (300, 1024, 5101)]      # K/128 a power of two
+OTHER = [(1000, 3072, 5103), (300, 1152, 5104)]     # K/128 = 24, 9
+LONG = [(64, 128 * 600, 5105), (8, 128 * 520, 5106)]  # rows past 512 superblocks
+
+
+@pytest.mark.parametrize("gran,g,shapes", [
+    ("per_tensor", 128, POW2), ("per_tensor", 128, OTHER), ("per_channel", 128, LONG),
+    ("per_group", 256, LONG), ("per_channel", 128, POW2), ("per_group", 256, POW2),
+    ("per_group", 128, POW2), ("per_group", 128, LONG)],
+    ids=["tensor-pow2", "tensor-other", "channel-long", "group256-long", "channel-pow2", "group256-pow2",
+         "group128-pow2", "group128-long"])
+def test_noalloc_matches_quantize_pack_two_calls(gran, g, shapes):
+    # second call smaller
     for n, k, seed in shapes:
         bits, _ = WL.latent_weight_outliers_bf16(n, k, seed)
         w = torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to(DEV)

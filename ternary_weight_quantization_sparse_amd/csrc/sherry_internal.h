@@ -19,7 +19,7 @@ inline __host__ __device__ int64_t nibble_plane_bytes(int64_t n, int64_t k) { re
 
 // ---------------------------------------------------------------- quantize
 struct QuantizePlan {
-  bool rows;               // row-streaming kernel (K up to 512 superblocks)
+  bool rows;               // row-group kernel (K up to 512 superblocks)
   int rows_mode;           // its scale stage
   int64_t wg_rows;         // rows per workgroup of that kernel
   bool direct_alpha;       // superblock-tile kernel, per_group with G == 128: alpha written by the pack kernel

@@ -94,6 +94,14 @@ def test_quantize_group_not_power_of_two(gran, g):
     check_quantize(dev_f32(w), w, gran, g)
 
 
+@pytest.mark.parametrize("g", [256, 384, 512, 1536])
+def test_quantize_bf16_groups_of_several_superblocks(g):
+    """bf16 weights, groups of 2, 3, 4 and 12 superblocks (the group tree runs
+    over each group's superblock sums after the chunk walk), ragged rows."""
+    bits, vals = WL.latent_weight_outliers_bf16(37, 1536, 33)
+    check_quantize(dev_bf16(bits), vals, "per_group", g)
+
+
 @pytest.mark.parametrize("gran", ["per_group", "per_channel", "per_tensor"])
 def test_quantize_ties_zeros_signed_zero(gran):
     g = np.random.default_rng(12)

@@ -13,7 +13,7 @@ results table, which times the 1.67-bit "TL2" kernels):
 * about 1.67-bit: three weights in 5 bits (3^3 = 27 <= 32 states), groups of
   three that do not fall on power-of-two boundaries.
 
-The pages fix neither bit layout; the readings taken here (also in the design doc):
+The pages fix neither bit layout; the readings taken here:
 
 * 2-bit: weight value v in {0, +1, -1} is the code 0, 1, 2 (3 unused).  K runs
   in superblocks of 128 weights; the 32-byte record of (superblock g, row n)

@@ -19,7 +19,7 @@ Sources (the pages that define the method):
 * [P4] the ACL 2026 abstract page (paperdot): four weights per five bits.
 
 What the method computes, and where the pages leave a step open, the reading
-taken here (each reading is also listed in the design doc):
+taken here:
 
 1. Blocks are 4 consecutive weights along K (the last dim of the ``[out, in]``
    weight) [P1 1.1, the reshape to ``(rows, K/m, m)``; P2 format].

@@ -728,30 +728,36 @@ def bench_quantize(dev, reps=10):
         log(f"[quantize] {gran}: consistent={ok} repeatable={same} {t * 1e3:.1f} us, "
             f"{res[gran]['gbs']:.0f} GB/s")
     # quantization-aware-training forward: dense bf16 T*alpha from the same
-    # weight (per_group 128: the fused kernel)
-    # (equal, bit for bit, to quantize + pack followed by unpack to bf16)
-    out, a = S.fake_quant(w0, "per_group", 128)
-    pw = S.quantize_pack(w0, "per_group", 128)
-    ok = bool(torch.equal(out.view(torch.int16), S.unpack(pw, "bfloat16").view(torch.int16)) and
-              torch.equal(a, pw.alpha))
-    del pw
+    # weight (per_group 128: one fused kernel; per_channel / per_tensor:
+    # quantize + pack into the workspace, then unpack), each equal, bit for
+    # bit, to quantize + pack followed by unpack to bf16
     outs = [torch.empty_like(w0) for _ in range(2)]
-    alpha = torch.empty(S.num_scales(n, k, "per_group", 128), dtype=torch.float32, device=dev)
     lib = S.load()
+    for gran in ("per_group", "per_channel", "per_tensor"):
+        out, a = S.fake_quant(w0, gran, 128)
+        pw = S.quantize_pack(w0, gran, 128)
+        ok = bool(torch.equal(out.view(torch.int16), S.unpack(pw, "bfloat16").view(torch.int16)) and
+                  torch.equal(a, pw.alpha))
+        del pw, out, a
+        alpha = torch.empty(S.num_scales(n, k, gran, 128), dtype=torch.float32, device=dev)
+        wsb = S.workspace_bytes(4, n, k, gran, 128)
+        ws = torch.empty(max(wsb, 16), dtype=torch.uint8, device=dev)
+        g = S._lib.GRANULARITY[gran]
 
-    def fq(i=[0]):
-        w, o = copies[i[0] % 4], outs[i[0] % 2]
-        i[0] += 1
-        S.check(lib.sherry_fake_quant(n, k, S._lib.PER_GROUP, 128, w.data_ptr(), S._lib.BF16, o.data_ptr(),
-                                      S._lib.BF16, alpha.data_ptr(), None, 0,
-                                      torch.cuda.current_stream().cuda_stream))
-    total, per, _ = timed_launches([fq], reps, 2)
-    t = float(np.median(per[0]))
-    nbytes = n * k * 2 + n * k * 2 + 4 * alpha.numel()
-    res["fake_quant_per_group_bf16"] = {"equals_quantize_then_unpack": ok, "ms": t, "gbs": nbytes / (t * 1e-3) / 1e9,
-                                        "gweights_per_s": n * k / (t * 1e-3) / 1e9}
-    log(f"[fake-quant] per_group bf16->bf16: equals quantize+unpack={ok} {t * 1e3:.1f} us, "
-        f"{res['fake_quant_per_group_bf16']['gbs']:.0f} GB/s")
+        def fq(i=[0]):
+            w, o = copies[i[0] % 4], outs[i[0] % 2]
+            i[0] += 1
+            S.check(lib.sherry_fake_quant(n, k, g, 128, w.data_ptr(), S._lib.BF16, o.data_ptr(), S._lib.BF16,
+                                          alpha.data_ptr(), ws.data_ptr() if wsb else None, wsb,
+                                          torch.cuda.current_stream().cuda_stream))
+        total, per, _ = timed_launches([fq], reps, 2)
+        t = float(np.median(per[0]))
+        nbytes = n * k * 2 + n * k * 2 + 4 * alpha.numel()
+        key = f"fake_quant_{gran}_bf16"
+        res[key] = {"equals_quantize_then_unpack": ok, "ms": t, "gbs": nbytes / (t * 1e-3) / 1e9,
+                    "gweights_per_s": n * k / (t * 1e-3) / 1e9}
+        log(f"[fake-quant] {gran} bf16->bf16: equals quantize+unpack={ok} {t * 1e3:.1f} us, "
+            f"{res[key]['gbs']:.0f} GB/s")
     return res
 
 

@@ -544,6 +544,7 @@ constexpr int kRowsGroup = 0, kRowsChannel = 1, kRowsTensor = 2, kRowsSums = 3, 
 constexpr int64_t kRowsMaxSb = 512;  // 8 rows x 512 superblock sums in LDS = 16 KB
 constexpr int kRgRows = kRowsPerWave;  // rows per wave and per row group
 constexpr int kRgWaves = 4;            // waves per workgroup (at most)
+constexpr int64_t kDenseMaxSb = 128;   // fused fake quant: 8 rows x 128 superblocks of codes in LDS = 32 KB
 constexpr int kRor1 = 0x121, kRor2 = 0x122;
 
 // row_ror moves: every lane of the row has a source, so no bound control
@@ -602,14 +603,17 @@ __device__ inline float tree_inplace(float* x, int64_t r) {
   return x[0];
 }
 
-template <bool BF16, int MODE, int E>
+template <bool BF16, int MODE, int E, int DENSE = 0>
 // (eight waves per SIMD: the register budget is 64)
 __global__ __launch_bounds__(64 * kRgWaves) __attribute__((amdgpu_waves_per_eu(8)))
 void quantize_rowgroup_kernel(
     const void* __restrict__ w, int64_t n, int64_t k, int group_r, uint8_t* __restrict__ packed,
-    float* __restrict__ alpha, float* __restrict__ ws) {
+    float* __restrict__ alpha, float* __restrict__ ws, void* __restrict__ dense = nullptr) {
+  static_assert(DENSE == 0 || MODE == kRowsGroup || MODE == kRowsChannel, "dense output needs row-local scales");
   constexpr int RW = kRgRows;
-  extern __shared__ float sb_lds[];  // [RW][4 C] superblock kept-|w| sums (unless per_group 128)
+  // [RW][4 C] superblock kept-|w| sums (unless per_group 128); with DENSE
+  // then [RW][4 C][16] 16-bit block-pair entries (the codes) and the scales
+  extern __shared__ float sb_lds[];
   __shared__ uint16_t tab[128];      // per index: block 2i's entry, block 2i + 1's entry
   __shared__ float roots[RW];
   const int64_t nsb = k / kSuperblock;
@@ -631,7 +635,9 @@ void quantize_rowgroup_kernel(
   // v_perm selector putting the low byte of its second source at byte i / 4
   const uint32_t sel_nib = 0x0C0C0C0Cu & ~(0xFFu << (8 * (i >> 2)));
   uint32_t* nib_plane = reinterpret_cast<uint32_t*>(packed);
-  uint32_t* sgn_plane = reinterpret_cast<uint32_t*>(packed + nibble_plane_bytes(n, k));
+  uint32_t* sgn_plane = reinterpret_cast<uint32_t*>(packed + (DENSE ? 0 : nibble_plane_bytes(n, k)));
+  uint16_t* codes_lds = reinterpret_cast<uint16_t*>(sb_lds + RW * 4 * C);     // DENSE only
+  float* scale_lds = reinterpret_cast<float*>(codes_lds + RW * 4 * C * 16);  // DENSE only: [RW][groups]
 
   // one chunk of the 8 rows, from registers already loaded
   auto process = [&](const LaneRaw<BF16, 2>(&lw)[RW], int64_t c) {
@@ -652,7 +658,11 @@ void quantize_rowgroup_kernel(
       uint32_t nib = __builtin_amdgcn_perm(0u, comb, sel_nib);
       nib |= dpp_ror<kRor4>(nib);
       nib |= dpp_ror<kRor8>(nib);
-      if (gv && row < n && i < 4) nib_rec[it * 4] = nib;
+      if constexpr (DENSE != 0) {
+        codes_lds[(it * 4 * C + g) * 16 + i] = (uint16_t)comb;  // (g < 4 C always)
+      } else {
+        if (gv && row < n && i < 4) nib_rec[it * 4] = nib;
+      }
       // sign dword (every lane of the group): bit b = sign bit of block b
       uint32_t sg = ((comb >> 8) & 3u) << (2 * i);
       sg |= dpp_ror<kRor1>(sg);
@@ -677,7 +687,7 @@ void quantize_rowgroup_kernel(
     }
     const int rit = 15 - i;  // the row this lane now holds
     if (gv && rit < RW && row0 + rit < n) {
-      sgn_plane[rec0 + rit] = sgv;
+      if constexpr (DENSE == 0) sgn_plane[rec0 + rit] = sgv;
       if (direct) alpha[rec0 + rit] = (float)((double)sv / 96.0);
       else sb_lds[rit * 4 * C + g] = sv;
     }
@@ -708,9 +718,9 @@ void quantize_rowgroup_kernel(
       const double denom = (double)group_r * kSuperblock / 4.0 * 3.0;
       for (int64_t t = threadIdx.x; t < RW * groups; t += blockDim.x) {
         const int64_t rit = t / groups, gg = t % groups;
-        if (row0 + rit < n)
-          alpha[gg * n + row0 + rit] =
-              (float)((double)tree_inplace(sb_lds + rit * 4 * C + gg * group_r, group_r) / denom);
+        const float a = (float)((double)tree_inplace(sb_lds + rit * 4 * C + gg * group_r, group_r) / denom);
+        if (row0 + rit < n) alpha[gg * n + row0 + rit] = a;
+        if constexpr (DENSE != 0) scale_lds[rit * groups + gg] = a;
       }
     } else if constexpr (MODE == kRowsSums) {
       for (int64_t t = threadIdx.x; t < RW * nsb; t += blockDim.x) {
@@ -738,7 +748,10 @@ void quantize_rowgroup_kernel(
         sum += __shfl_xor(sum, 16);
         sum += __shfl_xor(sum, 32);
         if constexpr (MODE == kRowsChannel) {
-          if (lane == 0 && row0 + rit < n) alpha[row0 + rit] = (float)((double)sum / ((double)k / 4.0 * 3.0));
+          const float a = (float)((double)sum / ((double)k / 4.0 * 3.0));
+          if (lane == 0 && row0 + rit < n) alpha[row0 + rit] = a;
+          if constexpr (DENSE != 0)
+            if (lane == 0) scale_lds[rit] = a;
         } else {
           if (lane == 0) roots[rit] = sum;  // rows past n: +0
         }
@@ -746,6 +759,42 @@ void quantize_rowgroup_kernel(
       if constexpr (MODE == kRowsTensor) {
         __syncthreads();
         if (threadIdx.x == 0) ws[grp] = tree_inplace(roots, RW);
+      }
+    }
+  }
+  if constexpr (DENSE != 0) {
+    // Dense T * alpha (the fake-quant forward): per (row, chunk) a wave writes
+    // 4 superblocks, lane (s, i) the 8 weights of blocks 2i, 2i + 1 of
+    // superblock 4c + s from that pair's entry: each block's nibble (z << 2 |
+    // p1 << 1 | p0) and sign bit (its code is sign << 4 | nibble).
+    __syncthreads();  // every scale of the row group is in LDS
+    const int64_t groups = MODE == kRowsChannel ? 1 : nsb / group_r;
+    for (int64_t task = wave; task < RW * C; task += W) {
+      const int rit = (int)(task / C);
+      const int64_t c = task % C, g = 4 * c + s, row = row0 + rit;
+      if (row >= n || g >= nsb) continue;
+      const float a = scale_lds[rit * groups + (MODE == kRowsChannel ? 0 : g / group_r)];
+      const uint32_t comb = codes_lds[(rit * 4 * C + g) * 16 + i];
+      float f[8];
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const uint32_t code = (((comb >> (8 + j)) & 1u) << 4) | ((comb >> (4 * j)) & 15u);
+        int t[4];
+        decode_block(code, t);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) f[4 * j + e] = t[e] == 0 ? 0.f : (t[e] > 0 ? a : -a);
+      }
+      const int64_t off = row * k + g * kSuperblock + 8 * i;
+      if constexpr (DENSE == SHERRY_F32 + 1) {
+        float4* d = reinterpret_cast<float4*>(reinterpret_cast<float*>(dense) + off);
+        d[0] = make_float4(f[0], f[1], f[2], f[3]);
+        d[1] = make_float4(f[4], f[5], f[6], f[7]);
+      } else {
+        uint32_t hv[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          hv[e] = (uint32_t)f32_to_bf16_rne(f[2 * e]) | ((uint32_t)f32_to_bf16_rne(f[2 * e + 1]) << 16);
+        *reinterpret_cast<uint4*>(reinterpret_cast<uint16_t*>(dense) + off) = make_uint4(hv[0], hv[1], hv[2], hv[3]);
       }
     }
   }
@@ -900,15 +949,59 @@ FakeQuantPlan plan_fake_quant(int64_t n, int64_t k, int gran, int group_size) {
   FakeQuantPlan p{};
   p.fused = gran == SHERRY_PER_GROUP && group_size == kSuperblock;
   if (p.fused) return p;
+  // row-local scales over rows of up to kDenseMaxSb superblocks: the
+  // row-group kernel writes T * alpha itself once its rows' scales are known
+  p.fused_rows = gran != SHERRY_PER_TENSOR && k / kSuperblock <= kDenseMaxSb;
+  if (p.fused_rows) return p;
   p.packed_offset = 0;
   p.quant_ws_offset = ((size_t)(n * k / 32 * 5) + 255) / 256 * 256;
   p.workspace_bytes = p.quant_ws_offset + plan_quantize(n, k, gran, group_size).workspace_bytes;
   return p;
 }
 
+namespace {
+
+template <bool BF16, int MODE, int E, int DENSE>
+void launch_rows_dense(int64_t n, int64_t k, int group_r, const void* w, float* alpha, void* out, hipStream_t s) {
+  const int64_t nsb = k / kSuperblock;
+  const int64_t chunks = (nsb + 3) / 4;
+  const int waves = (int)(chunks < kRgWaves ? chunks : kRgWaves);
+  const int64_t groups = MODE == kRowsChannel ? 1 : nsb / group_r;
+  const size_t lds = (size_t)kRgRows * 4 * chunks * (sizeof(float) + 16 * sizeof(uint16_t)) +
+                     (size_t)kRgRows * groups * sizeof(float);
+  const dim3 grid((unsigned)((n + kRgRows - 1) / kRgRows));
+  hipLaunchKernelGGL((quantize_rowgroup_kernel<BF16, MODE, E, DENSE>), grid, dim3(64 * waves), lds, s, w, n, k,
+                     group_r, nullptr, alpha, nullptr, out);
+}
+
+template <bool BF16, int DENSE>
+void launch_rows_dense_mode(int64_t n, int64_t k, int gran, int group_size, const void* w, float* alpha, void* out,
+                            hipStream_t s) {
+  if (gran == SHERRY_PER_GROUP) {
+    launch_rows_dense<BF16, kRowsGroup, 1, DENSE>(n, k, group_size / kSuperblock, w, alpha, out, s);
+    return;
+  }
+  const int64_t e = (k / kSuperblock + 63) / 64;  // sums per lane in the row tree
+  if (e <= 1) launch_rows_dense<BF16, kRowsChannel, 1, DENSE>(n, k, 1, w, alpha, out, s);
+  else launch_rows_dense<BF16, kRowsChannel, 2, DENSE>(n, k, 1, w, alpha, out, s);
+}
+
+}  // namespace
+
 hipError_t launch_fake_quant(const FakeQuantPlan& p, int64_t n, int64_t k, int gran, int group_size,
                              const void* w, bool w_bf16, void* out, int out_dtype, float* alpha,
                              uint8_t* ws, hipStream_t s) {
+  if (p.fused_rows) {
+    static_assert(kDenseMaxSb <= 128, "row trees of at most 2 sums per lane");
+    if (w_bf16) {
+      if (out_dtype == SHERRY_F32) launch_rows_dense_mode<true, SHERRY_F32 + 1>(n, k, gran, group_size, w, alpha, out, s);
+      else launch_rows_dense_mode<true, SHERRY_BF16 + 1>(n, k, gran, group_size, w, alpha, out, s);
+    } else {
+      if (out_dtype == SHERRY_F32) launch_rows_dense_mode<false, SHERRY_F32 + 1>(n, k, gran, group_size, w, alpha, out, s);
+      else launch_rows_dense_mode<false, SHERRY_BF16 + 1>(n, k, gran, group_size, w, alpha, out, s);
+    }
+    return hipGetLastError();
+  }
   if (p.fused) {
     const int64_t nsb = k / kSuperblock;
     const dim3 grid = quantize_grid(n, nsb);

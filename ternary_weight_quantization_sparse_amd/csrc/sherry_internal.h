@@ -40,6 +40,7 @@ hipError_t quantize_scratch(float** ptr);
 // ---------------------------------------------------------------- fake quant
 struct FakeQuantPlan {
   bool fused;              // per_group G = 128: one kernel writes T*alpha and the scales
+  bool fused_rows;         // per_channel / per_group G > 128, K <= 16384: the row-group kernel writes them
   size_t packed_offset;    // otherwise: packed planes, then the quantize workspace
   size_t quant_ws_offset;
   size_t workspace_bytes;

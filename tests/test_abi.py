@@ -182,18 +182,26 @@ def fq(lib, n=64, k=512, gran=L.PER_GROUP, g=128, w=FAKE, wdt=L.F32, out=FAKE2, 
     (dict(wdt=L.I8), L.ERR_DTYPE), (dict(odt=L.I8), L.ERR_DTYPE), (dict(odt=7), L.ERR_DTYPE),
     (dict(w=None), L.ERR_NULL), (dict(out=None), L.ERR_NULL), (dict(alpha=None), L.ERR_NULL),
     (dict(out=MIS), L.ERR_ALIGN), (dict(k=516, gran=L.PER_TENSOR), L.ERR_UNSUPPORTED),
-    (dict(gran=L.PER_CHANNEL), L.ERR_WORKSPACE), (dict(g=256), L.ERR_WORKSPACE),
+    (dict(gran=L.PER_TENSOR), L.ERR_WORKSPACE), (dict(k=128 * 200, gran=L.PER_CHANNEL), L.ERR_WORKSPACE),
+    (dict(k=128 * 200, g=256), L.ERR_WORKSPACE),
 ])
 def test_fake_quant_rejects(lib, kw, code):
     assert fq(lib, **kw) == code
 
 
 def test_fake_quant_workspace_sizes(lib):
-    # per_group 128 is one fused kernel; the rest pack into the workspace first
-    assert lib.sherry_workspace_bytes(L.OP_FAKE_QUANT, 64, 512, L.PER_GROUP, 128, 1, 1) == 0
-    need = lib.sherry_workspace_bytes(L.OP_FAKE_QUANT, 64, 512, L.PER_CHANNEL, 128, 1, 1)
-    assert need >= 64 * 512 * 5 // 32  # the packed planes
-    assert fq(lib, gran=L.PER_CHANNEL, ws=FAKE, wsb=need - 4) == L.ERR_WORKSPACE
+    # one kernel, no workspace: per_group 128 at any K; per_channel and
+    # per_group G > 128 with K up to 16384 (128 superblocks).  The rest pack
+    # into the workspace first, then unpack.
+    for gran, g in ((L.PER_GROUP, 128), (L.PER_CHANNEL, 128), (L.PER_GROUP, 256)):
+        assert lib.sherry_workspace_bytes(L.OP_FAKE_QUANT, 64, 512, gran, g, 1, 1) == 0
+        assert lib.sherry_workspace_bytes(L.OP_FAKE_QUANT, 64, 16384, gran, g, 1, 1) == 0
+    assert lib.sherry_workspace_bytes(L.OP_FAKE_QUANT, 64, 128 * 200, L.PER_GROUP, 128, 1, 1) == 0
+    for gran, k in ((L.PER_TENSOR, 512), (L.PER_CHANNEL, 128 * 129), (L.PER_GROUP, 128 * 200)):
+        need = lib.sherry_workspace_bytes(L.OP_FAKE_QUANT, 64, k, gran, 128 if gran != L.PER_GROUP else 256, 1, 1)
+        assert need >= 64 * k * 5 // 32  # the packed planes
+    need = lib.sherry_workspace_bytes(L.OP_FAKE_QUANT, 64, 512, L.PER_TENSOR, 128, 1, 1)
+    assert fq(lib, gran=L.PER_TENSOR, ws=FAKE, wsb=need - 4) == L.ERR_WORKSPACE
 
 
 def ar(lib, n=64, k=512, gran=L.PER_GROUP, g=128, packed=FAKE, alpha=FAKE2, w=FAKE, lam=0.5, x=FAKE2, m=32,

@@ -457,17 +457,26 @@ def test_quantize_rows_past_512_superblocks(gran, g, dtype):
 
 
 # ------------------------------------------------------------------ fake quant
-@pytest.mark.parametrize("n,k", [(256, 512), (130, 384), (1, 128)])
-@pytest.mark.parametrize("gran,g", [("per_group", 128), ("per_group", 256), ("per_channel", 128),
-                                    ("per_tensor", 128)])
+@pytest.mark.parametrize("n,k", [(256, 512), (130, 384), (1, 128), (19, 1536), (9, 128 * 130)])
+@pytest.mark.parametrize("gran,g", [("per_group", 128), ("per_group", 256), ("per_group", 384),
+                                    ("per_channel", 128), ("per_tensor", 128)])
 @pytest.mark.parametrize("odt", ["float32", "bfloat16"])
-def test_fake_quant_matches_oracle(n, k, gran, g, odt):
+@pytest.mark.parametrize("wdt", ["f32", "bf16"])
+def test_fake_quant_matches_oracle(n, k, gran, g, odt, wdt):
     """Dense T * alpha and the scales, bit for bit: fp32 exactly, bf16 as the
-    nearest-even rounding of the fp32 product."""
+    nearest-even rounding of the fp32 product.  Covers the three kernels:
+    per_group 128 fused, per_channel / per_group G > 128 fused in the
+    row-group kernel (K up to 128 superblocks), and quantize + unpack (per
+    tensor; rows of 130 superblocks)."""
     if k % g:
         pytest.skip("group does not divide K")
     w = WL.latent_weight(n, k, 40 + n)
-    out, a = S.fake_quant(dev_f32(w), gran, g, out_dtype=getattr(torch, odt))
+    if wdt == "bf16":
+        bits = WL.f32_to_bf16_bits(w)
+        w, wd = WL.bf16_bits_to_f32(bits), dev_bf16(bits)
+    else:
+        wd = dev_f32(w)
+    out, a = S.fake_quant(wd, gran, g, out_dtype=getattr(torch, odt))
     ref, ref_a = O.fake_quant(w, gran, g)
     assert np.array_equal(to_np(a).view(np.uint32), ref_a.reshape(-1).view(np.uint32))
     ref32 = ref.astype(np.float32)
@@ -477,13 +486,15 @@ def test_fake_quant_matches_oracle(n, k, gran, g, odt):
         assert np.array_equal(to_np(out), O.round_to_bf16_bits(ref32))
 
 
-def test_fake_quant_bf16_outliers_8192():
-    """The 8192x8192 bf16 weight with 1% outliers x10, per_group 128 (the
-    fused kernel), bf16 out; ties at the block minimum occur here."""
+@pytest.mark.parametrize("gran", ["per_group", "per_channel"])
+def test_fake_quant_bf16_outliers_8192(gran):
+    """The 8192x8192 bf16 weight with 1% outliers x10, bf16 out (per_group
+    128: the fused quantize kernel; per_channel: the row-group kernel's dense
+    phase); ties at the block minimum occur here."""
     wb, wv = WL.latent_weight_outliers_bf16(8192, 8192, 5000)
-    print("[fake-quant] 8192x8192 bf16 outliers", flush=True)
-    out, a = S.fake_quant(dev_bf16(wb), "per_group", 128)
-    ref, ref_a = O.fake_quant(wv, "per_group", 128)
+    print(f"[fake-quant] 8192x8192 bf16 outliers {gran}", flush=True)
+    out, a = S.fake_quant(dev_bf16(wb), gran, 128)
+    ref, ref_a = O.fake_quant(wv, gran, 128)
     assert np.array_equal(to_np(a).view(np.uint32), ref_a.reshape(-1).view(np.uint32))
     assert np.array_equal(to_np(out), O.round_to_bf16_bits(ref.astype(np.float32)))
 

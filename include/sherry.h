@@ -245,9 +245,10 @@ int32_t sherry_gemm(int64_t n, int64_t k, int32_t granularity, int32_t group_siz
  *            sherry_quantize_pack writes.
  *   Codes and scales are those of sherry_quantize_pack, bit for bit.
  *   workspace: sherry_workspace_bytes(SHERRY_OP_FAKE_QUANT, ...) bytes: 0 for
- *            per_group with G == 128 (one fused kernel); otherwise room for
- *            the packed planes plus the quantize workspace (quantize + pack,
- *            then a dense decode).
+ *            per_group with G == 128 and, for K up to 16384, per_channel and
+ *            per_group G > 128 (one kernel each); otherwise (per_tensor,
+ *            longer rows) room for the packed planes plus the quantize
+ *            workspace (quantize + pack, then a dense decode).
  */
 int32_t sherry_fake_quant(int64_t n, int64_t k, int32_t granularity, int32_t group_size,
                           const void* w, int32_t w_dtype, void* out, int32_t out_dtype, float* alpha,

@@ -603,8 +603,12 @@ __device__ inline float tree_inplace(float* x, int64_t r) {
   return x[0];
 }
 
+// DENSE (per_channel and per_group G > 128, rows of up to kDenseMaxSb
+// superblocks): the fused fake-quant forward -- no planes; the codes stay in
+// LDS and a last phase writes T * alpha densely (fp32, or bf16 rounded to
+// nearest even) once the scales are known.  Eight waves per SIMD: the
+// register budget is 64.
 template <bool BF16, int MODE, int E, int DENSE = 0>
-// (eight waves per SIMD: the register budget is 64)
 __global__ __launch_bounds__(64 * kRgWaves) __attribute__((amdgpu_waves_per_eu(8)))
 void quantize_rowgroup_kernel(
     const void* __restrict__ w, int64_t n, int64_t k, int group_r, uint8_t* __restrict__ packed,
@@ -644,7 +648,7 @@ void quantize_rowgroup_kernel(
     const int64_t g = 4 * c + s;  // this lane's superblock
     const bool gv = g < nsb;
     const int64_t rec0 = g * n + row0;  // record of (g, row0); rows follow
-    uint32_t* nib_rec = nib_plane + rec0 * 4 + i;
+    uint32_t* nib_rec = DENSE ? nullptr : nib_plane + rec0 * 4 + i;
     float sv = 0.f;
     uint32_t sgv = 0;
 #pragma unroll

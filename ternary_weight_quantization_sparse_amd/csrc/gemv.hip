@@ -722,6 +722,7 @@ hipError_t launch_lut(const GemvPlan& p, dim3 grid, hipStream_t s, const uint8_t
   const int cfg = p.rw * 100 + p.kw;
   if (cfg == 401 && p.rows_per_thread == 4) SHERRY_LUT_WIN(4, 4, 1);
   else if (cfg == 401) SHERRY_LUT_WIN(1, 4, 1);
+  else if (cfg == 801) SHERRY_LUT_WIN(1, 8, 1);
   else if (cfg == 402) SHERRY_LUT_WIN(1, 4, 2);
   else if (cfg == 404) SHERRY_LUT_WIN(1, 4, 4);
   else if (cfg == 208) {
@@ -809,10 +810,18 @@ GemvPlan plan_gemv(int64_t n, int64_t k, int gran, int group_size, int batch, in
     // workgroups then need no barrier coupling between slices).
     p.kind = 0;
     p.rw = 4;
+    // Launches with workgroups to spare take 512-row panels (fewer, longer
+    // lived workgroups, each table build shared by twice the rows) when the
+    // last panel wastes at most an eighth of its rows and the launch still
+    // has >= 2048 workgroups: +1-2% per shape on the 1B headline launches.
+    {
+      const int64_t panels8 = (n + 511) / 512;
+      if (panels8 * 512 * 8 <= n * 9 && panels8 * count >= 2048) p.rw = 8;
+    }
     p.kw = 1;
     const int64_t wg256 = (n + kLutThreads - 1) / kLutThreads * count;
     p.rows_per_thread = wg256 >= 4096 ? SHERRY_LUT_ROWS : 1;
-    p.panels = (n + 256 * p.rows_per_thread - 1) / (256 * p.rows_per_thread);
+    p.panels = (n + 64 * p.rw * p.rows_per_thread - 1) / (64 * p.rw * p.rows_per_thread);
     int64_t split = 1;
     while (p.panels * count * split * 2 <= SHERRY_GEMV_SPLIT_TARGET && groups % (split * 2) == 0) split *= 2;
     if (split > 1) {

@@ -692,6 +692,13 @@ def _unpack_i8(pw):
     return S.unpack(pw, "int8")
 
 
+def back_to_back_ms(fn, reps, warmup=10):
+    """ms per call of ``reps`` calls issued back to back (events around the
+    region only), after ``warmup`` calls: the throughput rate."""
+    total, _, _ = timed_launches([fn], reps, warmup, per_launch=False)
+    return total / reps
+
+
 def bench_quantize(dev, reps=10):
     import numpy as np
     import workloads as WL
@@ -718,15 +725,17 @@ def bench_quantize(dev, reps=10):
             S.check(lib.sherry_quantize_pack(n, k, g, 128, w.data_ptr(), S._lib.BF16, packed.data_ptr(),
                                              alpha.data_ptr(), ws.data_ptr(), ws.numel(),
                                              torch.cuda.current_stream().cuda_stream))
-        total, per, _ = timed_launches([launch], reps, 2)
-        t = float(np.median(per[0]))
+        _, per, _ = timed_launches([launch], reps, 2)
+        t1 = float(np.median(per[0]))
+        t = back_to_back_ms(launch, 10 * reps)
         # the timed launches rewrote packed / alpha from identical copies
         same = bool(torch.equal(packed, pw.packed) and torch.equal(alpha, pw.alpha))
         rd, wr = n * k * 2, S.packed_bytes(n, k) + 4 * alpha.numel()
         res[gran] = {"consistent": ok, "repeatable": same, "ms": t, "gbs": (rd + wr) / (t * 1e-3) / 1e9,
-                     "gweights_per_s": n * k / (t * 1e-3) / 1e9}
-        log(f"[quantize] {gran}: consistent={ok} repeatable={same} {t * 1e3:.1f} us, "
-            f"{res[gran]['gbs']:.0f} GB/s")
+                     "gweights_per_s": n * k / (t * 1e-3) / 1e9, "ms_single_call": t1,
+                     "gbs_single_call": (rd + wr) / (t1 * 1e-3) / 1e9}
+        log(f"[quantize] {gran}: consistent={ok} repeatable={same} {t * 1e3:.1f} us back to back, "
+            f"{res[gran]['gbs']:.0f} GB/s (single call {t1 * 1e3:.1f} us)")
     # quantization-aware-training forward: dense bf16 T*alpha from the same
     # weight (per_group 128: one fused kernel; per_channel / per_tensor:
     # quantize + pack into the workspace, then unpack), each equal, bit for
@@ -750,14 +759,16 @@ def bench_quantize(dev, reps=10):
             S.check(lib.sherry_fake_quant(n, k, g, 128, w.data_ptr(), S._lib.BF16, o.data_ptr(), S._lib.BF16,
                                           alpha.data_ptr(), ws.data_ptr() if wsb else None, wsb,
                                           torch.cuda.current_stream().cuda_stream))
-        total, per, _ = timed_launches([fq], reps, 2)
-        t = float(np.median(per[0]))
+        _, per, _ = timed_launches([fq], reps, 2)
+        t1 = float(np.median(per[0]))
+        t = back_to_back_ms(fq, 10 * reps)
         nbytes = n * k * 2 + n * k * 2 + 4 * alpha.numel()
         key = f"fake_quant_{gran}_bf16"
         res[key] = {"equals_quantize_then_unpack": ok, "ms": t, "gbs": nbytes / (t * 1e-3) / 1e9,
-                    "gweights_per_s": n * k / (t * 1e-3) / 1e9}
-        log(f"[fake-quant] {gran} bf16->bf16: equals quantize+unpack={ok} {t * 1e3:.1f} us, "
-            f"{res[key]['gbs']:.0f} GB/s")
+                    "gweights_per_s": n * k / (t * 1e-3) / 1e9, "ms_single_call": t1,
+                    "gbs_single_call": nbytes / (t1 * 1e-3) / 1e9}
+        log(f"[fake-quant] {gran} bf16->bf16: equals quantize+unpack={ok} {t * 1e3:.1f} us back to back, "
+            f"{res[key]['gbs']:.0f} GB/s (single call {t1 * 1e3:.1f} us)")
     return res
 
 
@@ -802,12 +813,15 @@ def bench_unpack(dev, reps=20):
                                       o.data_ptr(), od, torch.cuda.current_stream().cuda_stream))
         timed_launches([launch], reps, reps)
         _, per, _ = timed_launches([launch], reps, 2)
-        t = float(np.median(per[0]))
+        t1 = float(np.median(per[0]))
+        t = back_to_back_ms(launch, 5 * reps)
         nbytes = S.packed_bytes(n, k) + (0 if name == "int8" else 4 * pw.alpha.numel()) + n * k * esize
         res[name] = {"consistent": ok, "ms": t, "gbs": nbytes / (t * 1e-3) / 1e9,
                      "frac_of_hbm_peak": nbytes / (t * 1e-3) / 1e9 / HBM_PEAK_GBS, "bytes": nbytes,
-                     "output_buffers": len(outs)}
-        log(f"[unpack] 8192x8192 -> {name}: consistent={ok} {t * 1e3:.1f} us, {res[name]['gbs']:.0f} GB/s")
+                     "output_buffers": len(outs), "ms_single_call": t1,
+                     "gbs_single_call": nbytes / (t1 * 1e-3) / 1e9}
+        log(f"[unpack] 8192x8192 -> {name}: consistent={ok} {t * 1e3:.1f} us back to back, "
+            f"{res[name]['gbs']:.0f} GB/s (single call {t1 * 1e3:.1f} us)")
         del outs, ins
     # reference write rate at the int8 output's size: torch's fill of 64 MiB
     # buffers, rotating over 1 GiB
@@ -817,8 +831,7 @@ def bench_unpack(dev, reps=20):
         bufs[i[0] % len(bufs)].fill_(1)
         i[0] += 1
     timed_launches([fill], reps, reps)
-    _, per, _ = timed_launches([fill], reps, 2)
-    t = float(np.median(per[0]))
+    t = back_to_back_ms(fill, 5 * reps)
     res["torch_fill_64mib"] = {"ms": t, "gbs": (64 << 20) / (t * 1e-3) / 1e9}
     log(f"[unpack] reference: torch fill of 64 MiB {t * 1e3:.1f} us, {res['torch_fill_64mib']['gbs']:.0f} GB/s")
     return res

@@ -523,7 +523,7 @@ __global__ __launch_bounds__(256) void tree_level_kernel(const float* __restrict
 // (four waves, 8 rows each) -- consecutive workgroups read adjacent spans of
 // the same rows -- and each superblock sum over 96 is stored at once.  Every
 // other scale needs a row's sums from all chunks, so there a workgroup of
-// min(4, chunks) waves owns one row group and walks its chunks, the sums wait
+// min(8, chunks) waves owns one row group and walks its chunks, the sums wait
 // in LDS, and after a barrier:
 //   kRowsGroup    per_group G = 128 r: the pairwise tree over each group's r
 //                 sums, over 96 r;
@@ -536,14 +536,20 @@ __global__ __launch_bounds__(256) void tree_level_kernel(const float* __restrict
 //                 the tree levels that follow;
 //   kRowsSums     per_tensor otherwise: the superblock sums, row-major, for
 //                 the tree levels.
-// Measured on the 8192 x 8192 bf16 weight against the superblock-tile kernel
-// and its second-stage launches: per_channel 33.0 vs 33.6 us, per_tensor
-// 35.4 vs 37.0 us, per_group 128 30.0 vs 29.6 us, with 21% fewer VALU
-// instructions -- the time is set by the memory pipeline, not the ALU.
+// Measured on the 8192 x 8192 bf16 weight, 100 calls back to back:
+// per_group 128 29.4 us, per_channel 30.2 us, per_tensor 33.6 us (with the
+// tree launch).  Against the superblock-tile kernel and its second-stage
+// launches the row-group kernel needs 18% fewer VALU instructions per weight
+// (integer-domain selection) at about the same time: the memory pipeline, not
+// the ALU, sets it.
 constexpr int kRowsGroup = 0, kRowsChannel = 1, kRowsTensor = 2, kRowsSums = 3, kRowsDirect = 4;
 constexpr int64_t kRowsMaxSb = 512;  // 8 rows x 512 superblock sums in LDS = 16 KB
 constexpr int kRgRows = kRowsPerWave;  // rows per wave and per row group
-constexpr int kRgWaves = 4;            // waves per workgroup (at most)
+constexpr int kRgWaves = 4;            // waves per workgroup, per_group 128 (one chunk per wave)
+// waves per workgroup (at most) of the modes that walk a row group's chunks:
+// 8 waves per SIMD in one round for 8192-wide rows; 1-2.5% faster than 4 for
+// per_channel / per_tensor and 10% for the fused fake quant, 16 slower
+constexpr int kRgWavesWalk = 8;
 constexpr int64_t kDenseMaxSb = 128;   // fused fake quant: 8 rows x 128 superblocks of codes in LDS = 32 KB
 constexpr int kRor1 = 0x121, kRor2 = 0x122;
 
@@ -570,27 +576,96 @@ __device__ inline uint32_t positive_bytes_bf16(uint32_t d0, uint32_t d1) {
   return __builtin_amdgcn_perm(t1, t0, 0x0B0A0908u);
 }
 
-// Table index of block j (0, 1) of a lane: 4 * pos + z, pos = the positive
-// flags of weights 0..3 in bits 0..3; kept = the block's kept-|w| sum.
+// Table index h of block j (0, 1) of a lane, returned as the byte offset 2h
+// of its 16-bit entry; kept = the block's kept-|w| sum, the tree
+// ((k0 + k1) + (k2 + k3)) with the zero position's term +0.
+//
+// bf16: h = 8 * pos + (c01 | c23 << 1 | c << 2), pos = the positive flags of
+// weights 0..3 in bits 0..3, c01 = |w1| < |w0|, c23 = |w3| < |w2|, c = the
+// smaller of the right pair is below the smaller of the left pair (so the
+// zero is 2 + c23 if c, else c01: the smallest |w|, lowest index on ties).
+// The magnitudes are compared as 15-bit integers, which order like the
+// values they encode; the pairs (w0, w2) and (w1, w3) share a packed 16-bit
+// operation.  A pair's kept sum is its larger magnitude plus its smaller one
+// where the zero is in the other pair, +0 where it is not: the same fp32
+// additions the tree makes, operands commuted.
+// fp32: h = 4 * pos + z.
+typedef short i16x2 __attribute__((ext_vector_type(2)));
+typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+__device__ inline i16x2 as_i16x2(uint32_t v) { return __builtin_bit_cast(i16x2, v); }
+__device__ inline u16x2 as_u16x2(uint32_t v) { return __builtin_bit_cast(u16x2, v); }
+
 template <bool BF16>
 __device__ inline uint32_t lane_block(const LaneRaw<BF16, 2>& r, int j, float& kept) {
-  float v[4];
   if constexpr (BF16) {
     const uint32_t d0 = j ? r.q[0].z : r.q[0].x, d1 = j ? r.q[0].w : r.q[0].y;
-    v[0] = __uint_as_float(d0 << 16);
-    v[1] = __uint_as_float(d0 & 0xFFFF0000u);
-    v[2] = __uint_as_float(d1 << 16);
-    v[3] = __uint_as_float(d1 & 0xFFFF0000u);
-    const uint32_t z = block_zero(v, kept);
-    // bytes of -1 (0xFF) where positive, times -4, -8, -16, -32, plus z
-    return (uint32_t)__builtin_amdgcn_sdot4((int)positive_bytes_bf16(d0, d1), (int)0xE0F0F8FCu, (int)z, false);
+    const uint32_t a = __builtin_amdgcn_perm(d1, d0, 0x05040100u) & 0x7FFF7FFFu;  // |w0|, |w2|
+    const uint32_t b = __builtin_amdgcn_perm(d1, d0, 0x07060302u) & 0x7FFF7FFFu;  // |w1|, |w3|
+    const uint32_t t1 = __builtin_bit_cast(uint32_t, as_i16x2(b) - as_i16x2(a));  // signs: c01, c23
+    const uint32_t mn = __builtin_bit_cast(uint32_t, __builtin_elementwise_min(as_u16x2(a), as_u16x2(b)));
+    const uint32_t mx = __builtin_bit_cast(uint32_t, __builtin_elementwise_max(as_u16x2(a), as_u16x2(b)));
+    const uint32_t sw = __builtin_amdgcn_alignbit(mn, mn, 16);                    // halves swapped
+    const uint32_t t2 = __builtin_bit_cast(uint32_t, as_i16x2(sw) - as_i16x2(mn)); // sign of the low half: c
+    // kept smaller magnitudes: the left pair's if c, else the right pair's
+    const uint32_t all_c = __builtin_amdgcn_perm(t2, t2, 0x08080808u);            // c ? ~0 : 0
+    const uint32_t ms = __builtin_amdgcn_bitop3_b32(mn, all_c, 0xFFFF0000u, 0x60); // mn & (all_c ^ K)
+    const float left = __uint_as_float(mx << 16) + __uint_as_float(ms << 16);
+    const float right = __uint_as_float(mx & 0xFFFF0000u) + __uint_as_float(ms & 0xFFFF0000u);
+    kept = left + right;
+    // bytes of -1 where set: positive flags times -16 .. -128, c01 / c23 / c times -2, -4, -8
+    const uint32_t cbytes = __builtin_amdgcn_perm(t2, t1, 0x0C0A0908u);
+    const int ip = __builtin_amdgcn_sdot4((int)positive_bytes_bf16(d0, d1), (int)0x80C0E0F0u, 0, false);
+    return (uint32_t)__builtin_amdgcn_sdot4((int)cbytes, (int)0x00F8FCFEu, ip, false);
   } else {
+    float v[4];
     const uint4 u = r.q[j];
     v[0] = __uint_as_float(u.x); v[1] = __uint_as_float(u.y);
     v[2] = __uint_as_float(u.z); v[3] = __uint_as_float(u.w);
     const uint32_t z = block_zero(v, kept);
-    return z | (v[0] > 0.f ? 4u : 0u) | (v[1] > 0.f ? 8u : 0u) | (v[2] > 0.f ? 16u : 0u) | (v[3] > 0.f ? 32u : 0u);
+    return 2u * z | (v[0] > 0.f ? 8u : 0u) | (v[1] > 0.f ? 16u : 0u) | (v[2] > 0.f ? 32u : 0u) |
+           (v[3] > 0.f ? 64u : 0u);
   }
+}
+// The block code of a table index h of lane_block.
+template <bool BF16>
+__device__ inline uint32_t lane_index_code(uint32_t idx) {
+  if constexpr (BF16) {
+    const uint32_t z = (idx & 4u) ? 2u + ((idx >> 1) & 1u) : (idx & 1u);
+    return block_code(z, idx >> 3);
+  } else {
+    return block_code(idx & 3u, idx >> 2);
+  }
+}
+template <bool BF16>
+constexpr int kLaneIndices = BF16 ? 128 : 64;
+
+// p, known to be the same in every lane, as a scalar global-memory address.
+typedef __attribute__((address_space(1))) const char gchar;
+__device__ inline gchar* uniform_ptr(const char* p) {
+  const uint64_t u = reinterpret_cast<uint64_t>(p);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)u);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(u >> 32));
+  return reinterpret_cast<gchar*>(((uint64_t)hi << 32) | lo);
+}
+// The two blocks of a bf16 lane at row address p (scalar) + off.
+__device__ inline LaneRaw<true, 2> load_lane_at(gchar* p, uint32_t off) {
+  typedef unsigned int v4u __attribute__((ext_vector_type(4)));
+  typedef __attribute__((address_space(1))) const v4u gv4u;
+  const v4u t = __builtin_nontemporal_load(reinterpret_cast<gv4u*>(p + off));
+  LaneRaw<true, 2> r;
+  r.q[0] = make_uint4(t.x, t.y, t.z, t.w);
+  return r;
+}
+__device__ inline LaneRaw<false, 2> load_lane_at_f32(gchar* p, uint32_t off) {
+  typedef unsigned int v4u __attribute__((ext_vector_type(4)));
+  typedef __attribute__((address_space(1))) const v4u gv4u;
+  LaneRaw<false, 2> r;
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const v4u t = __builtin_nontemporal_load(reinterpret_cast<gv4u*>(p + off) + h);
+    r.q[h] = make_uint4(t.x, t.y, t.z, t.w);
+  }
+  return r;
 }
 
 // In-place pairwise tree over x[0 .. r) padded with +0 to a power of two
@@ -608,8 +683,8 @@ __device__ inline float tree_inplace(float* x, int64_t r) {
 // LDS and a last phase writes T * alpha densely (fp32, or bf16 rounded to
 // nearest even) once the scales are known.  Eight waves per SIMD: the
 // register budget is 64.
-template <bool BF16, int MODE, int E, int DENSE = 0>
-__global__ __launch_bounds__(64 * kRgWaves) __attribute__((amdgpu_waves_per_eu(8)))
+template <bool BF16, int MODE, int E, int DENSE = 0, int WM = kRgWaves>
+__global__ __launch_bounds__(64 * WM) __attribute__((amdgpu_waves_per_eu(8)))
 void quantize_rowgroup_kernel(
     const void* __restrict__ w, int64_t n, int64_t k, int group_r, uint8_t* __restrict__ packed,
     float* __restrict__ alpha, float* __restrict__ ws, void* __restrict__ dense = nullptr) {
@@ -618,11 +693,12 @@ void quantize_rowgroup_kernel(
   // [RW][4 C] superblock kept-|w| sums (unless per_group 128); with DENSE
   // then [RW][4 C][16] 16-bit block-pair entries (the codes) and the scales
   extern __shared__ float sb_lds[];
-  __shared__ uint16_t tab[128];      // per index: block 2i's entry, block 2i + 1's entry
+  __shared__ uint16_t tab[2 * 128];  // [slot][h]: block 2i's entry, then block 2i + 1's
   __shared__ float roots[RW];
   const int64_t nsb = k / kSuperblock;
   const int64_t C = (nsb + 3) / 4;  // chunks of four superblocks
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, W = blockDim.x >> 6;
+  const int lane = threadIdx.x & 63, W = blockDim.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));  // uniform: scalar row addresses
   const int s = lane >> 4, i = lane & 15;
   constexpr bool direct = MODE == kRowsDirect;
   const int64_t grp = blockIdx.x;  // row group (modes other than direct)
@@ -630,10 +706,10 @@ void quantize_rowgroup_kernel(
 
   // entry = the block's nibble and sign bit where the lane's byte wants them:
   // block 2i: nibble bits 0..3, sign bit 8; block 2i + 1: bits 4..7, bit 9
-  if (threadIdx.x < 64) {
-    const uint32_t code = block_code(threadIdx.x & 3, threadIdx.x >> 2);
-    tab[2 * threadIdx.x] = (uint16_t)((code & 15u) | ((code >> 4) << 8));
-    tab[2 * threadIdx.x + 1] = (uint16_t)(((code & 15u) << 4) | ((code >> 4) << 9));
+  for (int t = threadIdx.x; t < kLaneIndices<BF16>; t += blockDim.x) {
+    const uint32_t code = lane_index_code<BF16>((uint32_t)t);
+    tab[t] = (uint16_t)((code & 15u) | ((code >> 4) << 8));
+    tab[128 + t] = (uint16_t)(((code & 15u) << 4) | ((code >> 4) << 9));
   }
   constexpr int64_t kElem = BF16 ? 2 : 4;
   // v_perm selector putting the low byte of its second source at byte i / 4
@@ -643,6 +719,8 @@ void quantize_rowgroup_kernel(
   uint16_t* codes_lds = reinterpret_cast<uint16_t*>(sb_lds + RW * 4 * C);     // DENSE only
   float* scale_lds = reinterpret_cast<float*>(codes_lds + RW * 4 * C * 16);  // DENSE only: [RW][groups]
 
+  // rows past row0 + last repeat it (last < RW; negative for a wave wholly past n)
+  const int last = n - 1 - row0 < RW ? (int)(n - 1 - row0) : RW;
   // one chunk of the 8 rows, from registers already loaded
   auto process = [&](const LaneRaw<BF16, 2>(&lw)[RW], int64_t c) {
     const int64_t g = 4 * c + s;  // this lane's superblock
@@ -653,11 +731,12 @@ void quantize_rowgroup_kernel(
     uint32_t sgv = 0;
 #pragma unroll
     for (int it = 0; it < RW; ++it) {
-      const int64_t row = row0 + it;
       float k0, k1;
       const uint32_t i0 = lane_block<BF16>(lw[it], 0, k0);
       const uint32_t i1 = lane_block<BF16>(lw[it], 1, k1);
-      const uint32_t comb = (uint32_t)tab[2 * i0] + (uint32_t)tab[2 * i1 + 1];
+      const char* tb = reinterpret_cast<const char*>(tab);
+      const uint32_t comb = (uint32_t)*reinterpret_cast<const uint16_t*>(tb + i0) +
+                            (uint32_t)*reinterpret_cast<const uint16_t*>(tb + 256 + i1);
       // nibble dwords: lane i's byte is byte i / 4 of dword i % 4
       uint32_t nib = __builtin_amdgcn_perm(0u, comb, sel_nib);
       nib |= dpp_ror<kRor4>(nib);
@@ -665,7 +744,7 @@ void quantize_rowgroup_kernel(
       if constexpr (DENSE != 0) {
         codes_lds[(it * 4 * C + g) * 16 + i] = (uint16_t)comb;  // (g < 4 C always)
       } else {
-        if (gv && row < n && i < 4) nib_rec[it * 4] = nib;
+        if (gv && it <= last && i < 4) nib_rec[it * 4] = nib;
       }
       // sign dword (every lane of the group): bit b = sign bit of block b
       uint32_t sg = ((comb >> 8) & 3u) << (2 * i);
@@ -690,7 +769,7 @@ void quantize_rowgroup_kernel(
       }
     }
     const int rit = 15 - i;  // the row this lane now holds
-    if (gv && rit < RW && row0 + rit < n) {
+    if (gv && rit < RW && rit <= last) {
       if constexpr (DENSE == 0) sgn_plane[rec0 + rit] = sgv;
       if (direct) alpha[rec0 + rit] = (float)((double)sv / 96.0);
       else sb_lds[rit * 4 * C + g] = sv;
@@ -698,16 +777,21 @@ void quantize_rowgroup_kernel(
   };
   // every load of a chunk at once, from clamped in-bounds addresses (rows
   // past n and superblocks past K repeat the last valid ones, never stored)
-  const int64_t last = n - 1 - row0;  // rows past it repeat it
   auto load = [&](LaneRaw<BF16, 2>(&lw)[RW], int64_t c) {
+    // row addresses in scalar registers; the lane adds a 32-bit offset inside the chunk
     const int64_t g = 4 * c + s < nsb ? 4 * c + s : nsb - 1;
-    const char* p = reinterpret_cast<const char*>(w) + (row0 * k + g * kSuperblock + 8 * i) * kElem;
+    const uint32_t off = (uint32_t)(((g - 4 * c) * kSuperblock + 8 * i) * kElem);
+    const char* p = reinterpret_cast<const char*>(w) + (row0 * k + 4 * c * kSuperblock) * kElem;
 #pragma unroll
-    for (int it = 0; it < RW; ++it) lw[it] = load_lane<BF16, 2>(p + (it < last ? it : last) * k * kElem);
+    for (int it = 0; it < RW; ++it) {
+      gchar* rp = uniform_ptr(p + (int64_t)(it < last ? it : last) * k * kElem);
+      if constexpr (BF16) lw[it] = load_lane_at(rp, off);
+      else lw[it] = load_lane_at_f32(rp, off);
+    }
   };
 
   // direct: this wave's one chunk; otherwise the row group's chunks in turn
-  const int64_t stride = direct ? C : W;
+  const int64_t stride = direct ? (int64_t)gridDim.x : W;
   int64_t c = direct ? (int64_t)blockIdx.x : wave;
   __syncthreads();  // the table is written
   for (; c < C; c += stride) {
@@ -871,11 +955,12 @@ void launch_rows(const QuantizePlan& p, int64_t n, int64_t k, int group_r, const
   const int64_t nsb = k / kSuperblock;
   const int64_t chunks = (nsb + 3) / 4;
   constexpr bool direct = MODE == kRowsDirect;
-  const int waves = direct ? kRgWaves : (int)(chunks < kRgWaves ? chunks : kRgWaves);
+  constexpr int WM = direct ? kRgWaves : kRgWavesWalk;
+  const int waves = direct ? kRgWaves : (int)(chunks < WM ? chunks : WM);
   const size_t lds = direct ? 0 : (size_t)kRgRows * 4 * chunks * sizeof(float);
   const int64_t groups = (n + kRgRows - 1) / kRgRows;
   const dim3 grid = direct ? dim3((unsigned)chunks, (unsigned)((groups + waves - 1) / waves)) : dim3((unsigned)groups);
-  hipLaunchKernelGGL((quantize_rowgroup_kernel<BF16, MODE, E>), grid, dim3(64 * waves), lds, s, w, n, k, group_r,
+  hipLaunchKernelGGL((quantize_rowgroup_kernel<BF16, MODE, E, 0, WM>), grid, dim3(64 * waves), lds, s, w, n, k, group_r,
                      packed, alpha, ws);
 }
 
@@ -969,12 +1054,13 @@ template <bool BF16, int MODE, int E, int DENSE>
 void launch_rows_dense(int64_t n, int64_t k, int group_r, const void* w, float* alpha, void* out, hipStream_t s) {
   const int64_t nsb = k / kSuperblock;
   const int64_t chunks = (nsb + 3) / 4;
-  const int waves = (int)(chunks < kRgWaves ? chunks : kRgWaves);
+  constexpr int WM = kRgWavesWalk;
+  const int waves = (int)(chunks < WM ? chunks : WM);
   const int64_t groups = MODE == kRowsChannel ? 1 : nsb / group_r;
   const size_t lds = (size_t)kRgRows * 4 * chunks * (sizeof(float) + 16 * sizeof(uint16_t)) +
                      (size_t)kRgRows * groups * sizeof(float);
   const dim3 grid((unsigned)((n + kRgRows - 1) / kRgRows));
-  hipLaunchKernelGGL((quantize_rowgroup_kernel<BF16, MODE, E, DENSE>), grid, dim3(64 * waves), lds, s, w, n, k,
+  hipLaunchKernelGGL((quantize_rowgroup_kernel<BF16, MODE, E, DENSE, WM>), grid, dim3(64 * waves), lds, s, w, n, k,
                      group_r, nullptr, alpha, nullptr, out);
 }
 

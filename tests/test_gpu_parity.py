@@ -116,6 +116,28 @@ def test_quantize_ties_zeros_signed_zero(gran):
 
 
 @pytest.mark.parametrize("gran", ["per_group", "per_channel", "per_tensor"])
+@pytest.mark.parametrize("k", [1024, 128 * 40])
+def test_quantize_bf16_special_patterns(gran, k):
+    """bf16 blocks built from signed zeros, subnormals, the smallest normal,
+    +-1 and its neighbour and large finite values: every ordered block of 4
+    over six of them (ties of equal magnitude and opposite sign, zeros kept
+    beside a zero), then random blocks over the whole set.  The kernel
+    compares bf16 magnitudes as integers; the oracle compares the values."""
+    enum = np.array([0x0000, 0x8000, 0x0001, 0x8001, 0x3F80, 0xBF80], np.uint16)
+    extra = np.array([0x007F, 0x807F, 0x0080, 0x8080, 0x3F81, 0xBF81, 0x7000, 0xF000, 0x0100], np.uint16)
+    pool = np.concatenate([enum, extra])
+    n = 64
+    g = np.random.default_rng(31 + k)
+    bits = pool[g.integers(0, pool.size, size=n * k)]
+    combos = np.stack(np.meshgrid(*([np.arange(enum.size)] * 4), indexing="ij"), -1).reshape(-1, 4)
+    bits[:combos.size] = enum[combos].reshape(-1)
+    bits = bits.reshape(n, k)
+    vals = WL.bf16_bits_to_f32(bits)
+    check_quantize(dev_bf16(bits), vals, gran)
+    check_quantize(dev_f32(vals), vals, gran)
+
+
+@pytest.mark.parametrize("gran", ["per_group", "per_channel", "per_tensor"])
 def test_quantize_8192_bf16_outliers(gran):
     bits, vals = WL.latent_weight_outliers_bf16(8192, 8192, 5000)
     check_quantize(dev_bf16(bits), vals, gran)

@@ -139,6 +139,23 @@ def test_gemv_workspace_rejected_when_needed(lib):
     assert gv(lib, b=4, ws=FAKE, wsb=need - 4) == L.ERR_WORKSPACE
 
 
+@pytest.mark.parametrize("n,k,count,split", [
+    (3072, 3072, 28, 6),   # 3B q / o over 28 layers: 6 splits of one 4-superblock window
+    (1024, 3072, 28, 6),   # 3B k / v: 6, not 8 splits of 3 superblocks
+    (8192, 3072, 28, 2),   # 3B gate / up: 2 splits of 12 superblocks
+    (3072, 8192, 28, 4),   # 3B down: 4 splits of 16 superblocks
+    (2048, 8192, 1, 16),   # a K = 8192 single call: 16 splits, not 64 of one superblock
+    (2048, 2048, 1366, 1),  # the 1B headline launches: no split
+])
+def test_gemv_batch1_split_sizes(lib, n, k, count, split):
+    """Batch 1 splits K across workgroups by the largest divisor of the groups
+    that keeps the launch within ~2048 workgroups and leaves each split whole
+    4-superblock windows; the workspace holds count * split * N fp32
+    partials."""
+    need = lib.sherry_workspace_bytes(L.OP_GEMV, n, k, L.PER_GROUP, 128, 1, count)
+    assert need == (count * split * n * 4 if split > 1 else 0)
+
+
 def gm(lib, n=64, k=512, gran=L.PER_GROUP, g=128, packed=FAKE, alpha=FAKE2, x=FAKE, m=32, y=FAKE2):
     return lib.sherry_gemm(n, k, gran, g, packed, alpha, x, m, y, None, 0, None)
 

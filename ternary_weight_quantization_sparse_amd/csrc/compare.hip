@@ -97,6 +97,26 @@ __global__ void repack_tl2_kernel(const uint8_t* __restrict__ packed, uint8_t* _
   for (int i = 0; i < 5; ++i) dst[i] = u32x2{w[2 * i], w[2 * i + 1]};
 }
 
+// Entries [16 H, 16 H + 16) of a triple's table: code = d0 + 3 d1 + 9 d2,
+// value (v(d0) + v(d1)) + v(d2) with v(d) = (d - 1) x_i, from the nine sums
+// of the first two digits (every index below is a compile-time constant).
+template <int H>
+__device__ inline void tl2_table_half(float* t, const float xs[3]) {
+  const float a[3] = {-xs[0], 0.f, xs[0]}, b[3] = {-xs[1], 0.f, xs[1]}, c[3] = {-xs[2], 0.f, xs[2]};
+  float p[9];
+#pragma unroll
+  for (int i = 0; i < 9; ++i) p[i] = a[i % 3] + b[i / 3];
+  float e[16];
+#pragma unroll
+  for (int j = 0; j < 16; ++j) {
+    const int code = 16 * H + j;
+    e[j] = code < 27 ? p[code % 9] + c[code / 9] : 0.f;
+  }
+  float4* d = reinterpret_cast<float4*>(t);
+#pragma unroll
+  for (int q = 0; q < 4; ++q) d[q] = make_float4(e[4 * q], e[4 * q + 1], e[4 * q + 2], e[4 * q + 3]);
+}
+
 template <bool YBF16>
 __device__ inline void store_out(void* y, int64_t i, float v) {
   if constexpr (YBF16) {
@@ -107,8 +127,11 @@ __device__ inline void store_out(void* y, int64_t i, float v) {
 }
 
 // Batch-1 GEMV over 2-bit planes.  Table of pair p: entry e = v(e & 3) x[2p]
-// + v(e >> 2) x[2p+1], v = (0, +1, -1, 0).
-__global__ __launch_bounds__(kThreads) void gemv_2bit_kernel(const uint8_t* __restrict__ planes,
+// + v(e >> 2) x[2p+1], v = (0, +1, -1, 0).  TH threads (one row each) share
+// the tables: 256, or 512 on launches with workgroups to spare (as the
+// Sherry kernel's 512-row panels).
+template <int TH>
+__global__ __launch_bounds__(TH) void gemv_2bit_kernel(const uint8_t* __restrict__ planes,
                                                              const float* __restrict__ alpha,
                                                              const uint16_t* __restrict__ x,
                                                              uint16_t* __restrict__ y, int64_t n, int64_t k,
@@ -118,7 +141,7 @@ __global__ __launch_bounds__(kThreads) void gemv_2bit_kernel(const uint8_t* __re
   const int tid = threadIdx.x;
   const int64_t c = blockIdx.y;
   const uint8_t* pl = planes + c * planes_stride;
-  const int64_t row = (int64_t)blockIdx.x * kThreads + tid;
+  const int64_t row = (int64_t)blockIdx.x * TH + tid;
   const uint32_t rr = (uint32_t)(row < n ? row : n - 1);  // clamped rows are not stored
   const int64_t nsb = k / kSb2;
   float acc = 0.f;
@@ -127,18 +150,20 @@ __global__ __launch_bounds__(kThreads) void gemv_2bit_kernel(const uint8_t* __re
     __syncthreads();
     {
       // thread tid builds pair tid of the window (256 pairs = 4 superblocks)
-      const int64_t kk = g0 * kSb2 + 2 * tid;
-      float x0 = 0.f, x1 = 0.f;
-      if (tid < wn * 64) {
-        const uint32_t xv = *reinterpret_cast<const uint32_t*>(x + kk);
-        x0 = bf16_to_f32((uint16_t)(xv & 0xFFFF));
-        x1 = bf16_to_f32((uint16_t)(xv >> 16));
-      }
-      const float v0[4] = {0.f, x0, -x0, 0.f};
-      const float v1[4] = {0.f, x1, -x1, 0.f};
-      float* t = tbl + tid * 16;
+      if (tid < kWin2 * 64) {
+        const int64_t kk = g0 * kSb2 + 2 * tid;
+        float x0 = 0.f, x1 = 0.f;
+        if (tid < wn * 64) {
+          const uint32_t xv = *reinterpret_cast<const uint32_t*>(x + kk);
+          x0 = bf16_to_f32((uint16_t)(xv & 0xFFFF));
+          x1 = bf16_to_f32((uint16_t)(xv >> 16));
+        }
+        const float v0[4] = {0.f, x0, -x0, 0.f};
+        const float v1[4] = {0.f, x1, -x1, 0.f};
+        float* t = tbl + tid * 16;
 #pragma unroll
-      for (int e = 0; e < 16; ++e) t[e] = v0[e & 3] + v1[e >> 2];
+        for (int e = 0; e < 16; ++e) t[e] = v0[e & 3] + v1[e >> 2];
+      }
     }
     __syncthreads();
     u32x4 rec[kWin2][2];
@@ -171,8 +196,12 @@ __global__ __launch_bounds__(kThreads) void gemv_2bit_kernel(const uint8_t* __re
 }
 
 // Batch-1 GEMV over 3-in-5 planes.  Table of triple t: entry code =
-// sum_i (digit_i(code) - 1) x[3t + i] (entries 27..31 unused).
-__global__ __launch_bounds__(kThreads) void gemv_tl2_kernel(const uint8_t* __restrict__ planes,
+// sum_i (digit_i(code) - 1) x[3t + i] (entries 27..31 unused), built with
+// adds of +-x / 0 only (with the digit products computed from the code at run
+// time the build took 75 VGPRs and ran the layer pass 14% slower).  TH
+// threads as in the 2-bit kernel.
+template <int TH>
+__global__ __launch_bounds__(TH) void gemv_tl2_kernel(const uint8_t* __restrict__ planes,
                                                             const float* __restrict__ alpha,
                                                             const uint16_t* __restrict__ x,
                                                             uint16_t* __restrict__ y, int64_t n, int64_t k,
@@ -182,14 +211,14 @@ __global__ __launch_bounds__(kThreads) void gemv_tl2_kernel(const uint8_t* __res
   const int tid = threadIdx.x;
   const int64_t c = blockIdx.y;
   const uint8_t* pl = planes + c * planes_stride;
-  const int64_t row = (int64_t)blockIdx.x * kThreads + tid;
+  const int64_t row = (int64_t)blockIdx.x * TH + tid;
   const uint32_t rr = (uint32_t)(row < n ? row : n - 1);
   const int64_t nsb = (k + kSb3 - 1) / kSb3;
   float acc = 0.f;
   for (int64_t g0 = 0; g0 < nsb; g0 += kWin3) {
     const int wn = (int)(nsb - g0 < kWin3 ? nsb - g0 : kWin3);
     __syncthreads();
-    {
+    if (tid < kWin3 * 64 * 2) {
       // thread tid builds half tid & 1 of triple tid >> 1 (128 triples = 2 superblocks)
       const int tri = tid >> 1, half = tid & 1;
       float xs[3];
@@ -199,18 +228,12 @@ __global__ __launch_bounds__(kThreads) void gemv_tl2_kernel(const uint8_t* __res
         xs[i] = (tri < wn * 64 && kk < k) ? bf16_to_f32(x[kk]) : 0.f;
       }
       float* t = tbl + tri * 32 + half * 16;
-#pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const int code = half * 16 + e;
-        float v = 0.f;
-        if (code < 27) {
-          const int d0 = code % 3, d1 = (code / 3) % 3, d2 = code / 9;
-          v = ((float)(d0 - 1) * xs[0] + (float)(d1 - 1) * xs[1]) + (float)(d2 - 1) * xs[2];
-        }
-        t[e] = v;
-      }
+      if (half == 0) tl2_table_half<0>(t, xs);
+      else tl2_table_half<1>(t, xs);
     }
     __syncthreads();
+    // both superblocks' records at once: their 8-byte loads share cache lines
+    // (loaded one superblock at a time, 5% more bytes were fetched)
     uint32_t rec[kWin3][10];
 #pragma unroll
     for (int gi = 0; gi < kWin3; ++gi) {
@@ -272,14 +295,23 @@ hipError_t launch_compare_repack(int fmt, int64_t n, int64_t k, const uint8_t* p
 hipError_t launch_compare_gemv(int fmt, int64_t n, int64_t k, const uint8_t* planes, const float* alpha,
                                const uint16_t* x, uint16_t* y, int count, int64_t planes_stride,
                                int64_t alpha_stride, int64_t y_stride, hipStream_t s) {
-  const dim3 grid((unsigned)((n + kThreads - 1) / kThreads), (unsigned)count);
+  // 2-bit: 512-row workgroups where the launch still has >= 2048 of them
+  // (1-2% faster); the 3-in-5 kernel keeps 256 (with 512, its 40-byte
+  // records fetched 4.6% more than their bytes and the pass ran 1% slower)
+  const bool wide = fmt == 0 && (n + 511) / 512 * 512 * 8 <= n * 9 && (n + 511) / 512 * count >= 2048;
+  const int th = wide ? 512 : kThreads;
+  const dim3 grid((unsigned)((n + th - 1) / th), (unsigned)count);
+#define SHERRY_CMP(KER)                                                                                        \
+  if (wide) hipLaunchKernelGGL(KER<512>, grid, dim3(512), 0, s, planes, alpha, x, y, n, k, planes_stride,       \
+                               alpha_stride, y_stride);                                                       \
+  else hipLaunchKernelGGL(KER<kThreads>, grid, dim3(kThreads), 0, s, planes, alpha, x, y, n, k, planes_stride, \
+                          alpha_stride, y_stride);
   if (fmt == 0) {
-    hipLaunchKernelGGL(gemv_2bit_kernel, grid, dim3(kThreads), 0, s, planes, alpha, x, y, n, k, planes_stride,
-                       alpha_stride, y_stride);
+    SHERRY_CMP(gemv_2bit_kernel)
   } else {
-    hipLaunchKernelGGL(gemv_tl2_kernel, grid, dim3(kThreads), 0, s, planes, alpha, x, y, n, k, planes_stride,
-                       alpha_stride, y_stride);
+    SHERRY_CMP(gemv_tl2_kernel)
   }
+#undef SHERRY_CMP
   return hipGetLastError();
 }
 

@@ -919,3 +919,33 @@ def test_compare_gemv_count_strides(fmt):
         y_ref = O.gemv(xv, O.dequant(O.ternary(ws[c]), a, "per_channel", 128))
         check_close(yv[c:c + 1, :n], y_ref,
                     O.tolerance_bound(xv, O.alpha_per_weight(a, n, k, "per_channel", 128), y_ref), f"copy {c}")
+
+
+@pytest.mark.parametrize("fmt", [0, 1])
+def test_compare_gemv_many_copies(fmt):
+    """A launch large enough for the 2-bit kernel's 512-row workgroups (2100
+    copies of a 1000 x 384 matrix, the last workgroup of each copy ragged):
+    the first and last copies against the oracle, every copy equal to the
+    first."""
+    n, k, count = 1000, 384, 2100
+    w = WL.latent_weight(n, k, 1400)
+    pw = S.quantize_pack(dev_f32(w), "per_channel")
+    planes = S.compare_repack(pw, fmt)
+    nb = planes.numel()
+    ps = (nb + 255) // 256 * 256
+    as_ = 1024
+    allp = torch.empty((count, ps), dtype=torch.uint8, device=DEV)
+    allp[:, :nb] = planes
+    alla = torch.empty((count, as_), dtype=torch.float32, device=DEV)
+    alla[:, :n] = pw.alpha
+    xb, xv = WL.activations_bf16(1, k, 1410)
+    y = torch.empty((count, as_), dtype=torch.bfloat16, device=DEV)
+    print(f"[compare] fmt {fmt} {n}x{k} x {count} copies", flush=True)
+    S.compare_gemv(fmt, allp, alla, n, k, dev_bf16(xb), count, ps, as_, y, as_)
+    yv = to_np(y)[:, :n]
+    assert np.array_equal(yv, np.broadcast_to(yv[0], yv.shape))
+    a = O.alpha(w, "per_channel", 128)
+    y_ref = O.gemv(xv, O.dequant(O.ternary(w), a, "per_channel", 128))
+    bound = O.tolerance_bound(xv, O.alpha_per_weight(a, n, k, "per_channel", 128), y_ref)
+    for c in (0, count - 1):
+        check_close(O.bf16_bits_to_f32(yv[c:c + 1]), y_ref, bound, f"copy {c}")

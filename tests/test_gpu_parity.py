@@ -949,3 +949,32 @@ def test_compare_gemv_many_copies(fmt):
     bound = O.tolerance_bound(xv, O.alpha_per_weight(a, n, k, "per_channel", 128), y_ref)
     for c in (0, count - 1):
         check_close(O.bf16_bits_to_f32(yv[c:c + 1]), y_ref, bound, f"copy {c}")
+
+
+@pytest.mark.parametrize("gran", ["per_group", "per_channel"])
+def test_gemv_512_row_panels_ragged(gran):
+    """Batch 1 over 1100 copies of a 1000 x 384 matrix: enough workgroups for
+    the 512-row panels, the second panel of each copy ragged (488 rows);
+    the first and last copies against the oracle, every copy equal."""
+    n, k, count = 1000, 384, 1100
+    w = WL.latent_weight(n, k, 1500)
+    pw = S.quantize_pack(dev_f32(w), gran)
+    nb, nsc = S.packed_bytes(n, k), S.num_scales(n, k, gran, 128)
+    ps, as_ = (nb + 255) // 256 * 256, (nsc + 63) // 64 * 64
+    allp = torch.empty((count, ps), dtype=torch.uint8, device=DEV)
+    allp[:, :nb] = pw.packed
+    alla = torch.empty((count, as_), dtype=torch.float32, device=DEV)
+    alla[:, :nsc] = pw.alpha
+    xb, xv = WL.activations_bf16(1, k, 1510)
+    ys = 1024
+    y = torch.empty((count, ys), dtype=torch.float32, device=DEV)
+    print(f"[gemv] {n}x{k} {gran} x {count} copies", flush=True)
+    S.gemv_batched(allp, alla, n, k, dev_bf16(xb), count, ps, as_, gran, 128, y_dtype="float32", y=y,
+                   y_stride=ys)
+    yv = to_np(y)[:, :n]
+    assert np.array_equal(yv, np.broadcast_to(yv[0], yv.shape))
+    a = O.alpha(w, gran, 128)
+    y_ref = O.gemv(xv, O.dequant(O.ternary(w), a, gran, 128))
+    bound = O.tolerance_bound(xv, O.alpha_per_weight(a, n, k, gran, 128))
+    for c in (0, count - 1):
+        check_close(yv[c:c + 1], y_ref, bound, f"copy {c}")

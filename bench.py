@@ -736,6 +736,30 @@ def bench_quantize(dev, reps=10):
                      "gbs_single_call": (rd + wr) / (t1 * 1e-3) / 1e9}
         log(f"[quantize] {gran}: consistent={ok} repeatable={same} {t * 1e3:.1f} us back to back, "
             f"{res[gran]['gbs']:.0f} GB/s (single call {t1 * 1e3:.1f} us)")
+    # the same weight as fp32 latent (training master weights), per_group 128:
+    # the codes and scales of an fp32 weight that holds the bf16 values exactly
+    # equal the bf16 weight's
+    wf = [c.float() for c in copies]
+    pwf = S.quantize_pack(wf[0], "per_group", 128)
+    pwb = S.quantize_pack(w0, "per_group", 128)
+    same_f = bool(torch.equal(pwf.packed, pwb.packed) and torch.equal(pwf.alpha, pwb.alpha))
+    del pwf, pwb
+    packed = torch.empty(S.packed_bytes(n, k), dtype=torch.uint8, device=dev)
+    alpha = torch.empty(S.num_scales(n, k, "per_group", 128), dtype=torch.float32, device=dev)
+    lib = S.load()
+
+    def launch_f(i=[0]):
+        w = wf[i[0] % 4]
+        i[0] += 1
+        S.check(lib.sherry_quantize_pack(n, k, S._lib.PER_GROUP, 128, w.data_ptr(), S._lib.F32, packed.data_ptr(),
+                                         alpha.data_ptr(), None, 0, torch.cuda.current_stream().cuda_stream))
+    t = back_to_back_ms(launch_f, 10 * reps)
+    rd, wr = n * k * 4, S.packed_bytes(n, k) + 4 * alpha.numel()
+    res["per_group_f32"] = {"equals_bf16": same_f, "ms": t, "gbs": (rd + wr) / (t * 1e-3) / 1e9,
+                            "gweights_per_s": n * k / (t * 1e-3) / 1e9}
+    log(f"[quantize] per_group, fp32 weight: equals bf16={same_f} {t * 1e3:.1f} us back to back, "
+        f"{res['per_group_f32']['gbs']:.0f} GB/s")
+    del wf
     # quantization-aware-training forward: dense bf16 T*alpha from the same
     # weight (per_group 128: one fused kernel; per_channel / per_tensor:
     # quantize + pack into the workspace, then unpack), each equal, bit for

@@ -47,6 +47,9 @@ constexpr int kLutThreads = 256;
 #ifndef SHERRY_LUT_NT
 #define SHERRY_LUT_NT 1       // non-temporal loads for the packed stream
 #endif
+#ifndef SHERRY_LUT_ONEWIN
+#define SHERRY_LUT_ONEWIN 1  // batch-1 splits of one window: records and activations loaded together
+#endif
 #ifndef SHERRY_LUT_ROWS
 #define SHERRY_LUT_ROWS 1     // row slots per thread on large launches
 #endif
@@ -198,7 +201,7 @@ __device__ inline void window_accumulate(const float* tbl, const RowWindow<MODE,
 // workgroup instead of across workgroups, so a call is one kernel with no
 // workspace.  Latency is hidden by occupancy: ~55 VGPRs and 16-64 KB of LDS
 // per workgroup, 8 waves per SIMD.
-template <int MODE, int WIN, int M, bool YBF16, int RW, int KW>
+template <int MODE, int WIN, int M, bool YBF16, int RW, int KW, bool ONEWIN = false>
 __global__ __launch_bounds__(64 * RW * KW) void gemv_b1_lut_kernel(
     const uint8_t* __restrict__ packed, const float* __restrict__ alpha,
     const uint16_t* __restrict__ x, void* __restrict__ y, float* __restrict__ partial, int64_t n, int64_t k,
@@ -244,7 +247,24 @@ __global__ __launch_bounds__(64 * RW * KW) void gemv_b1_lut_kernel(
   // the next table build.  Full launches keep one window of registers: their
   // occupancy (8 waves per SIMD) hides the latency.
   constexpr bool kAhead = KW > 1;
-  if constexpr (kAhead) {
+  if constexpr (ONEWIN) {
+    // One window per workgroup (the launcher checks it): the activations of
+    // the table and the row's records are loaded together before the table
+    // build, so one memory latency is exposed per workgroup instead of two in
+    // sequence.  The activations go first: the build waits only for them.
+    static_assert(KW == 1 && M == 1, "one row slot, one slice");
+    constexpr int kTasks = WIN * kBlocksPerSb * 2;
+    static_assert(kTasks <= kThreadsWg, "one table task per thread");
+    const bool has_task = tid < kTasks;
+    const int blk = (tid >> 1) % (WIN * kBlocksPerSb);
+    const uint2 xv = has_task ? *reinterpret_cast<const uint2*>(x + sb_begin * kSuperblock + blk * 4)
+                              : make_uint2(0u, 0u);
+    RowWindow<MODE, WIN> rw;
+    load_row_window<MODE, WIN>(rw, pk, sgn_base, al, n, rows[0], sb_begin, group_sbs);
+    if (has_task) build_block_half_x(tbl[0] + blk * 32, xv, tid & 1);
+    __syncthreads();
+    window_accumulate<MODE, WIN>(tbl[0], rw, acc[0], accg[0], gpos[0], group_sbs);
+  } else if constexpr (kAhead) {
     // the plan gives every thread at most one table task per window
     // (KW * WIN * 64 <= threads), so each thread also prefetches the 8 bytes
     // of activations its next task needs
@@ -383,7 +403,6 @@ __global__ __launch_bounds__(256) void gemv_mfma_kernel(
   constexpr int kOps = kGroup ? 3 : 2;        // record copies per wave per superblock
   constexpr int kXChunk = kXChunkOf<XR>, kXPitch = kXPitchOf<XR>;
   constexpr int kXPieces = kXChunk / 4;       // 1 KB copies per activation row per chunk
-  constexpr int kXOps = XR / 4 * kXPieces;    // activation copies per wave per chunk
   static_assert(kXChunk % 4 == 0, "chunks are whole 1 KB copies");
   static_assert(kMfmaRing - 2 <= kXChunk, "the chunk-end wait must not cover records still ahead");
   __shared__ __attribute__((aligned(16))) char ring[4][kMfmaRing * kRec];
@@ -702,6 +721,15 @@ template <int MODE, int WIN, int M, bool YBF16, int RW, int KW>
 void launch_lut_one(dim3 grid, hipStream_t s, const uint8_t* packed, const float* alpha, const uint16_t* x,
                     void* y, float* ws, int64_t n, int64_t k, int group_sbs, int ksplit, int64_t ps, int64_t as,
                     int64_t ys) {
+  if constexpr (KW == 1 && M == 1) {
+    // one window per workgroup (a split across workgroups into single windows,
+    // or K of one window)
+    if (SHERRY_LUT_ONEWIN && k / kSuperblock / ksplit == WIN) {
+      hipLaunchKernelGGL((gemv_b1_lut_kernel<MODE, WIN, M, YBF16, RW, KW, true>), grid, dim3(64 * RW * KW), 0, s,
+                         packed, alpha, x, y, ws, n, k, group_sbs, ksplit, ps, as, ys);
+      return;
+    }
+  }
   hipLaunchKernelGGL((gemv_b1_lut_kernel<MODE, WIN, M, YBF16, RW, KW>), grid, dim3(64 * RW * KW), 0, s, packed,
                      alpha, x, y, ws, n, k, group_sbs, ksplit, ps, as, ys);
 }

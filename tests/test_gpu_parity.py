@@ -976,3 +976,51 @@ def test_gemv_512_row_panels_ragged(gran):
     bound = O.tolerance_bound(xv, O.alpha_per_weight(a, n, k, gran, 128))
     for c in (0, count - 1):
         check_close(yv[c:c + 1], y_ref, bound, f"copy {c}")
+
+
+@pytest.mark.parametrize("n,k,gran,g,count,y_dtype", [
+    (1000, 8192, "per_group", 128, 1, "bfloat16"),   # 16 splits of one 4-superblock window
+    (1000, 8192, "per_group", 256, 1, "float32"),    # the same with 2-superblock groups
+    (700, 8192, "per_channel", 128, 1, "float32"),
+    (700, 8192, "per_tensor", 128, 1, "bfloat16"),
+    (1024, 3072, "per_group", 128, 3, "float32"),    # 6 splits of one window
+    (300, 512, "per_group", 128, 1100, "float32"),   # no split, K of one 4-superblock window
+    (300, 256, "per_channel", 128, 2100, "bfloat16"),  # no split, a 2-superblock window
+    (300, 128, "per_tensor", 128, 4200, "float32"),  # no split, a 1-superblock window
+])
+def test_gemv_one_window_launches(n, k, gran, g, count, y_dtype):
+    """Batch-1 launches whose workgroups each cover exactly one table window
+    (a K split into single windows, or K of one window): the records and the
+    table's activations are loaded together before the table build.  Codes
+    and scales bit-exact, products of the first and last copies against the
+    oracle, every copy equal."""
+    w = WL.latent_weight(n, k, 1600 + n)
+    pw = S.quantize_pack(dev_f32(w), gran, g)
+    ref_p, ref_a = O.quantize_pack(w, gran, g)
+    assert np.array_equal(to_np(pw.packed), ref_p)
+    assert np.array_equal(to_np(pw.alpha).view(np.uint32),
+                          np.ascontiguousarray(ref_a, dtype=np.float32).reshape(-1).view(np.uint32))
+    xb, xv = WL.activations_bf16(1, k, 1610 + n)
+    print(f"[gemv one window] {n}x{k} {gran} G={g} x {count} {y_dtype}", flush=True)
+    if count == 1:
+        yv = to_np(S.gemv(pw, dev_bf16(xb), y_dtype)).reshape(1, n)
+    else:
+        nb, nsc = S.packed_bytes(n, k), S.num_scales(n, k, gran, g)
+        ps, as_ = (nb + 255) // 256 * 256, (nsc + 63) // 64 * 64
+        allp = torch.empty((count, ps), dtype=torch.uint8, device=DEV)
+        allp[:, :nb] = pw.packed
+        alla = torch.empty((count, as_), dtype=torch.float32, device=DEV)
+        alla[:, :nsc] = pw.alpha
+        ys = (n + 7) // 8 * 8
+        ydt = torch.float32 if y_dtype == "float32" else torch.bfloat16
+        y = torch.empty((count, ys), dtype=ydt, device=DEV)
+        S.gemv_batched(allp, alla, n, k, dev_bf16(xb), count, ps, as_, gran, g, y_dtype=y_dtype, y=y, y_stride=ys)
+        yv = to_np(y)[:, :n]
+        assert np.array_equal(yv, np.broadcast_to(yv[0], yv.shape))
+    if y_dtype == "bfloat16":
+        yv = O.bf16_bits_to_f32(yv)
+    a = np.asarray(ref_a)
+    y_ref = O.gemv(xv, O.dequant(O.ternary(w), a, gran, g))
+    bound = O.tolerance_bound(xv, O.alpha_per_weight(a, n, k, gran, g), y_ref if y_dtype == "bfloat16" else None)
+    for c in sorted({0, count - 1}):
+        check_close(yv[c:c + 1], y_ref, bound, f"copy {c}")

@@ -987,6 +987,8 @@ def test_gemv_512_row_panels_ragged(gran):
     (300, 512, "per_group", 128, 1100, "float32"),   # no split, K of one 4-superblock window
     (300, 256, "per_channel", 128, 2100, "bfloat16"),  # no split, a 2-superblock window
     (300, 128, "per_tensor", 128, 4200, "float32"),  # no split, a 1-superblock window
+    (1000, 512, "per_group", 128, 1100, "bfloat16"),  # the same on 512-row workgroups (ragged last panel)
+    (1000, 256, "per_tensor", 128, 2100, "float32"),
 ])
 def test_gemv_one_window_launches(n, k, gran, g, count, y_dtype):
     """Batch-1 launches whose workgroups each cover exactly one table window

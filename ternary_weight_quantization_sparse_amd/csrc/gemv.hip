@@ -436,24 +436,36 @@ __global__ __launch_bounds__(256) void gemv_mfma_kernel(
   // Copies of the records, in superblock order: each call copies superblock
   // `iss` of the split into ring slot `slot` and moves on to the next one
   // (past the end it copies the last one again; those are never used).  The
-  // plane pointers advance with it, so no per-copy address arithmetic.
+  // copies are buffer loads from resources based at the superblock's slice
+  // of each plane (uniform bases advanced per copy, per-lane row offsets
+  // fixed): with flat-encoded global_load_lds copies in flight the compiler
+  // cannot count LDS reads in order and would wait for every table lookup
+  // in flight before each tile's MFMAs, including the next tile's.
   int iss = 0, apos = 0;
-  const uint8_t* nib_p = pk + sb_begin * n * 16 + crow * 16;
-  const uint8_t* sgn_p = sgn_base + sb_begin * n * 4 + crow * 4;
-  const float* al_p = al + (kGroup ? (sb_begin / group_sbs) * n : 0) + crow;
+  const uint8_t* nib_s = pk + sb_begin * n * 16;
+  const uint8_t* sgn_s = sgn_base + sb_begin * n * 4;
+  const float* al_s = al + (kGroup ? (sb_begin / group_sbs) * n : 0);
+  const uint32_t v16 = (uint32_t)crow * 16u, v4 = (uint32_t)crow * 4u;
   auto issue = [&](int slot) {
     char* rb = my_ring + slot * kRec;
-    __builtin_amdgcn_global_load_lds(const_cast<uint8_t*>(nib_p), (lds_void*)(rb + kMRecNib), 16, 0, 0);
-    __builtin_amdgcn_global_load_lds(const_cast<uint8_t*>(sgn_p), (lds_void*)(rb + kMRecSgn), 4, 0, 0);
-    if constexpr (kGroup)
-      __builtin_amdgcn_global_load_lds(const_cast<float*>(al_p), (lds_void*)(rb + kMRecAlpha), 4, 0, 0);
+    const __amdgpu_buffer_rsrc_t nr =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(nib_s), (short)0, (int)(n * 16), kBufferWord3);
+    const __amdgpu_buffer_rsrc_t sr =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(sgn_s), (short)0, (int)(n * 4), kBufferWord3);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(nr, (lds_void*)(rb + kMRecNib), 16, v16, 0, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(sr, (lds_void*)(rb + kMRecSgn), 4, v4, 0, 0, 0);
+    if constexpr (kGroup) {
+      const __amdgpu_buffer_rsrc_t ar =
+          __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(al_s), (short)0, (int)(n * 4), kBufferWord3);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(ar, (lds_void*)(rb + kMRecAlpha), 4, v4, 0, 0, 0);
+    }
     if (iss + 1 < sb_per_split) {
       ++iss;
-      nib_p += n * 16;
-      sgn_p += n * 4;
-      if constexpr (MODE == kGroup1) al_p += n;
+      nib_s += n * 16;
+      sgn_s += n * 4;
+      if constexpr (MODE == kGroup1) al_s += n;
       if constexpr (MODE == kGroupN) {
-        if (++apos == group_sbs) { apos = 0; al_p += n; }
+        if (++apos == group_sbs) { apos = 0; al_s += n; }
       }
     }
   };

@@ -440,7 +440,8 @@ __global__ __launch_bounds__(256) void gemv_mfma_kernel(
   // of each plane (uniform bases advanced per copy, per-lane row offsets
   // fixed): with flat-encoded global_load_lds copies in flight the compiler
   // cannot count LDS reads in order and would wait for every table lookup
-  // in flight before each tile's MFMAs, including the next tile's.
+  // in flight before each tile's MFMAs, including the next tile's.  (The
+  // shape checks keep n below 2^22, so a slice's byte range fits 32 bits.)
   int iss = 0, apos = 0;
   const uint8_t* nib_s = pk + sb_begin * n * 16;
   const uint8_t* sgn_s = sgn_base + sb_begin * n * 4;
